@@ -1,0 +1,107 @@
+"""The synthetic decode workloads: shapes, seeds and byte counts.
+
+Shapes follow the decode steps the pages measure: a 0.5B-class and a
+7B-class Qwen2-style model ('07 · R3 — Small-model per-token overhead',
+§1 and §5; '04 · 8o — Killing the CPU stall at decode start', §1), each
+GEMV at n=1 with q4_K weights and a q8_0 lm_head; plus a small-batch
+variant and a routed-expert FFN.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+Q4K_BYTES_PER_WEIGHT = 144 / 256
+Q8_BYTES_PER_VALUE = 34 / 32
+
+
+def q4k_bytes(m: int, k: int) -> int:
+    return m * (-(-k // 256)) * 144
+
+
+def q8_bytes(m: int, k: int) -> int:
+    return m * (k // 32) * 34
+
+
+@dataclass(frozen=True)
+class SingleGemv:
+    name: str = "q4_K x q8_0 GEMV 1024x1024"
+    m: int = 1024
+    k: int = 1024
+    seed: int = 0
+
+    def algorithmic_bytes(self) -> int:
+        return q4k_bytes(self.m, self.k) + q8_bytes(1, self.k) + 4 * self.m
+
+
+@dataclass(frozen=True)
+class DecodeModel:
+    name: str
+    hidden: int
+    n_layers: int
+    qkv_rows: int
+    inter: int
+    vocab: int
+    seed: int
+    eps: float = 1e-6
+
+    def layer_shapes(self):
+        """(rows, k) of the four q4_K GEMVs of one layer, in step order."""
+        return [(self.qkv_rows, self.hidden), (self.hidden, self.hidden),
+                (2 * self.inter, self.hidden), (self.hidden, self.inter)]
+
+    def weight_bytes(self) -> int:
+        per_layer = sum(q4k_bytes(m, k) for m, k in self.layer_shapes())
+        return self.n_layers * per_layer + q8_bytes(self.vocab, self.hidden)
+
+    def algorithmic_bytes(self) -> int:
+        """Weights + q8_0 activations read + f32 outputs written, per step."""
+        acts = 0
+        for m, k in self.layer_shapes():
+            acts += q8_bytes(1, k) + 4 * m
+        acts *= self.n_layers
+        acts += q8_bytes(1, self.hidden) + 4 * self.vocab
+        return self.weight_bytes() + acts
+
+
+DECODE_05B = DecodeModel("0.5B-class decode step (hidden 1024, 24 layers, q8_0 lm_head 151552x1024)",
+                         hidden=1024, n_layers=24, qkv_rows=1280, inter=4864, vocab=151552, seed=1)
+DECODE_7B = DecodeModel("7B-class decode step (hidden 3584, 28 layers, q8_0 lm_head 152064x3584)",
+                        hidden=3584, n_layers=28, qkv_rows=4608, inter=18944, vocab=152064, seed=2)
+
+
+@dataclass(frozen=True)
+class Batched:
+    name: str = "7B-class shapes, n in {2,4,8} activation columns"
+    seed: int = 3
+    ns: tuple = (2, 4, 8)
+    shapes: tuple = ((4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944))
+
+
+@dataclass(frozen=True)
+class MoE:
+    name: str = "routed expert FFN, 64 experts, top-8, hidden 2048, expert inter 1408"
+    seed: int = 4
+    n_experts: int = 64
+    n_sel: int = 8
+    hidden: int = 2048
+    inter: int = 1408
+    n_tokens: int = 1000
+
+    @property
+    def k_pad(self) -> int:
+        """Down-projection K padded up to whole 256-weight super-blocks."""
+        return -(-self.inter // 256) * 256
+
+    def gate_up_bytes(self) -> int:
+        return q4k_bytes(2 * self.inter, self.hidden)
+
+    def down_bytes(self) -> int:
+        return q4k_bytes(self.hidden, self.k_pad)
+
+    def token_weight_bytes(self) -> int:
+        return self.n_sel * (self.gate_up_bytes() + self.down_bytes())
+
+
+SINGLE = SingleGemv()
+BATCHED = Batched()
+MOE = MoE()
