@@ -1,0 +1,399 @@
+"""Benchmark: q4_K x q8_0 decode GEMV throughput on one MI355X.
+
+Default workload: one 7B-class decode step (hidden 3584, 28 layers, q4_K
+QKV/O/gate-up/down GEMVs at n=1 with RMSNorm/SwiGLU glue, q8_0 lm_head
+152064x3584), replayed as one hipGraph per step.  A step streams
+4.25 GB of weights once; the timed region starts with every input resident
+in HBM.  Prints one JSON line (rank 0):
+
+  value      = algorithmic bytes per step / step time, GB/s
+  tok_per_s  = decode steps per second
+  roofline   = the q4_K GEMV kernel (the dominant kernel): average
+               algorithmic bytes per launch / average launch duration, the
+               durations taken with HIP events around each launch on the
+               launching stream, against 8 TB/s
+  cpu_baseline = the reference oracle on the host, on a bounded sample
+
+Other workloads (--workload 05b|single|batched|moe) print their own line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "q4_K x q8_0 GEMV HBM GB/s (% of peak); decode-step tok/s, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="7b", choices=["7b", "05b", "single", "batched", "moe"])
+    p.add_argument("--eager", action="store_true", help="also time the eager arm, interleaved")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel-reps", type=int, default=3, help="passes of the dominant-kernel timing region")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def sem(xs):
+    xs = np.asarray(xs, np.float64)
+    return float(xs.std(ddof=1) / math.sqrt(xs.size)) if xs.size > 1 else 0.0
+
+
+# ------------------------------------------------------------------------------
+
+def upload_model(model, dev):
+    """Weights generated per matrix on the host, moved to HBM, host copy dropped."""
+    import torch
+    from block_quantized_gemv_amd import synth
+    s = model.seed
+    W = {"qkv": [], "o": [], "gu": [], "down": []}
+    shapes = model.layer_shapes()
+    for l in range(model.n_layers):
+        for key, kind, (m, k) in zip(("qkv", "o", "gu", "down"), range(4), shapes):
+            W[key].append(torch.from_numpy(synth.q4k_matrix(s, (synth.KEY_LAYER, l, kind), m, k)).to(dev))
+    W["lm"] = torch.from_numpy(synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, model.hidden)).to(dev)
+    return W
+
+
+def time_kernel_region(mq, model, W, dev, reps):
+    """Every q4_K GEMV of the step, in step order over all layers (each matrix
+    read once per pass, nothing reused from cache), each launch bracketed by
+    HIP events on the launching stream."""
+    import torch
+    from block_quantized_gemv_amd import synth, workloads
+    H, I = model.hidden, model.inter
+    xq = {k: mq.mq_quantize_q8_0(torch.from_numpy(synth.normal_f32(99, (k,), (k,))).to(dev)) for k in (H, I)}
+    shapes = model.layer_shapes()
+    ys = [torch.empty(m, dtype=torch.float32, device=dev) for m, _ in shapes]
+    launches = []
+    for _ in range(reps):
+        for l in range(model.n_layers):
+            for i, key in enumerate(("qkv", "o", "gu", "down")):
+                m, k = shapes[i]
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                mq.mq_gemv_q4k_q8(W[key][l], xq[k], m, k, y=ys[i])
+                b.record()
+                launches.append((key, m, k, a, b))
+    torch.cuda.synchronize()
+    per = {}
+    tot_b = tot_t = 0.0
+    for key, m, k, a, b in launches:
+        us = a.elapsed_time(b) * 1e3
+        nbytes = workloads.q4k_bytes(m, k) + workloads.q8_bytes(1, k) + 4 * m
+        d = per.setdefault(key, {"m": m, "k": k, "bytes": nbytes, "us": []})
+        d["us"].append(us)
+        tot_b += nbytes
+        tot_t += us
+    n = len(launches)
+    shape_rows = {}
+    for key, d in per.items():
+        mu = float(np.mean(d["us"]))
+        shape_rows[key] = {"shape": f"{d['m']}x{d['k']}", "us": round(mu, 2), "sem_us": round(sem(d["us"]), 3),
+                           "GB_s": round(d["bytes"] / mu / 1e3, 1)}
+    avg_bytes, avg_us = tot_b / n, tot_t / n
+    achieved = avg_bytes / avg_us / 1e3
+    return {"bound": "hbm", "kernel": "mq::k_gemv_q4k<1,false>", "launches": n,
+            "bytes_per_launch": round(avg_bytes), "us_per_launch": round(avg_us, 3),
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "per_shape": shape_rows}
+
+
+def cpu_baseline_decode(model, n_layers_sample):
+    """The oracle, single thread, on the first layers of the step (all four
+    GEMVs with their glue) plus the same fraction of lm_head rows."""
+    import oracle
+    from block_quantized_gemv_amd import synth, workloads
+    o = oracle.Oracle()
+    s = model.seed
+    H, I, eps = model.hidden, model.inter, model.eps
+    mats = []
+    for l in range(n_layers_sample):
+        mats.append([synth.q4k_matrix(s, (synth.KEY_LAYER, l, kind), m, k)
+                     for kind, (m, k) in enumerate(model.layer_shapes())])
+    lm_rows = int(round(model.vocab * n_layers_sample / model.n_layers))
+    lm = synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, H)[:lm_rows]
+    h = synth.normal_f32(s, (synth.KEY_STEP_INPUTS,), (1, H))[0]
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    t0 = time.perf_counter()
+    nbytes = 0
+    for qkv, ow, gu, dn in mats:
+        a = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel()
+        t, _ = o.gemv_q4k(qkv, model.qkv_rows, H, a)
+        b = o.quantize_q8_0(o.rmsnorm(t[:H], eps)).ravel()
+        ov, _ = o.gemv_q4k(ow, H, H, b)
+        c = o.quantize_q8_0(o.rmsnorm(ov, eps)).ravel()
+        g_u, _ = o.gemv_q4k(gu, 2 * I, H, c)
+        g = o.quantize_q8_0(o.swiglu(g_u)).ravel()
+        h, _ = o.gemv_q4k(dn, H, I, g)
+        nbytes += sum(workloads.q4k_bytes(m, k) + workloads.q8_bytes(1, k) + 4 * m for m, k in model.layer_shapes())
+    z = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel()
+    o.gemv_q8_0(lm, lm_rows, H, z)
+    nbytes += workloads.q8_bytes(lm_rows, H) + workloads.q8_bytes(1, H) + 4 * lm_rows
+    dt = time.perf_counter() - t0
+    frac = n_layers_sample / model.n_layers
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tok_per_s": round(frac / dt, 6), "seconds": round(dt, 2),
+            "sample": f"{n_layers_sample} of {model.n_layers} layers (4 GEMVs + glue each) and "
+                      f"{lm_rows} of {model.vocab} lm_head rows, single thread; tok/s scaled by "
+                      f"{model.n_layers}/{n_layers_sample}",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_decode(args, model, cpu_layers):
+    import torch
+    from block_quantized_gemv_amd import binding as mq
+    from block_quantized_gemv_amd import synth
+    dev = torch.device("cuda:0")
+    log(f"generating and uploading {model.weight_bytes() / 1e9:.2f} GB of weights")
+    W = upload_model(model, dev)
+    X = torch.from_numpy(synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (16, model.hidden))).to(dev)
+    chain = mq.DecodeChain(model, W, X)
+    info = chain.info()
+    eager = mq.DecodeChain(model, W, X, flags=mq.MQ_EAGER_ONLY) if args.eager else None
+    log(f"chain captured={info['captured']} nodes={info['n_nodes']}")
+    for _ in range(args.warmup):
+        chain.step(mq.MQ_GRAPH)
+        if eager:
+            eager.step(mq.MQ_EAGER)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        chain.step(mq.MQ_GRAPH)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = wall * 1e3 / args.steps
+    log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
+
+    eager_ms = None
+    if eager:
+        # interleaved A/B on one binary: graph and eager steps alternate
+        ga, ea = [], []
+        for _ in range(args.steps):
+            for arm, out in ((chain, ga), (eager, ea)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                arm.step(mq.MQ_GRAPH)
+                b.record()
+                out.append((a, b))
+        torch.cuda.synchronize()
+        ga = [a.elapsed_time(b) for a, b in ga]
+        ea = [a.elapsed_time(b) for a, b in ea]
+        eager_ms = {"graph_ms": round(float(np.mean(ga)), 4), "graph_sem_ms": round(sem(ga), 5),
+                    "eager_ms": round(float(np.mean(ea)), 4), "eager_sem_ms": round(sem(ea), 5)}
+        log(f"interleaved A/B: {eager_ms}")
+
+    roof = time_kernel_region(mq, model, W, dev, args.kernel_reps)
+    log(f"q4_K GEMV: {roof['achieved']} GB/s per launch ({roof['frac'] * 100:.1f}% of 8 TB/s)")
+    nbytes = model.algorithmic_bytes()
+    value = nbytes / (ms * 1e-3) / 1e9
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+           "config": {"workload": model.name, "hidden": model.hidden, "layers": model.n_layers,
+                      "qkv_rows": model.qkv_rows, "inter": model.inter, "vocab": model.vocab, "n": 1,
+                      "seed": model.seed, "weights": "q4_K (lm_head q8_0)", "graph": bool(info["captured"]),
+                      "graph_nodes": info["n_nodes"], "bytes_per_step": nbytes},
+           "tok_per_s": round(1e3 / ms, 2), "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+           "step_event_ms": round(float(np.mean(per_step)), 4), "step_event_sem_ms": round(sem(per_step), 5),
+           "roofline": roof}
+    if eager_ms:
+        out["ab_graph_vs_eager"] = eager_ms
+    chain.close()
+    if eager:
+        eager.close()
+    del W
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline_decode(model, cpu_layers)
+    return out
+
+
+# ------------------------------------------------------------ other workloads ----
+
+def run_single(args):
+    import torch
+    from block_quantized_gemv_amd import binding as mq
+    from block_quantized_gemv_amd import synth, workloads
+    wl = workloads.SINGLE
+    dev = torch.device("cuda:0")
+    # cold: rotate enough copies that the working set (>= 1.2 GB) exceeds every cache
+    copies = 2048
+    base = synth.q4k_matrix(wl.seed, (synth.KEY_MATRIX,), wl.m, wl.k)
+    W = torch.from_numpy(base).to(dev).repeat(copies, 1).view(copies, -1)
+    xq = mq.mq_quantize_q8_0(torch.from_numpy(synth.normal_f32(wl.seed, (synth.KEY_COLUMNS,), (wl.k,))).to(dev))
+    y = torch.empty(wl.m, dtype=torch.float32, device=dev)
+    res = {}
+    for mode in ("hot", "cold"):
+        for i in range(args.warmup):
+            mq.mq_gemv_q4k_q8(W[0 if mode == "hot" else i % copies], xq, wl.m, wl.k, y=y)
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            mq.mq_gemv_q4k_q8(W[0 if mode == "hot" else (i * 7) % copies], xq, wl.m, wl.k, y=y)
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        res[mode] = {"us": round(float(np.median(us)), 3), "sem_us": round(sem(us), 4),
+                     "GB_s": round(wl.algorithmic_bytes() / float(np.median(us)) / 1e3, 1)}
+    return {"metric": METRIC, "value": res["cold"]["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": res["cold"]["us"] / 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": wl.name, "m": wl.m, "k": wl.k, "seed": wl.seed}, "modes": res}
+
+
+def run_batched(args):
+    import torch
+    from block_quantized_gemv_amd import binding as mq
+    from block_quantized_gemv_amd import synth, workloads
+    wl = workloads.BATCHED
+    dev = torch.device("cuda:0")
+    rows = {}
+    for (m, k) in wl.shapes:
+        reps = max(2, int(math.ceil(1.2e9 / workloads.q4k_bytes(m, k))))
+        W = torch.from_numpy(synth.q4k_matrix(wl.seed, (synth.KEY_MATRIX, m, k), m, k)).to(dev)
+        Ws = [W] + [W.clone() for _ in range(reps - 1)]
+        for n in (1,) + tuple(wl.ns):
+            xq = mq.mq_quantize_q8_0(torch.from_numpy(synth.normal_f32(wl.seed, (synth.KEY_COLUMNS, n, k), (n, k))).to(dev))
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            for i in range(args.warmup):
+                mq.mq_gemv_q4k_q8_batched(Ws[i % reps], xq, m, k, n, y=y)
+            evs = []
+            for i in range(args.steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                mq.mq_gemv_q4k_q8_batched(Ws[i % reps], xq, m, k, n, y=y)
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            nbytes = workloads.q4k_bytes(m, k) + workloads.q8_bytes(n, k) + 4 * m * n
+            rows[f"{m}x{k} n={n}"] = {"us": round(us, 2), "GB_s": round(nbytes / us / 1e3, 1)}
+            log(f"{m}x{k} n={n}: {us:.2f} us, {nbytes / us / 1e3:.1f} GB/s")
+        del Ws, W
+        torch.cuda.empty_cache()
+    best = rows[f"37888x3584 n=8"]["GB_s"]
+    return {"metric": METRIC, "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": rows["37888x3584 n=8"]["us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": wl.name, "seed": wl.seed, "value_is": "7B gate/up n=8, cold"}, "shapes": rows}
+
+
+def run_moe(args):
+    import torch
+    from block_quantized_gemv_amd import binding as mq
+    from block_quantized_gemv_amd import synth, workloads
+    wl = workloads.MOE
+    dev = torch.device("cuda:0")
+    H, I = wl.hidden, wl.inter
+    gu = torch.from_numpy(np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 0), 2 * I, H)
+                                    for e in range(wl.n_experts)])).to(dev)
+    dn = torch.from_numpy(np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 1), H, I)
+                                    for e in range(wl.n_experts)])).to(dev)
+    T = wl.n_tokens
+    ids, logits = synth.routing(wl.seed, T, wl.n_experts, wl.n_sel)
+    X = synth.normal_f32(wl.seed, (synth.KEY_TOKEN_X,), (T, H))
+    chain = mq.MoEChain(wl.n_experts, wl.n_sel, H, I, gu.view(-1), gu[0].numel(), dn.view(-1), dn[0].numel(),
+                        torch.from_numpy(ids).to(dev), torch.from_numpy(logits).to(dev), torch.from_numpy(X).to(dev))
+    for _ in range(args.warmup):
+        chain.step()
+    chain.reset(0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(T):
+        chain.step()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = wall * 1e6 / T
+    nbytes = wl.token_weight_bytes()
+    return {"metric": METRIC, "value": round(nbytes / us / 1e3, 1), "unit": "GB/s", "n_gpus": 1, "steps": T,
+            "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": wl.name, "seed": wl.seed, "tokens": T, "bytes_per_token_padded": nbytes},
+            "us_per_token": round(us, 3), "event_us_per_token": round(a.elapsed_time(b) * 1e3 / T, 3),
+            "tokens_per_s": round(1e6 / us, 1)}
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the row-sharded multi-GPU design is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    from block_quantized_gemv_amd import workloads
+    if args.workload == "7b":
+        out = run_decode(args, workloads.DECODE_7B, cpu_layers=2)
+    elif args.workload == "05b":
+        out = run_decode(args, workloads.DECODE_05B, cpu_layers=8)
+    elif args.workload == "single":
+        out = run_single(args)
+    elif args.workload == "batched":
+        out = run_batched(args)
+    else:
+        out = run_moe(args)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

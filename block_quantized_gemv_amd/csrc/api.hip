@@ -1,0 +1,506 @@
+// The extern "C" boundary of libmq: argument validation (host only, before
+// any HIP call), error reporting, and the graph-captured decode-step chains.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <functional>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mq.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace mq;
+
+namespace {
+
+thread_local std::string g_err;
+unsigned g_fault = MQ_FAULT_NONE;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return MQ_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+#define CHECK_ARG(cond, ...) \
+    do { if (!(cond)) return fail(MQ_ERR_ARG, __VA_ARGS__); } while (0)
+#define CHECK_SHAPE(cond, ...) \
+    do { if (!(cond)) return fail(MQ_ERR_SHAPE, __VA_ARGS__); } while (0)
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+constexpr int64_t kMaxK = (int64_t)1 << 24;
+
+int check_q4k(const void* w, const void* xq, const float* y, int64_t m, int64_t k) {
+    CHECK_ARG(w && xq && y, "null pointer (w=%p xq=%p y=%p)", w, xq, (const void*)y);
+    CHECK_ARG(aligned(w, 16), "q4_K weights must be 16-byte aligned");
+    CHECK_ARG(aligned(xq, 2), "q8_0 activation must be 2-byte aligned");
+    CHECK_ARG(aligned(y, 4), "y must be 4-byte aligned");
+    CHECK_SHAPE(m >= 1 && m <= kMaxRows, "m=%lld out of range [1, 2^30]", (long long)m);
+    CHECK_SHAPE(k >= 256 && k <= kMaxK && k % 256 == 0, "k=%lld must be a positive multiple of 256", (long long)k);
+    return MQ_OK;
+}
+
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+    return st != hipStreamCaptureStatusNone;
+}
+
+// Device workspace for the split-k partials, one per device, grown on demand.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+Workspace g_ws[64];
+
+int workspace(size_t need, hipStream_t stream, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MQ_ERR_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& ws = g_ws[dev];
+    if (ws.bytes < need) {
+        if (capturing(stream))
+            return fail(MQ_ERR_CAPTURE, "workspace must grow to %zu bytes while the stream is captured; "
+                        "call once outside capture first", need);
+        if (ws.ptr) {
+            hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_status(e, "hipDeviceSynchronize");
+            (void)hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        size_t b = need < (1u << 20) ? (1u << 20) : need;
+        if (hipMalloc(&ws.ptr, b) != hipSuccess) {
+            ws.ptr = nullptr;
+            return fail(MQ_ERR_NOMEM, "hipMalloc(%zu) for the workspace failed", b);
+        }
+        ws.bytes = b;
+    }
+    *out = ws.ptr;
+    return MQ_OK;
+}
+
+// Chooses full staging or split-k for a q4_K GEMV with ncols columns.
+int run_q4k(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t m, int64_t k, int ncols,
+            hipStream_t stream) {
+    const int lds = ncols * stage_bytes((int)(k / 32));
+    if (lds <= kMaxStageLds)
+        return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, nullptr, nullptr, m, k, ncols, stream),
+                          "q4_K GEMV launch");
+    if (ncols * kStageGroupBytes > kMaxStageLds) return fail(MQ_ERR_SHAPE, "too many columns");
+    void* ws = nullptr;
+    const size_t need = (size_t)gemv_q4k_splitk_nsplit(k) * (size_t)m * ncols * sizeof(double);
+    int rc = workspace(need, stream, &ws);
+    if (rc != MQ_OK) return rc;
+    return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)ws, m, k, ncols, stream),
+                      "q4_K split-k GEMV launch");
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ chains ----
+
+struct mq_chain {
+    int kind = 0;                     // 0: decode step, 1: routed-expert token
+    std::vector<std::function<hipError_t(hipStream_t)>> ops;
+    std::vector<void*> allocs;
+    int64_t* step = nullptr;
+    int64_t* cur = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int captured = 0;
+    int n_nodes = 0;
+    uint8_t* q8_trace = nullptr;
+    float* f32_trace = nullptr;
+    int64_t q8_bytes = 0, f32_count = 0;
+};
+
+namespace {
+
+void* chain_alloc(mq_chain* c, size_t bytes, int* rc) {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes < 256 ? 256 : bytes) != hipSuccess) {
+        *rc = fail(MQ_ERR_NOMEM, "hipMalloc(%zu) for a chain buffer failed", bytes);
+        return nullptr;
+    }
+    c->allocs.push_back(p);
+    return p;
+}
+
+void chain_free(mq_chain* c) {
+    if (c->exec) (void)hipGraphExecDestroy(c->exec);
+    if (c->graph) (void)hipGraphDestroy(c->graph);
+    for (void* p : c->allocs) (void)hipFree(p);
+    delete c;
+}
+
+int enqueue(mq_chain* c, hipStream_t s) {
+    for (auto& op : c->ops) {
+        hipError_t e = op(s);
+        if (e != hipSuccess) return hip_status(e, "chain kernel launch");
+    }
+    return ok();
+}
+
+// Warm run, counter reset, then capture; failure to capture leaves an eager chain.
+int chain_finish(mq_chain* c, hipStream_t stream, bool eager_only) {
+    int rc = enqueue(c, stream);
+    if (rc != MQ_OK) return rc;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "chain warm-up step");
+    if ((e = launch_set_i64(c->step, 0, stream)) != hipSuccess) return hip_status(e, "counter reset");
+    if (c->cur && (e = launch_set_i64(c->cur, 0, stream)) != hipSuccess) return hip_status(e, "counter reset");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_status(e, "counter reset");
+    if (eager_only) return ok();
+
+    const char* why = nullptr;
+    hipStream_t cs = nullptr;
+    if (g_fault & MQ_FAULT_CAPTURE) {
+        why = "capture failure injected by mq_test_set_fault";
+    } else if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) {
+        why = "hipStreamCreateWithFlags failed";
+        cs = nullptr;
+    } else if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        why = "hipStreamBeginCapture failed";
+    } else {
+        bool launched = true;
+        for (auto& op : c->ops)
+            if (op(cs) != hipSuccess) { launched = false; break; }
+        hipGraph_t g = nullptr;
+        const hipError_t ee = hipStreamEndCapture(cs, &g);
+        if (!launched || ee != hipSuccess || !g) {
+            why = "a launch failed during capture";
+            if (g) (void)hipGraphDestroy(g);
+        } else if (hipGraphInstantiate(&c->exec, g, nullptr, nullptr, 0) != hipSuccess) {
+            why = "hipGraphInstantiate failed";
+            (void)hipGraphDestroy(g);
+            c->exec = nullptr;
+        } else {
+            size_t n = 0;
+            (void)hipGraphGetNodes(g, nullptr, &n);
+            c->graph = g;
+            c->n_nodes = (int)n;
+            c->captured = 1;
+        }
+    }
+    if (cs) (void)hipStreamDestroy(cs);
+    (void)hipGetLastError();
+    if (!c->captured)
+        fprintf(stderr, "mq: decode-step graph capture failed (%s); this chain runs eagerly\n", why);
+    return ok();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- C ABI ----
+
+extern "C" {
+
+const char* mq_last_error(void) { return g_err.c_str(); }
+const char* mq_version(void) { return "libmq 0.1 (gfx950)"; }
+
+int mq_test_set_fault(unsigned fault_mask) {
+    g_fault = fault_mask;
+    return ok();
+}
+
+int mq_quantize_q8_0(const float* x, void* xq, int64_t k, int n_cols, hipStream_t stream) {
+    CHECK_ARG(x && xq, "null pointer");
+    CHECK_ARG(aligned(x, 4) && aligned(xq, 2), "x must be 4-byte and xq 2-byte aligned");
+    CHECK_SHAPE(k >= 32 && k <= kMaxK && k % 32 == 0, "k=%lld must be a positive multiple of 32", (long long)k);
+    CHECK_SHAPE(n_cols >= 1 && (int64_t)n_cols * k <= ((int64_t)1 << 32), "n_cols=%d out of range", n_cols);
+    return hip_status(launch_quantize_q8_0(x, xq, k, n_cols, stream), "quantize launch");
+}
+
+int mq_gemv_q4k_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k, hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    return run_q4k(w, xq, 0, y, m, k, 1, stream);
+}
+
+int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n,
+                           hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
+    return run_q4k(w, xq, (k / 32) * kQ8Bytes, y, m, k, n, stream);
+}
+
+int mq_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts, const int32_t* ids,
+                        int n_sel, const void* xq, int64_t xq_stride_bytes, float* y,
+                        const float* combine, float* y_out, int64_t m, int64_t k, hipStream_t stream) {
+    CHECK_ARG(w_all && ids && xq, "null pointer");
+    CHECK_ARG(y || combine, "need y, combine or both");
+    CHECK_ARG(!combine || y_out, "combine needs y_out");
+    CHECK_ARG(aligned(w_all, 16) && aligned(xq, 2) && aligned(ids, 4), "misaligned pointer");
+    CHECK_ARG(expert_bytes % 16 == 0, "expert_bytes must be a multiple of 16");
+    CHECK_ARG(xq_stride_bytes >= 0 && xq_stride_bytes % 2 == 0, "bad xq_stride_bytes");
+    CHECK_SHAPE(m >= 1 && m <= kMaxRows, "m out of range");
+    CHECK_SHAPE(k >= 256 && k <= kMaxK && k % 256 == 0, "k must be a positive multiple of 256");
+    CHECK_SHAPE(n_sel >= 1 && n_sel <= 16, "n_sel=%d must be in 1..16", n_sel);
+    CHECK_SHAPE(n_experts >= 1, "n_experts must be >= 1");
+    CHECK_SHAPE(expert_bytes >= m * (k / 256) * kQ4KBytes, "expert_bytes smaller than one expert matrix");
+    CHECK_SHAPE(xq_stride_bytes == 0 || xq_stride_bytes >= (k / 32) * kQ8Bytes, "xq_stride_bytes too small");
+    const int lds = (xq_stride_bytes ? n_sel : 1) * stage_bytes((int)(k / 32));
+    CHECK_SHAPE(lds <= kMaxStageLds, "activations need %d bytes of LDS (max %d)", lds, kMaxStageLds);
+    return hip_status(launch_gemv_q4k_grouped(w_all, expert_bytes, n_experts, ids, n_sel, xq, xq_stride_bytes,
+                                              y, combine, y_out, nullptr, 1, m, k, stream),
+                      "grouped GEMV launch");
+}
+
+int mq_gemv_q8_0_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k, hipStream_t stream) {
+    CHECK_ARG(w && xq && y, "null pointer");
+    CHECK_ARG(aligned(w, 4) && aligned(xq, 2) && aligned(y, 4), "misaligned pointer");
+    CHECK_SHAPE(m >= 1 && m <= kMaxRows, "m out of range");
+    CHECK_SHAPE(k >= 64 && k % 64 == 0 && stage_bytes((int)(k / 32)) <= kMaxStageLds,
+                "k=%lld must be a positive multiple of 64 (and at most ~43k)", (long long)k);
+    return hip_status(launch_gemv_q8_0(w, xq, y, nullptr, m, k, stream), "q8_0 GEMV launch");
+}
+
+int mq_rmsnorm_quantize_q8_0(const float* x, void* xq, int64_t k, float eps, hipStream_t stream) {
+    CHECK_ARG(x && xq && aligned(x, 4) && aligned(xq, 2), "null or misaligned pointer");
+    CHECK_SHAPE(k >= 32 && k % 32 == 0 && k <= kMaxK, "k must be a positive multiple of 32");
+    CHECK_ARG(eps >= 0.0f, "eps must be >= 0");
+    return hip_status(launch_rmsnorm_quantize(x, xq, k, eps, nullptr, 1, stream), "rmsnorm launch");
+}
+
+int mq_swiglu_quantize_q8_0(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
+                            hipStream_t stream) {
+    CHECK_ARG(gu && xq && aligned(gu, 4) && aligned(xq, 2), "null or misaligned pointer");
+    CHECK_SHAPE(inter >= 32 && inter % 32 == 0 && inter <= kMaxK, "inter must be a positive multiple of 32");
+    CHECK_SHAPE(k_pad >= inter && k_pad % 32 == 0 && k_pad <= kMaxK, "k_pad must be >= inter and a multiple of 32");
+    CHECK_SHAPE(n_cols >= 1 && n_cols <= 4096, "n_cols out of range");
+    return hip_status(launch_swiglu_quantize(gu, xq, inter, n_cols, k_pad, stream), "swiglu launch");
+}
+
+int mq_debug_gemv_q4k_q8_isums(const void* w, const void* xq, float* y, int32_t* isum, int32_t* ysum,
+                               int64_t m, int64_t k, hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    CHECK_ARG(isum && aligned(isum, 4), "isum must be a non-null int32 buffer");
+    CHECK_SHAPE(stage_bytes((int)(k / 32)) <= kMaxStageLds, "k too large for the dump kernel");
+    return hip_status(launch_gemv_q4k(w, xq, 0, y, isum, ysum, m, k, 1, stream), "dump GEMV launch");
+}
+
+int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t* isum, int64_t m,
+                                int64_t k, hipStream_t stream) {
+    CHECK_ARG(w && xq && y && isum, "null pointer");
+    CHECK_ARG(aligned(w, 4) && aligned(xq, 2) && aligned(y, 4) && aligned(isum, 4), "misaligned pointer");
+    CHECK_SHAPE(m >= 1 && m <= kMaxRows, "m out of range");
+    CHECK_SHAPE(k >= 64 && k % 64 == 0 && stage_bytes((int)(k / 32)) <= kMaxStageLds, "bad k");
+    return hip_status(launch_gemv_q8_0(w, xq, y, isum, m, k, stream), "dump GEMV launch");
+}
+
+int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) {
+    CHECK_ARG(d && out, "null desc or out");
+    *out = nullptr;
+    CHECK_SHAPE(d->n_layers >= 1 && d->n_layers <= 4096, "n_layers out of range");
+    CHECK_SHAPE(d->hidden >= 256 && d->hidden % 256 == 0 && d->hidden <= kMaxK, "hidden must be a multiple of 256");
+    CHECK_SHAPE(d->inter >= 256 && d->inter % 256 == 0 && d->inter <= kMaxK, "inter must be a multiple of 256");
+    CHECK_SHAPE(d->qkv_rows >= d->hidden && d->qkv_rows <= kMaxRows, "qkv_rows must be >= hidden");
+    CHECK_SHAPE(d->vocab >= 1 && d->vocab <= kMaxRows, "vocab out of range");
+    CHECK_SHAPE(stage_bytes((int)(d->inter / 32)) <= kMaxStageLds, "inter too large");
+    CHECK_ARG(d->w_qkv && d->w_o && d->w_gu && d->w_down && d->w_lm && d->x_table && d->logits,
+              "null pointer in the descriptor");
+    CHECK_ARG(d->n_inputs >= 1, "n_inputs must be >= 1");
+    CHECK_ARG(d->eps >= 0.0f, "eps must be >= 0");
+    CHECK_ARG(aligned(d->w_lm, 4) && aligned(d->x_table, 4) && aligned(d->logits, 4), "misaligned pointer");
+    for (int l = 0; l < d->n_layers; ++l)
+        CHECK_ARG(d->w_qkv[l] && d->w_o[l] && d->w_gu[l] && d->w_down[l] && aligned(d->w_qkv[l], 16) &&
+                      aligned(d->w_o[l], 16) && aligned(d->w_gu[l], 16) && aligned(d->w_down[l], 16),
+                  "layer %d: null or misaligned weight pointer", l);
+    if (capturing(stream)) return fail(MQ_ERR_CAPTURE, "mq_chain_create cannot run inside a stream capture");
+
+    mq_chain* c = new mq_chain();
+    c->kind = 0;
+    const int L = d->n_layers;
+    const int64_t H = d->hidden, I = d->inter, QKV = d->qkv_rows;
+    const int64_t qH = H / 32 * kQ8Bytes, qI = I / 32 * kQ8Bytes;
+    const bool keep = (d->flags & MQ_KEEP_INTERMEDIATES) != 0;
+    int rc = MQ_OK;
+    c->step = (int64_t*)chain_alloc(c, sizeof(int64_t), &rc);
+    // Q8 inputs of every GEMV and f32 outputs; with MQ_KEEP_INTERMEDIATES every
+    // layer gets its own slice of the trace (same layout as the reference trace).
+    const int64_t q8_layer = 3 * qH + qI, f32_layer = QKV + H + 2 * I + H;
+    c->q8_bytes = L * q8_layer + qH;
+    c->f32_count = L * f32_layer;
+    const int64_t q8_alloc = keep ? c->q8_bytes : q8_layer + qH;
+    const int64_t f32_alloc = keep ? c->f32_count : f32_layer;
+    if (rc == MQ_OK) c->q8_trace = (uint8_t*)chain_alloc(c, q8_alloc, &rc);
+    if (rc == MQ_OK) c->f32_trace = (float*)chain_alloc(c, f32_alloc * sizeof(float), &rc);
+    if (rc != MQ_OK) { chain_free(c); return rc; }
+
+    const float eps = d->eps;
+    int64_t* step = c->step;
+    const float* x_table = d->x_table;
+    const int n_inputs = d->n_inputs;
+    const float* h_prev = nullptr;
+    for (int l = 0; l < L; ++l) {
+        uint8_t* q8 = c->q8_trace + (keep ? l * q8_layer : 0);
+        float* f = c->f32_trace + (keep ? l * f32_layer : 0);
+        uint8_t *qa = q8, *qb = q8 + qH, *qc = q8 + 2 * qH, *qg = q8 + 3 * qH;
+        float *t = f, *o = f + QKV, *gu = f + QKV + H, *h = f + QKV + H + 2 * I;
+        const void *wq = d->w_qkv[l], *wo = d->w_o[l], *wg = d->w_gu[l], *wd = d->w_down[l];
+        if (l == 0)
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(x_table, qa, H, eps, step, n_inputs, s); });
+        else
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qa, H, eps, nullptr, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wg, qc, 0, gu, nullptr, nullptr, 2 * I, H, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, qg, I, 1, I, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s); });
+        h_prev = h;
+    }
+    uint8_t* qz = c->q8_trace + (keep ? L * q8_layer : q8_layer);
+    const void* wlm = d->w_lm;
+    float* logits = d->logits;
+    const int64_t V = d->vocab;
+    c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qz, H, eps, nullptr, 1, s); });
+    c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0(wlm, qz, logits, nullptr, V, H, s); });
+    if (!keep) c->q8_bytes = c->f32_count = 0;
+
+    rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
+    if (rc != MQ_OK) { chain_free(c); return rc; }
+    *out = c;
+    return ok();
+}
+
+int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
+    CHECK_ARG(d && out, "null desc or out");
+    *out = nullptr;
+    CHECK_SHAPE(d->n_experts >= 1 && d->n_sel >= 1 && d->n_sel <= 16, "n_experts/n_sel out of range");
+    CHECK_SHAPE(d->hidden >= 256 && d->hidden % 256 == 0 && d->hidden <= kMaxK, "hidden must be a multiple of 256");
+    CHECK_SHAPE(d->inter >= 32 && d->inter % 32 == 0 && d->inter <= kMaxK, "inter must be a multiple of 32");
+    CHECK_SHAPE(d->n_tokens >= 1, "n_tokens must be >= 1");
+    const int64_t H = d->hidden, I = d->inter, KP = (I + 255) / 256 * 256;
+    CHECK_SHAPE(d->gu_expert_bytes >= 2 * I * (H / 256) * kQ4KBytes && d->gu_expert_bytes % 16 == 0,
+                "gu_expert_bytes too small or not a multiple of 16");
+    CHECK_SHAPE(d->dn_expert_bytes >= H * (KP / 256) * kQ4KBytes && d->dn_expert_bytes % 16 == 0,
+                "dn_expert_bytes too small or not a multiple of 16");
+    CHECK_SHAPE(d->n_sel * stage_bytes((int)(KP / 32)) <= kMaxStageLds, "too many slots for LDS");
+    CHECK_ARG(d->w_gu_all && d->w_dn_all && d->ids_table && d->logits_table && d->x_table && d->y_table,
+              "null pointer in the descriptor");
+    CHECK_ARG(aligned(d->w_gu_all, 16) && aligned(d->w_dn_all, 16) && aligned(d->ids_table, 4) &&
+                  aligned(d->logits_table, 4) && aligned(d->x_table, 4) && aligned(d->y_table, 4),
+              "misaligned pointer");
+    if (capturing(stream)) return fail(MQ_ERR_CAPTURE, "mq_moe_create cannot run inside a stream capture");
+
+    mq_chain* c = new mq_chain();
+    c->kind = 1;
+    int rc = MQ_OK;
+    const int S = d->n_sel;
+    c->step = (int64_t*)chain_alloc(c, sizeof(int64_t), &rc);
+    if (rc == MQ_OK) c->cur = (int64_t*)chain_alloc(c, sizeof(int64_t), &rc);
+    int32_t* ids = rc == MQ_OK ? (int32_t*)chain_alloc(c, 64 * sizeof(int32_t), &rc) : nullptr;
+    float* comb = rc == MQ_OK ? (float*)chain_alloc(c, 64 * sizeof(float), &rc) : nullptr;
+    uint8_t* xq = rc == MQ_OK ? (uint8_t*)chain_alloc(c, H / 32 * kQ8Bytes, &rc) : nullptr;
+    float* gu = rc == MQ_OK ? (float*)chain_alloc(c, (size_t)S * 2 * I * sizeof(float), &rc) : nullptr;
+    const int64_t gstride = KP / 32 * kQ8Bytes;
+    uint8_t* gq = rc == MQ_OK ? (uint8_t*)chain_alloc(c, (size_t)S * gstride, &rc) : nullptr;
+    if (rc != MQ_OK) { chain_free(c); return rc; }
+
+    int64_t *step = c->step, *cur = c->cur;
+    const mq_moe_desc dd = *d;
+    c->ops.push_back([=](hipStream_t s) {
+        return launch_moe_prep(step, cur, dd.n_tokens, dd.ids_table, dd.logits_table, dd.x_table, S, H, ids,
+                               comb, xq, s);
+    });
+    c->ops.push_back([=](hipStream_t s) {
+        return launch_gemv_q4k_grouped(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, ids, S, xq, 0, gu,
+                                       nullptr, nullptr, nullptr, 1, 2 * I, H, s);
+    });
+    c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, gq, I, S, KP, s); });
+    c->ops.push_back([=](hipStream_t s) {
+        return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,
+                                       nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, s);
+    });
+    rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
+    if (rc != MQ_OK) { chain_free(c); return rc; }
+    *out = c;
+    return ok();
+}
+
+static int chain_step(mq_chain* c, int mode, hipStream_t stream) {
+    CHECK_ARG(c, "null chain");
+    CHECK_ARG(mode == MQ_GRAPH || mode == MQ_EAGER, "mode must be MQ_GRAPH or MQ_EAGER");
+    if (mode == MQ_GRAPH && c->captured) return hip_status(hipGraphLaunch(c->exec, stream), "hipGraphLaunch");
+    return enqueue(c, stream);
+}
+
+int mq_decode_chain(mq_chain* c, int mode, hipStream_t stream) {
+    CHECK_ARG(!c || c->kind == 0, "not a decode-step chain");
+    return chain_step(c, mode, stream);
+}
+
+int mq_moe_step(mq_chain* c, int mode, hipStream_t stream) {
+    CHECK_ARG(!c || c->kind == 1, "not a routed-expert chain");
+    return chain_step(c, mode, stream);
+}
+
+int mq_chain_info(const mq_chain* c, int* captured, int* n_nodes, int64_t* step) {
+    CHECK_ARG(c, "null chain");
+    if (captured) *captured = c->captured;
+    if (n_nodes) *n_nodes = c->n_nodes;
+    if (step) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipMemcpy(step, c->step, sizeof(int64_t), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_status(e, "reading the step counter");
+    }
+    return ok();
+}
+
+int mq_chain_reset(mq_chain* c, int64_t step, hipStream_t stream) {
+    CHECK_ARG(c, "null chain");
+    CHECK_ARG(step >= 0, "step must be >= 0");
+    return hip_status(launch_set_i64(c->step, step, stream), "counter reset");
+}
+
+int mq_chain_trace_sizes(const mq_chain* c, int64_t* q8_bytes, int64_t* f32_count) {
+    CHECK_ARG(c, "null chain");
+    if (q8_bytes) *q8_bytes = c->q8_bytes;
+    if (f32_count) *f32_count = c->f32_count;
+    return ok();
+}
+
+int mq_chain_read_trace(const mq_chain* c, void* q8_out, float* f32_out, hipStream_t stream) {
+    CHECK_ARG(c, "null chain");
+    CHECK_ARG(c->q8_bytes > 0, "chain was created without MQ_KEEP_INTERMEDIATES");
+    hipError_t e = hipSuccess;
+    if (q8_out) e = hipMemcpyAsync(q8_out, c->q8_trace, c->q8_bytes, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess && f32_out)
+        e = hipMemcpyAsync(f32_out, c->f32_trace, c->f32_count * sizeof(float), hipMemcpyDeviceToDevice, stream);
+    return hip_status(e, "trace copy");
+}
+
+int mq_chain_destroy(mq_chain* c) {
+    if (!c) return ok();
+    (void)hipDeviceSynchronize();
+    chain_free(c);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Device-side building blocks shared by the libmq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kWave = 64;
+constexpr int kQ4KBytes = 144;     // q4_K super-block: 256 weights
+constexpr int kQ8Bytes = 34;       // q8_0 block: 32 values
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
+
+// ---------------------------------------------------------------- f16 ----
+// Hardware conversions: v_cvt_f32_f16 is exact; v_cvt_f16_f32 rounds to
+// nearest even under the default MODE register, subnormals included.
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);   // v_dot4_i32_i8
+}
+
+// ------------------------------------------------------ wave reductions ----
+// All-reduce steps over aligned lane groups.  Every step adds a lane's value
+// to its partner's (IEEE addition is commutative), so all lanes of a group
+// end with the same bits and the order of additions is fixed: the sum is
+// deterministic and tree-shaped, which is also the more accurate schedule
+// ('Part 4 · Lecture 08 — Graph-Resident Decode', §8).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double swizzle_xor16_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    // ds_swizzle bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10
+    const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x401F);
+    const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x401F);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over aligned groups of 2^log2s lanes (log2s in 2..6).  Afterwards every
+// lane of a group holds the group's sum (for log2s == 6: the wave's sum).
+// Must be called with all 64 lanes active.
+__device__ __forceinline__ double group_sum_f64(double v, int log2s) {
+    v += dpp_f64<0xB1>(v);                        // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_f64<0x4E>(v);                        // quad_perm [2,3,0,1]: lane ^ 2
+    if (log2s >= 3) v += dpp_f64<0x141>(v);       // row_half_mirror: quads of each 8
+    if (log2s >= 4) v += dpp_f64<0x140>(v);       // row_mirror: halves of each 16
+    if (log2s >= 5) v += swizzle_xor16_f64(v);    // rows of each 32
+    if (log2s >= 6) v = readlane_f64(v, 0) + readlane_f64(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) { return group_sum_f64(v, 6); }
+
+// ------------------------------------------------ q8_0 activation staging ----
+// A q8_0 vector is restaged once per workgroup into LDS in an aligned,
+// lane-friendly layout.  Blocks are taken in pairs (P = block/2, 64 values);
+// pairs are grouped 64 at a time, one pair per lane of a wave:
+//
+//   group G = P / 64 occupies kStageGroupBytes at G * kStageGroupBytes:
+//     [0, 4096)      codes: 16-byte chunk k (0..3) of pair L = P % 64 at (k*64 + L)*16
+//                    (chunks 0,1 = block 2P, chunks 2,3 = block 2P+1)
+//     [4096, 5120)   (double)d of blocks 2P, 2P+1 at 4096 + L*16
+//     [5120, 6144)   (double)d * sum(codes) of blocks 2P, 2P+1 at 5120 + L*16
+//
+// A wave whose lane L reads pair 64*G + L reads 1 KB contiguously per chunk,
+// so the 16-byte LDS reads are free of bank conflicts; lanes that read the
+// same pair get a broadcast.
+constexpr int kStageGroupBytes = 6144;
+
+__host__ __device__ constexpr int stage_groups(int nblocks) { return (nblocks / 2 + 63) / 64; }
+__host__ __device__ constexpr int stage_bytes(int nblocks) { return stage_groups(nblocks) * kStageGroupBytes; }
+
+// Reads block b of a q8_0 vector.  The 34-byte block starts 2-byte aligned;
+// the nine aligned dwords read here are the ones that contain the block's
+// bytes, so every dword holds at least one byte of the block and lies in its
+// page.  Returns the f16 scale bits and the 32 codes as 8 dwords.
+__device__ __forceinline__ uint32_t load_q8_block(const uint8_t* blk, uint32_t (&q)[8]) {
+    const uint32_t shift = (uint32_t)((uintptr_t)blk & 3u);      // 0 or 2
+    const uint32_t* p = (const uint32_t*)(blk - shift);
+    uint32_t w[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = p[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = shift ? w[i + 1] : __builtin_amdgcn_alignbyte(w[i + 1], w[i], 2);
+    return shift ? (w[0] >> 16) : (w[0] & 0xFFFFu);
+}
+
+// Stage blocks [b0, b0 + nb) of the vector at xq into the layout above at
+// lds (relative block index starts at 0).  Optionally records the int32
+// code sums (for the debug dump).
+__device__ __forceinline__ void stage_q8(const uint8_t* __restrict__ xq, int b0, int nb,
+                                         uint8_t* __restrict__ lds, int tid, int nthreads,
+                                         int32_t* __restrict__ ysum_out) {
+    for (int b = tid; b < nb; b += nthreads) {
+        uint32_t q[8];
+        const uint32_t dbits = load_q8_block(xq + (int64_t)(b0 + b) * kQ8Bytes, q);
+        int s = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = dot4(q[i], 0x01010101u, s);
+        const double d = (double)f16_to_f32(dbits);
+        const int P = b >> 1, half = b & 1, G = P >> 6, L = P & 63;
+        uint8_t* g = lds + G * kStageGroupBytes;
+        *(u32x4*)(g + ((2 * half + 0) * 64 + L) * 16) = u32x4{q[0], q[1], q[2], q[3]};
+        *(u32x4*)(g + ((2 * half + 1) * 64 + L) * 16) = u32x4{q[4], q[5], q[6], q[7]};
+        *(double*)(g + 4096 + L * 16 + half * 8) = d;
+        *(double*)(g + 5120 + L * 16 + half * 8) = d * (double)s;
+        if (ysum_out) ysum_out[b0 + b] = s;
+    }
+}
+
+// The staged data of pair P: codes of blocks 2P (c[0..7]) and 2P+1 (c[8..15]),
+// their scales and scale*code-sums.
+struct StagedPair {
+    uint32_t c[16];
+    double d0, d1, ds0, ds1;
+};
+__device__ __forceinline__ void read_pair(const uint8_t* __restrict__ lds, int P, StagedPair& sp,
+                                          bool need_sums) {
+    const uint8_t* g = lds + (P >> 6) * kStageGroupBytes;
+    const int L = P & 63;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u32x4 v = *(const u32x4*)(g + (k * 64 + L) * 16);
+        sp.c[4 * k + 0] = v.x; sp.c[4 * k + 1] = v.y; sp.c[4 * k + 2] = v.z; sp.c[4 * k + 3] = v.w;
+    }
+    sp.d0 = *(const double*)(g + 4096 + L * 16);
+    sp.d1 = *(const double*)(g + 4096 + L * 16 + 8);
+    if (need_sums) {
+        sp.ds0 = *(const double*)(g + 5120 + L * 16);
+        sp.ds1 = *(const double*)(g + 5120 + L * 16 + 8);
+    } else {
+        sp.ds0 = sp.ds1 = 0.0;
+    }
+}
+
+}  // namespace mq

@@ -1,0 +1,61 @@
+// Internal host-side launchers (not part of the C ABI).  Each enqueues one
+// kernel on `stream` and returns hipGetLastError() of that launch.  Shapes
+// are validated by the caller (api.hip) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+// Lane layout of the q4_K kernels for a row of nsb super-blocks: rows get
+// aligned slots of S = 2^log2s lanes (4 lanes per super-block, one 32-byte
+// nibble chunk each), R = 64/S rows per wave tile, `passes` sweeps over the
+// row's super-blocks.
+struct Q4KPlan {
+    int log2s, rows_per_tile, passes, n_tiles;
+};
+Q4KPlan plan_q4k(int64_t m, int nsb);
+
+struct Q8Plan {
+    int log2s, rows_per_tile, passes, n_tiles;
+};
+Q8Plan plan_q8_0(int64_t m, int npairs);
+
+int device_cu_count();
+
+// Largest LDS a workgroup of the full-staging kernels may take.
+constexpr int kMaxStageLds = 64 * 1024;
+
+hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
+                           int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
+                           hipStream_t stream);
+// Split-k variant for shapes whose activation does not fit in LDS; `part`
+// holds n_split*m*ncols doubles.
+int gemv_q4k_splitk_nsplit(int64_t k);
+hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
+                                  double* part, int64_t m, int64_t k, int ncols, hipStream_t stream);
+hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,
+                                   const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
+                                   float* y, const float* combine, float* y_out,
+                                   const int64_t* out_row, int64_t out_rows, int64_t m, int64_t k,
+                                   hipStream_t stream);
+hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* dump_isum, int64_t m,
+                            int64_t k, hipStream_t stream);
+
+hipError_t launch_quantize_q8_0(const float* x, void* xq, int64_t k, int n_cols, hipStream_t stream);
+// x row: if step != NULL, row (step % n_inputs) of x (x_table) is used and the
+// counter is advanced by one inside the kernel.
+hipError_t launch_rmsnorm_quantize(const float* x, void* xq, int64_t k, float eps, int64_t* step,
+                                   int n_inputs, hipStream_t stream);
+hipError_t launch_swiglu_quantize(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
+                                  hipStream_t stream);
+// Routed-expert token set-up: token t = step % n_tokens (step advanced by one);
+// writes *cur = t, ids_out[n_sel], combine_out[n_sel] = softmax(logits_table[t]),
+// xq_out = Q8(x_table[t]).
+hipError_t launch_moe_prep(int64_t* step, int64_t* cur, int n_tokens, const int32_t* ids_table,
+                           const float* logits_table, const float* x_table, int n_sel, int64_t hidden,
+                           int32_t* ids_out, float* combine_out, void* xq_out, hipStream_t stream);
+hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t stream);
+
+}  // namespace mq

@@ -1,0 +1,266 @@
+/*
+ * libmq — q4_K x q8_0 decode matrix-vector products for AMD MI355X (gfx950).
+ *
+ * The per-token decode-step GEMV over block-quantized weights: a q4_K weight
+ * matrix times an activation requantized to q8_0, with integer 4-way dot
+ * products (the MMVQ "dp4a x q8_0" decode kernel that gave q4_K +37% in
+ * '07 · R3 — Small-model per-token overhead', §1), plus the fixed per-step
+ * cost around it: one graph per decode step, captured once and replayed
+ * ('Part 4 · Lecture 08 — Graph-Resident Decode', §1-§4).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says host.  The caller
+ *    owns all of them; the library keeps none of them after the call
+ *    returns, except inside a chain object (see mq_chain_create).
+ *  - Work is enqueued asynchronously on `stream` (may be NULL for the null
+ *    stream).  Nothing synchronizes unless stated.
+ *  - Return value: MQ_OK (0) or a negative mq_status.  Argument and shape
+ *    errors are found on the host before any HIP call and nothing is
+ *    enqueued.  MQ_ERR_HIP reports a launch error; faults during execution
+ *    surface at the caller's next synchronization (HIP errors are sticky
+ *    and may be reported by a later call — Lecture 08, §3).
+ *  - mq_last_error() returns this thread's message for the last failing
+ *    call (host memory owned by the library, valid until the next call).
+ *  - No exceptions cross this boundary; the library never exits or aborts.
+ *
+ * Formats (little-endian, packed):
+ *  - q4_K super-block, 256 weights in 144 bytes: f16 d at 0, f16 dmin at 2,
+ *    12 bytes of packed 6-bit scales/mins at 4 (sub-block j<4: sc = s[j]&63,
+ *    m = s[j+4]&63; j>=4: sc = (s[j+4]&15) | (s[j-4]>>6)<<4,
+ *    m = (s[j+4]>>4) | (s[j]>>6)<<4), 128 bytes of nibbles at 16 (32-byte
+ *    chunk c: low nibble of byte l = weight 64c+l, high nibble = weight
+ *    64c+32+l).  weight = d*sc_j*q - dmin*m_j, j = index/32.
+ *    A q4_K matrix is row-major: row r is ceil(k/256) consecutive
+ *    super-blocks, rows back to back.  Base pointers must be 16-byte aligned.
+ *  - q8_0 block, 32 values in 34 bytes: f16 d, then 32 int8 q; value = d*q.
+ *    A q8_0 vector of k values is k/32 consecutive blocks.  Base pointers
+ *    must be 2-byte aligned; q8_0 weight matrices 4-byte aligned.
+ *  The pages name these formats but do not lay them out; the layout above
+ *  is the synthetic workload's definition.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MQ_OK = 0,
+    MQ_ERR_ARG = -1,      /* null pointer, bad count, misaligned pointer */
+    MQ_ERR_SHAPE = -2,    /* k not a multiple of the block, m < 1, too large */
+    MQ_ERR_HIP = -3,      /* a HIP runtime call or launch failed */
+    MQ_ERR_CAPTURE = -4,  /* an operation that is illegal while the stream is being captured */
+    MQ_ERR_NOMEM = -5     /* device allocation failed */
+} mq_status;
+
+const char* mq_last_error(void);
+const char* mq_version(void);
+
+/* ---------------------------------------------------------------------------
+ * q8_0 activation quantizer.
+ * x: f32 [n_cols][k] row-major; xq: n_cols*(k/32) q8_0 blocks, column c's
+ * blocks first-to-last at xq + c*(k/32)*34.  k % 32 == 0, 1 <= n_cols.
+ * Per block of 32: amax = max|x| (f32), d = f16(amax/127) rounded to
+ * nearest even, q = roundf(x/d) with the stored d (halves away from zero),
+ * clamped to +-127; a block whose stored d is 0 gets q = 0.  The scan is a
+ * max over magnitudes, so the bytes do not depend on reduction order
+ * (Lecture 08, §8).  Inputs with |x| > 65504*127 or NaN are out of contract.
+ */
+int mq_quantize_q8_0(const float* x, void* xq, int64_t k, int n_cols, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_K x q8_0 GEMV (n = 1): y[r] = sum_i w[r,i] * x[i] for r < m.
+ * w: q4_K matrix [m][k/256 super-blocks]; xq: k/32 q8_0 blocks; y: f32 [m].
+ * k % 256 == 0, m >= 1.  Per 32-value sub-block the kernel forms the exact
+ * int32 sums  isum = sum q4*q8 (v_dot4) and ysum = sum q8, then adds
+ * d8*(d*sc*isum - dmin*m*ysum) in f64; rows are reduced across the wave in
+ * a fixed order and rounded to f32 once.
+ */
+int mq_gemv_q4k_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Batched q4_K x q8_0 GEMV, 1 <= n <= 8 activation columns, weights streamed
+ * once for all columns.  xq: [n][k/32] q8_0 blocks (column c at
+ * xq + c*(k/32)*34); y: f32 [m][n] row-major, y[r*n + c].
+ * Same arithmetic per column as mq_gemv_q4k_q8.  For large n*k the kernel
+ * splits k across workgroups and sums the f64 partials in a second pass in
+ * split order; the partials live in a device workspace the library grows on
+ * demand (MQ_ERR_CAPTURE if it must grow while `stream` is being captured;
+ * call once outside capture first).
+ */
+int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                           int n, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped GEMV for routed experts.  For slot s < n_sel the expert is
+ * e = ids[s] (device int32, read on the device so a captured graph can
+ * replay new routing), whose matrix starts at w_all + e*expert_bytes
+ * (expert_bytes % 16 == 0, >= m*ceil(k/256)*144).
+ * xq_stride_bytes == 0: every slot uses the same activation xq (k/32 blocks);
+ * otherwise slot s uses xq + s*xq_stride_bytes.
+ * y: f32 [n_sel][m] (y[s*m + r]), may be NULL when combine is given.
+ * combine: optional device f32 [n_sel]; when non-NULL, y_out: f32 [m] gets
+ * sum_s combine[s]*y_s computed in f64 in slot order s = 0..n_sel-1 and
+ * rounded once.  A slot whose id is outside [0, n_experts) is not read; its
+ * y row is NaN and so is y_out.  1 <= n_sel <= 16, k % 256 == 0.
+ * Each slot's result is the same as mq_gemv_q4k_q8 on that expert.
+ */
+int mq_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,
+                        const int32_t* ids, int n_sel,
+                        const void* xq, int64_t xq_stride_bytes,
+                        float* y, const float* combine, float* y_out,
+                        int64_t m, int64_t k, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * q8_0 x q8_0 GEMV (the lm_head): w: q8_0 matrix [m][k/32 blocks], 4-byte
+ * aligned; xq: k/32 blocks; y: f32 [m].  k % 64 == 0.
+ * Per block isum = sum w8*x8 (int32), then y += d_w*d_x*isum in f64.
+ */
+int mq_gemv_q8_0_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Glue between GEMVs (the elementwise stand-in of the decode step).
+ * RMSNorm (unit gain) fused with q8_0 quantization of its output:
+ *   y_i = x_i / sqrt(mean(x^2) + eps)  in f64, rounded to f32, then quantized
+ *   exactly as mq_quantize_q8_0.  x: f32 [k]; xq: k/32 blocks; k % 32 == 0.
+ */
+int mq_rmsnorm_quantize_q8_0(const float* x, void* xq, int64_t k, float eps, hipStream_t stream);
+
+/* SwiGLU fused with q8_0 quantization, per column c < n_cols:
+ *   gu: f32 [n_cols][2*inter] = [gate | up];  y_i = silu(gate_i)*up_i in f64,
+ *   silu(g) = g/(1+exp(-g)), rounded to f32, then quantized.
+ *   xq: [n_cols][k_pad/32] blocks; blocks past inter/32 are written as zero
+ *   blocks (d = 0, q = 0), so a q4_K matrix padded to k_pad multiplies them
+ *   by exact zeros.  inter % 32 == 0, k_pad % 32 == 0, k_pad >= inter.
+ */
+int mq_swiglu_quantize_q8_0(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Debug dumps of the integer block sums formed inside the production GEMV
+ * kernels (the same kernel template, compiled with a dump store).
+ * isum: int32 [m][k/32]: isum[r*(k/32)+g] = sum over block g of q4*q8
+ * (q4 = stored nibble 0..15) or w8*x8; ysum: int32 [k/32] = sum of the
+ * activation codes of each block (q4_K only; may be NULL).  y as the
+ * matching GEMV.
+ */
+int mq_debug_gemv_q4k_q8_isums(const void* w, const void* xq, float* y, int32_t* isum,
+                               int32_t* ysum, int64_t m, int64_t k, hipStream_t stream);
+int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t* isum,
+                                int64_t m, int64_t k, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode-step chain: one decode step of a stand-in model, recorded once as a
+ * hipGraph and replayed with one submission per token (Lecture 08, §1).
+ * Per layer l (H = hidden, I = inter):
+ *   a = Q8(RMSNorm(h));       t  = W_qkv[l]  a   (qkv_rows outputs)
+ *   b = Q8(RMSNorm(t[0:H]));  o  = W_o[l]    b   (H)
+ *   c = Q8(RMSNorm(o));       gu = W_gu[l]   c   (2I: gate rows then up rows)
+ *   g = Q8(SwiGLU(gu));       h  = W_down[l] g   (H)
+ * then z = Q8(RMSNorm(h)); logits = W_lm z (q8_0 weights, vocab rows).
+ * The step's input h0 is row (step % n_inputs) of x_table, where `step` is
+ * a device-resident counter that the last kernel of the step increments:
+ * the one thing that must change between replays has to live on the device
+ * and be advanced inside the captured region (Lecture 08, §2).
+ * Inputs are declared before the step starts and nothing is filled from
+ * the host inside it, so the step is one split ('07 · R3', §2).
+ */
+typedef struct mq_chain mq_chain;
+
+enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u };
+enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
+
+typedef struct {
+    int n_layers;                      /* >= 1 */
+    int64_t hidden, qkv_rows, inter, vocab;   /* hidden, inter % 256 == 0; qkv_rows >= hidden */
+    const void* const* w_qkv;          /* HOST arrays of n_layers device pointers (q4_K) */
+    const void* const* w_o;
+    const void* const* w_gu;
+    const void* const* w_down;
+    const void* w_lm;                  /* device q8_0 [vocab][hidden/32] */
+    const float* x_table;              /* device f32 [n_inputs][hidden] */
+    int n_inputs;                      /* >= 1 */
+    float* logits;                     /* device f32 [vocab] */
+    float eps;
+    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES */
+} mq_chain_desc;
+
+/* Validates, allocates every device buffer the step needs (nothing is
+ * allocated later: allocation inside a capture is illegal — Lecture 08,
+ * §3), runs one eager warm step on `stream` and synchronizes it, resets the
+ * step counter to 0, then captures the step into a hipGraph on a private
+ * stream.  A capture failure is not an error: it is logged once to stderr
+ * and the chain runs eagerly (captured = 0).  Weight, table and logits
+ * pointers are baked into the chain: keep them alive and unmoved until
+ * mq_chain_destroy.  *out receives the chain (host object owned by the
+ * library). */
+int mq_chain_create(const mq_chain_desc* desc, hipStream_t stream, mq_chain** out);
+/* One decode step on `stream`: MQ_GRAPH replays the graph (falls back to
+ * eager launches when not captured), MQ_EAGER launches the same kernels with
+ * the same arguments one by one.  The two are byte-identical by
+ * construction. */
+int mq_decode_chain(mq_chain* c, int mode, hipStream_t stream);
+/* Host out-params (any may be NULL): whether a graph exists, its node count,
+ * and the device step counter (this call synchronizes the chain's copy). */
+int mq_chain_info(const mq_chain* c, int* captured, int* n_nodes, int64_t* step);
+/* Set the device step counter (enqueued on `stream`, capture-safe kernel). */
+int mq_chain_reset(mq_chain* c, int64_t step, hipStream_t stream);
+/* With MQ_KEEP_INTERMEDIATES: copy the last step's intermediates into the
+ * caller's device buffers (either may be NULL): q8_out gets, per layer, the
+ * q8_0 bytes of a, b, c, g, then z; f32_out gets, per layer, t, o, gu, h.
+ * Sizes: mq_chain_trace_sizes. */
+int mq_chain_trace_sizes(const mq_chain* c, int64_t* q8_bytes, int64_t* f32_count);
+int mq_chain_read_trace(const mq_chain* c, void* q8_out, float* f32_out, hipStream_t stream);
+int mq_chain_destroy(mq_chain* c);
+
+/* ---------------------------------------------------------------------------
+ * Routed-expert FFN token chain (one token per replay).  Per token t (t is
+ * a device counter advanced inside the step):
+ *   c = softmax(logits_table[t]) (f64, rounded to f32); xq = Q8(x_table[t]);
+ *   gu_s = W_gu[ids_table[t][s]] xq;  g_s = Q8(SwiGLU(gu_s)) padded to
+ *   ceil(inter/256)*256;  y_t = sum_s c_s * (W_dn[ids_table[t][s]] g_s).
+ * W_gu: n_experts matrices of 2*inter rows x hidden, gu_expert_bytes apart;
+ * W_dn: n_experts matrices of hidden rows x ceil(inter/256)*256 (q4_K),
+ * dn_expert_bytes apart.  ids/logits/x tables are device arrays of
+ * n_tokens rows; y_table: f32 [n_tokens][hidden], row t written by token t.
+ * Routing ids are bounds-checked on the device (see mq_gemv_q4k_grouped).
+ */
+typedef struct {
+    int n_experts, n_sel;              /* 1 <= n_sel <= 16 */
+    int64_t hidden, inter;             /* hidden % 256 == 0, inter % 32 == 0 */
+    const void* w_gu_all;
+    int64_t gu_expert_bytes;
+    const void* w_dn_all;
+    int64_t dn_expert_bytes;
+    const int32_t* ids_table;          /* device [n_tokens][n_sel] */
+    const float* logits_table;         /* device [n_tokens][n_sel] */
+    const float* x_table;              /* device [n_tokens][hidden] */
+    float* y_table;                    /* device [n_tokens][hidden] */
+    int n_tokens;
+    unsigned flags;                    /* MQ_EAGER_ONLY */
+} mq_moe_desc;
+
+/* Same life cycle and graph/eager semantics as the decode chain; each
+ * mq_moe_step runs one token and advances the token counter. */
+int mq_moe_create(const mq_moe_desc* desc, hipStream_t stream, mq_chain** out);
+int mq_moe_step(mq_chain* c, int mode, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Test hook, never read from the environment (environment variables are
+ * process-global and leak across tests — '07 · R3', §3.3).
+ * MQ_FAULT_CAPTURE makes the next chain creations behave as if graph
+ * capture failed, to exercise the eager fallback. */
+enum { MQ_FAULT_NONE = 0u, MQ_FAULT_CAPTURE = 1u };
+int mq_test_set_fault(unsigned fault_mask);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

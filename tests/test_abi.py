@@ -1,0 +1,85 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+
+
+@pytest.fixture(scope="module")
+def mq():
+    from block_quantized_gemv_amd import binding, build
+    if not os.path.exists(binding.LIBRARY):
+        build.build()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("mq_quantize_q8_0", "mq_gemv_q4k_q8", "mq_gemv_q4k_q8_batched", "mq_gemv_q4k_grouped",
+                     "mq_decode_chain", "mq_chain_create", "mq_gemv_q8_0_q8"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(mq):
+    lib = mq.lib()
+    raw = C.CDLL(mq.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in mq.h but not exported"
+        assert name in mq.SIGNATURES, f"{name} has no Python binding"
+    assert lib.mq_version().decode().startswith("libmq")
+
+
+FAKE = C.c_void_p(0x10000)     # aligned, never dereferenced: validation fails first
+
+
+def test_gemv_argument_errors(mq):
+    L = mq.lib()
+    assert L.mq_gemv_q4k_q8(None, FAKE, FAKE, 16, 256, None) == mq.MQ_ERR_ARG
+    assert "null" in L.mq_last_error().decode()
+    assert L.mq_gemv_q4k_q8(C.c_void_p(0x10008), FAKE, FAKE, 16, 256, None) == mq.MQ_ERR_ARG   # not 16-aligned
+    assert L.mq_gemv_q4k_q8(FAKE, FAKE, FAKE, 16, 300, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_q4k_q8(FAKE, FAKE, FAKE, 0, 256, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_q4k_q8_batched(FAKE, FAKE, FAKE, 16, 256, 9, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_q4k_q8_batched(FAKE, FAKE, FAKE, 16, 256, 0, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_q8_0_q8(FAKE, FAKE, FAKE, 16, 96, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_quantize_q8_0(FAKE, FAKE, 33, 1, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_quantize_q8_0(FAKE, C.c_void_p(0x10001), 32, 1, None) == mq.MQ_ERR_ARG
+    assert L.mq_swiglu_quantize_q8_0(FAKE, FAKE, 64, 1, 32, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_rmsnorm_quantize_q8_0(FAKE, FAKE, 64, -1.0, None) == mq.MQ_ERR_ARG
+
+
+def test_grouped_argument_errors(mq):
+    L = mq.lib()
+    # combine without y_out
+    assert L.mq_gemv_q4k_grouped(FAKE, 144 * 16, 4, FAKE, 2, FAKE, 0, FAKE, FAKE, None, 16, 256, None) == mq.MQ_ERR_ARG
+    # expert_bytes smaller than one matrix
+    assert L.mq_gemv_q4k_grouped(FAKE, 144, 4, FAKE, 2, FAKE, 0, FAKE, None, None, 16, 256, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_q4k_grouped(FAKE, 144 * 16, 4, FAKE, 17, FAKE, 0, FAKE, None, None, 16, 256, None) == mq.MQ_ERR_SHAPE
+
+
+def test_chain_argument_errors(mq):
+    L = mq.lib()
+    out = C.c_void_p()
+    arr = (C.c_void_p * 1)(FAKE.value)
+    d = mq.ChainDesc(1, 1000, 1280, 4864, 100, arr, arr, arr, arr, FAKE, FAKE, 1, FAKE, 1e-6, 0)
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # hidden % 256
+    d.hidden, d.n_inputs = 1024, 0
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_ARG          # n_inputs
+    d.n_inputs, d.qkv_rows = 1, 512
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # qkv_rows < hidden
+    assert L.mq_decode_chain(None, 0, None) == mq.MQ_ERR_ARG
+    assert L.mq_chain_destroy(None) == mq.MQ_OK
+    m = mq.MoEDesc(64, 8, 2048, 1408, FAKE, 16, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 10, 0)
+    assert L.mq_moe_create(C.byref(m), None, C.byref(out)) == mq.MQ_ERR_SHAPE          # expert bytes too small
+    assert L.mq_test_set_fault(0) == mq.MQ_OK

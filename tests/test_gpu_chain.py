@@ -1,0 +1,210 @@
+"""GPU tests of the graph-captured decode step and routed-expert chains.
+
+Replay of a captured graph runs the same kernels with the same arguments as
+the eager path, so the two must be byte-identical, over capture plus seven
+replays with a different input each step: a frozen host value is correct on
+the first replay and wrong from the second ('Part 4 · Lecture 08 —
+Graph-Resident Decode', §4).  A/A controls (graph vs graph, eager vs eager)
+run first (§5).  Against the oracle the chain is compared end to end at
+real widths; its per-stage intermediates are compared to the oracle's own.
+"""
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (check_tolerance, log, model_weights, oracle_chain_parallel, q8_code_diff, to_dev,
+                         to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mq():
+    import torch
+    assert torch.cuda.is_available()
+    from block_quantized_gemv_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.Oracle()
+
+
+@pytest.fixture(scope="module")
+def pool():
+    with ThreadPoolExecutor(16) as p:
+        yield p
+
+
+def _dev_weights(W):
+    return {k: ([to_dev(a) for a in v] if isinstance(v, list) else to_dev(v)) for k, v in W.items()}
+
+
+@pytest.fixture(scope="module")
+def small_model():
+    """0.5B-class widths, 4 layers (real widths; fewer layers)."""
+    from block_quantized_gemv_amd import synth, workloads
+    model = dataclasses.replace(workloads.DECODE_05B, n_layers=4)
+    W = model_weights(model, 4)
+    X = synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (8, model.hidden))
+    return model, W, _dev_weights(W), X
+
+
+def _run_steps(mq, chain, n, mode, traces=False):
+    outs = []
+    for _ in range(n):
+        logits = to_host(chain.step(mode)).copy()
+        if traces:
+            q8, f32 = chain.trace()
+            outs.append((logits, to_host(q8).copy(), to_host(f32).copy()))
+        else:
+            outs.append(logits)
+    return outs
+
+
+def _same(u, v):
+    return np.array_equal(np.asarray(u).view(np.uint8), np.asarray(v).view(np.uint8))
+
+
+def test_graph_equals_eager_over_replays(mq, o, small_model):
+    """Capture plus 7 replays against the eager path, every intermediate byte
+    compared; layer 0's quantized input at each step must be the oracle's
+    Q8(RMSNorm(x[step mod 8])), which proves the device counter moved the
+    input row on every replay.  (The stand-in step has no residual path, so
+    after a few layers its output barely depends on the input; the logits
+    alone cannot show the counter advancing.)"""
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    keep = mq.MQ_KEEP_INTERMEDIATES
+    g = mq.DecodeChain(model, Wd, xd, flags=keep)
+    e = mq.DecodeChain(model, Wd, xd, flags=keep | mq.MQ_EAGER_ONLY)
+    info = g.info()
+    log(f"captured={info['captured']} nodes={info['n_nodes']}")
+    assert info["captured"] and info["n_nodes"] == 8 * model.n_layers + 2
+    assert not e.info()["captured"]
+    # A/A first: two eager runs of one chain object agree with themselves
+    e.reset(0)
+    a1 = _run_steps(mq, e, 2, mq.MQ_EAGER, traces=True)
+    e.reset(0)
+    a2 = _run_steps(mq, e, 2, mq.MQ_EAGER, traces=True)
+    for u, v in zip(a1, a2):
+        assert all(_same(p, q) for p, q in zip(u, v)), "A/A eager mismatch: the test is broken"
+    e.reset(0)
+    go = _run_steps(mq, g, 8, mq.MQ_GRAPH, traces=True)
+    eo = _run_steps(mq, e, 8, mq.MQ_EAGER, traces=True)
+    qa_bytes = model.hidden // 32 * 34
+    for i, (u, v) in enumerate(zip(go, eo)):
+        for part, p, q in zip(("logits", "q8 trace", "f32 trace"), u, v):
+            assert _same(p, q), f"graph != eager at step {i} ({part})"
+        want_a0 = o.quantize_q8_0(o.rmsnorm(X[i % X.shape[0]], model.eps)).ravel()
+        assert _same(u[1][:qa_bytes], want_a0), f"step {i} did not read input row {i % X.shape[0]}"
+    assert g.info()["step"] == 8 and e.info()["step"] == 8
+    # the graph object can also be stepped eagerly: still identical
+    g.reset(3)
+    u = to_host(g.step(mq.MQ_EAGER)).copy()
+    assert _same(u, go[3][0])
+    g.close()
+    e.close()
+
+
+def test_graph_aa_control(mq, small_model):
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    g1, g2 = mq.DecodeChain(model, Wd, xd), mq.DecodeChain(model, Wd, xd)
+    o1, o2 = _run_steps(mq, g1, 3, mq.MQ_GRAPH), _run_steps(mq, g2, 3, mq.MQ_GRAPH)
+    for u, v in zip(o1, o2):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), "A/A graph mismatch"
+
+
+def test_capture_failure_falls_back_to_eager(mq, small_model):
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    ref = mq.DecodeChain(model, Wd, xd)
+    mq.mq_test_set_fault(mq.MQ_FAULT_CAPTURE)
+    try:
+        f = mq.DecodeChain(model, Wd, xd)
+    finally:
+        mq.mq_test_set_fault(mq.MQ_FAULT_NONE)
+    assert not f.info()["captured"]
+    for i in range(4):
+        u, v = to_host(ref.step()).copy(), to_host(f.step()).copy()
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), f"fallback differs at step {i}"
+
+
+def _chain_vs_oracle(mq, o, pool, model, n_layers, n_inputs=2):
+    from block_quantized_gemv_amd import synth
+    m = dataclasses.replace(model, n_layers=n_layers)
+    log(f"generating {m.name} x{n_layers} layers")
+    W = model_weights(m, n_layers)
+    X = synth.normal_f32(m.seed, (synth.KEY_STEP_INPUTS,), (n_inputs, m.hidden))
+    Wd = _dev_weights(W)
+    ch = mq.DecodeChain(m, Wd, to_dev(X), flags=mq.MQ_KEEP_INTERMEDIATES)
+    for step in range(n_inputs):
+        logits = to_host(ch.step()).copy()
+        q8t, f32t = ch.trace()
+        q8t, f32t = to_host(q8t), to_host(f32t)
+        log(f"oracle step {step}")
+        ref_logits, s_abs, rq8, rf32 = oracle_chain_parallel(o, m, W, X[step], n_layers, pool)
+        ds, dq, mx = q8_code_diff(q8t, rq8)
+        same_f32 = float(np.mean(f32t.view(np.uint32) == rf32.view(np.uint32)))
+        log(f"  intermediates: {q8t.size // 34} q8 blocks, scale diffs {ds}, code diffs {dq} (max {mx}); "
+            f"f32 bit-identical {same_f32:.5f}")
+        check_tolerance(logits, ref_logits, s_abs, f"{m.name} logits step {step}")
+    ch.close()
+
+
+def test_chain_05b_full_depth_vs_oracle(mq, o, pool):
+    from block_quantized_gemv_amd import workloads
+    _chain_vs_oracle(mq, o, pool, workloads.DECODE_05B, workloads.DECODE_05B.n_layers)
+
+
+def test_chain_7b_real_width_vs_oracle(mq, o, pool):
+    from block_quantized_gemv_amd import workloads
+    _chain_vs_oracle(mq, o, pool, workloads.DECODE_7B, 2, n_inputs=1)
+
+
+def test_chain_7b_full_depth_vs_oracle(mq, o, pool):
+    """The benchmark's configuration: all 28 layers and the lm_head."""
+    from block_quantized_gemv_amd import workloads
+    _chain_vs_oracle(mq, o, pool, workloads.DECODE_7B, workloads.DECODE_7B.n_layers, n_inputs=1)
+
+
+# ----------------------------------------------------------- routed experts ----
+
+def test_moe_chain(mq, o):
+    from block_quantized_gemv_amd import synth, workloads
+    wl = workloads.MOE
+    H, I = wl.hidden, wl.inter
+    T = 12
+    log("generating 64 experts")
+    gu = np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 0), 2 * I, H) for e in range(wl.n_experts)])
+    dn = np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 1), H, I) for e in range(wl.n_experts)])
+    ids, logits = synth.routing(wl.seed, T, wl.n_experts, wl.n_sel)
+    X = synth.normal_f32(wl.seed, (synth.KEY_TOKEN_X,), (T, H))
+    args = (wl.n_experts, wl.n_sel, H, I, to_dev(gu.ravel()), gu[0].nbytes, to_dev(dn.ravel()), dn[0].nbytes,
+            to_dev(ids), to_dev(logits), to_dev(X))
+    g = mq.MoEChain(*args)
+    e = mq.MoEChain(*args, flags=mq.MQ_EAGER_ONLY)
+    assert g.info()["captured"] and g.info()["n_nodes"] == 4
+    for t in range(T):
+        g.step(mq.MQ_GRAPH)
+        e.step(mq.MQ_EAGER)
+    yg, ye = to_host(g.y_table), to_host(e.y_table)
+    assert np.array_equal(yg.view(np.uint32), ye.view(np.uint32)), "graph != eager"
+    for t in range(T):
+        y_ref, ys_ref, c_ref = o.moe_token(gu.ravel(), gu[0].nbytes, dn.ravel(), dn[0].nbytes, ids[t], logits[t],
+                                           X[t], H, I)
+        # the combine's own bound: sum_s |c_s| * S_abs of each slot, computed from the oracle's slots
+        s_abs = np.zeros(H)
+        xq = o.quantize_q8_0(X[t]).ravel()
+        for s, ex in enumerate(ids[t]):
+            t_gu, _ = o.gemv_q4k(gu[ex], 2 * I, H, xq)
+            _, sa = o.gemv_q4k(dn[ex], H, I, o.quantize_q8_0(o.swiglu(t_gu)).ravel())
+            s_abs += abs(float(c_ref[s])) * sa
+        check_tolerance(yg[t], y_ref, s_abs, f"token {t}")
+    assert g.info()["step"] == T

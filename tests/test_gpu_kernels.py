@@ -1,0 +1,287 @@
+"""GPU parity of the single kernels against the oracle, through the C ABI.
+
+Integer and byte results must be bit-exact (q8_0 bytes, int32 block sums);
+float outputs must satisfy |y - y_ref| <= 1e-3 * sum_i |w_i x_i| + 1e-6 per
+row, with sum_i |w_i x_i| computed by the oracle in f64.  Small shapes span
+several tiles and a ragged tail and are compared in full; full-size shapes
+run exactly as the benchmark launches them and are compared on sampled rows
+the oracle computes one by one.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (check_tolerance, log, oracle_gemv_parallel, q8_code_diff, sample_rows, to_dev,
+                         to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mq():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_quantized_gemv_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.Oracle()
+
+
+@pytest.fixture(scope="module")
+def pool():
+    with ThreadPoolExecutor(16) as p:
+        yield p
+
+
+def _synth():
+    from block_quantized_gemv_amd import synth
+    return synth
+
+
+# ------------------------------------------------------------------ q8_0 ----
+
+def test_quantize_bytes_exact(mq, o):
+    synth = _synth()
+    cases = {
+        "normal 3x3584": synth.normal_f32(10, (1,), (3, 3584)),
+        "large scale": synth.normal_f32(10, (2,), (2, 1024)) * np.float32(1e3),
+        "subnormal scales": synth.normal_f32(10, (3,), (1, 2048)) * np.float32(1e-4),
+        "mixed zero blocks": np.where(np.arange(4096) % 96 < 32, 0.0,
+                                      synth.normal_f32(10, (4,), (4096,))).astype(np.float32)[None],
+    }
+    lines = [ln for ln in open(__file__.replace("test_gpu_kernels.py", "golden/q8_0_rounding.txt"))
+             if ln.startswith("x:")]
+    cases["hand-worked ties"] = np.array([[float(t) for ln in lines for t in ln.split(":")[1].split()]],
+                                         np.float32)
+    for name, x in cases.items():
+        log(f"quantize case: {name} {x.shape}")
+        got = to_host(mq.mq_quantize_q8_0(to_dev(x)))
+        want = o.quantize_q8_0(x).ravel()
+        assert np.array_equal(got, want), f"{name}: {q8_code_diff(got, want)}"
+
+
+# ------------------------------------------------------------- q4_K GEMV ----
+
+SMALL_SHAPES = [(1, 256), (3, 512), (17, 768), (1024, 1024), (1023, 1024), (1025, 3584), (4097, 1536),
+                (333, 4864), (64, 18944), (5, 2048), (7, 6400), (130, 4096)]
+
+
+@pytest.mark.parametrize("m,k", SMALL_SHAPES)
+def test_gemv_q4k_small(mq, o, m, k):
+    synth = _synth()
+    log(f"q4_K GEMV {m}x{k}")
+    w = synth.q4k_matrix(100 + k, (synth.KEY_MATRIX, m), m, k)
+    x = synth.normal_f32(100 + k, (synth.KEY_COLUMNS, m), (k,))
+    xq = o.quantize_q8_0(x).ravel()
+    wd, xd = to_dev(w), to_dev(xq)
+    y = to_host(mq.mq_gemv_q4k_q8(wd, xd, m, k))
+    yd, isum, ysum = mq.mq_debug_gemv_q4k_q8_isums(wd, xd, m, k)
+    yd, isum, ysum = to_host(yd), to_host(isum), to_host(ysum)
+    ri, ry = o.isums_q4k(w, m, k, xq)
+    assert np.array_equal(isum, ri), f"int32 block sums differ at {np.argwhere(isum != ri)[:4]}"
+    assert np.array_equal(ysum, ry), "activation sums differ"
+    assert np.array_equal(yd.view(np.uint32), y.view(np.uint32)), "dump build changed the float result"
+    y_ref, s_abs = o.gemv_q4k(w, m, k, xq)
+    check_tolerance(y, y_ref, s_abs, f"{m}x{k}")
+
+
+def test_gemv_worked_example(mq, o):
+    """The hand-worked super-block: y = -61.5 exactly."""
+    from oracle_pins import _golden_lines
+    lines = dict(ln.split(":", 1) for ln in _golden_lines("q4k_gemv_worked.txt"))
+    sb = np.array([int(t, 16) for t in lines["sb"].split()], np.uint8)
+    dbits = [int(t, 16) for t in lines["act_d_bits"].split()]
+    q = np.zeros((8, 32), np.int64)
+    for b in (0, 1, 7):
+        q[b] = [int(t) for t in lines[f"act_q_block{b}"].split()]
+    xq = np.frombuffer(b"".join(np.uint16(dbits[b]).tobytes() + q[b].astype(np.int8).tobytes()
+                                for b in range(8)), np.uint8)
+    y, isum, ysum = mq.mq_debug_gemv_q4k_q8_isums(to_dev(sb), to_dev(xq), 1, 256)
+    assert float(to_host(y)[0]) == -61.5
+    assert to_host(isum)[0].tolist() == [int(t) for t in lines["isum"].split()]
+    assert to_host(ysum).tolist() == [int(t) for t in lines["ysum"].split()]
+
+
+FULL_SHAPES = [("7B qkv", 4608, 3584), ("7B o", 3584, 3584), ("7B gate/up", 37888, 3584),
+               ("7B down", 3584, 18944), ("0.5B qkv", 1280, 1024), ("0.5B gate/up", 9728, 1024),
+               ("0.5B down", 1024, 4864), ("expert gate/up", 2816, 2048), ("expert down", 2048, 1536)]
+
+
+@pytest.mark.parametrize("name,m,k", FULL_SHAPES, ids=[s[0] for s in FULL_SHAPES])
+def test_gemv_q4k_full_size(mq, o, pool, name, m, k):
+    synth = _synth()
+    log(f"q4_K GEMV full size {name} {m}x{k}")
+    w = synth.q4k_matrix(2, (synth.KEY_MATRIX, m, k), m, k)
+    x = synth.normal_f32(2, (synth.KEY_COLUMNS, m, k), (k,))
+    xq_dev = mq.mq_quantize_q8_0(to_dev(x))
+    xq = o.quantize_q8_0(x).ravel()
+    assert np.array_equal(to_host(xq_dev), xq)
+    y = to_host(mq.mq_gemv_q4k_q8(to_dev(w), xq_dev, m, k))
+    rows = sample_rows(m, 2048, seed=m)
+    y_ref, s_abs = oracle_gemv_parallel(o.gemv_q4k, w, m, k, xq, rows=rows, pool=pool)
+    check_tolerance(y[rows], y_ref, s_abs, name)
+
+
+# ---------------------------------------------------------------- batched ----
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_batched_small(mq, o, n):
+    synth = _synth()
+    m, k = 301, 2560
+    w = synth.q4k_matrix(3, (synth.KEY_MATRIX, n), m, k)
+    x = synth.normal_f32(3, (synth.KEY_COLUMNS, n), (n, k))
+    xq = o.quantize_q8_0(x).reshape(n, -1)
+    y = to_host(mq.mq_gemv_q4k_q8_batched(to_dev(w), to_dev(xq.ravel()), m, k, n))
+    for c in range(n):
+        y_ref, s_abs = o.gemv_q4k(w, m, k, xq[c])
+        check_tolerance(y[:, c], y_ref, s_abs, f"batched n={n} col {c}")
+
+
+BATCH_SHAPES = [("qkv", 4608, 3584), ("o", 3584, 3584), ("gate/up", 37888, 3584), ("down", 3584, 18944)]
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("name,m,k", BATCH_SHAPES, ids=[s[0] for s in BATCH_SHAPES])
+def test_batched_full_size(mq, o, pool, name, m, k, n):
+    """7B-class shapes, n columns; each column also against the n=1 kernel."""
+    synth = _synth()
+    from block_quantized_gemv_amd import workloads
+    seed = workloads.BATCHED.seed
+    log(f"batched {name} {m}x{k} n={n}")
+    w = synth.q4k_matrix(seed, (synth.KEY_MATRIX, m, k), m, k)
+    x = synth.normal_f32(seed, (synth.KEY_COLUMNS, n, k), (n, k))
+    xq_dev = mq.mq_quantize_q8_0(to_dev(x))
+    xq = o.quantize_q8_0(x).reshape(n, -1)
+    assert np.array_equal(to_host(xq_dev), xq.ravel())
+    wd = to_dev(w)
+    y = to_host(mq.mq_gemv_q4k_q8_batched(wd, xq_dev, m, k, n))
+    rows = sample_rows(m, 512, seed=n * m)
+    for c in range(n):
+        y_ref, s_abs = oracle_gemv_parallel(o.gemv_q4k, w, m, k, xq[c], rows=rows, pool=pool)
+        check_tolerance(y[rows, c], y_ref, s_abs, f"{name} n={n} col {c}")
+        y1 = to_host(mq.mq_gemv_q4k_q8(wd, xq_dev[c * xq.shape[1]:(c + 1) * xq.shape[1]], m, k))
+        same = float(np.mean(y1.view(np.uint32) == y[:, c].copy().view(np.uint32)))
+        log(f"    col {c}: bit-identical to the n=1 kernel on {same:.4f} of rows")
+
+
+# ------------------------------------------------------------ q8_0 lm_head ----
+
+@pytest.mark.parametrize("m,k", [(1, 64), (5, 128), (130, 1024), (67, 3584), (1000, 2048)])
+def test_gemv_q8_0_small(mq, o, m, k):
+    synth = _synth()
+    w = synth.q8_0_matrix(5, (synth.KEY_MATRIX, m, k), m, k)
+    x = synth.normal_f32(5, (synth.KEY_COLUMNS, m, k), (k,))
+    xq = o.quantize_q8_0(x).ravel()
+    y, isum = mq.mq_debug_gemv_q8_0_q8_isums(to_dev(w), to_dev(xq), m, k)
+    assert np.array_equal(to_host(isum), o.isums_q8_0(w, m, k, xq)), "int32 block sums differ"
+    y2 = to_host(mq.mq_gemv_q8_0_q8(to_dev(w), to_dev(xq), m, k))
+    assert np.array_equal(to_host(y).view(np.uint32), y2.view(np.uint32))
+    y_ref, s_abs = o.gemv_q8_0(w, m, k, xq)
+    check_tolerance(y2, y_ref, s_abs, f"q8_0 {m}x{k}")
+
+
+@pytest.mark.parametrize("name,m,k", [("0.5B lm_head", 151552, 1024), ("7B lm_head", 152064, 3584)])
+def test_gemv_q8_0_full_size(mq, o, pool, name, m, k):
+    synth = _synth()
+    log(f"q8_0 GEMV full size {name}")
+    w = synth.q8_0_matrix(1, (synth.KEY_LM_HEAD, k), m, k)
+    x = synth.normal_f32(1, (synth.KEY_COLUMNS, k), (k,))
+    xq = o.quantize_q8_0(x).ravel()
+    y = to_host(mq.mq_gemv_q8_0_q8(to_dev(w), to_dev(xq), m, k))
+    rows = sample_rows(m, 4096, seed=k)
+    y_ref, s_abs = oracle_gemv_parallel(o.gemv_q8_0, w, m, k, xq, rows=rows, pool=pool)
+    check_tolerance(y[rows], y_ref, s_abs, name)
+
+
+# ------------------------------------------------------------------- glue ----
+
+def test_rmsnorm_quantize(mq, o):
+    synth = _synth()
+    for k, scale in ((1024, 1.0), (3584, 37.0), (3584, 1e-3), (18944, 2e4)):
+        x = synth.normal_f32(6, (k,), (k,)) * np.float32(scale)
+        got = to_host(mq.mq_rmsnorm_quantize_q8_0(to_dev(x), 1e-6))
+        want = o.quantize_q8_0(o.rmsnorm(x, 1e-6)).ravel()
+        ds, dq, mx = q8_code_diff(got, want)
+        log(f"  rmsnorm k={k} scale={scale}: scale diffs {ds}, code diffs {dq}, max {mx}")
+        assert ds == 0 and dq <= 2 and mx <= 1, (ds, dq, mx)
+
+
+def test_swiglu_quantize_padded(mq, o):
+    synth = _synth()
+    for inter, n_cols, k_pad in ((1408, 8, 1536), (4864, 1, 4864), (18944, 1, 18944)):
+        gu = synth.normal_f32(7, (inter, n_cols), (n_cols, 2 * inter)) * np.float32(4.0)
+        got = to_host(mq.mq_swiglu_quantize_q8_0(to_dev(gu), inter, n_cols, k_pad)).reshape(n_cols, -1)
+        nbi = inter // 32 * 34
+        for c in range(n_cols):
+            want = o.quantize_q8_0(o.swiglu(gu[c])).ravel()
+            ds, dq, mx = q8_code_diff(got[c, :nbi], want)
+            assert ds == 0 and dq <= 2 and mx <= 1, (inter, c, ds, dq, mx)
+            assert not got[c, nbi:].any(), "pad blocks must be zero"
+        log(f"  swiglu inter={inter} cols={n_cols} pad={k_pad}: ok")
+
+
+# ---------------------------------------------------------------- grouped ----
+
+@pytest.fixture(scope="module")
+def experts():
+    synth = _synth()
+    from block_quantized_gemv_amd import workloads
+    wl = workloads.MOE
+    log("generating 64 experts")
+    gu = np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 0), 2 * wl.inter, wl.hidden)
+                   for e in range(wl.n_experts)])
+    dn = np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 1), wl.hidden, wl.inter)
+                   for e in range(wl.n_experts)])
+    return wl, gu, dn
+
+
+def test_grouped_gate_up_and_down(mq, o, experts):
+    wl, gu, dn = experts
+    synth = _synth()
+    import torch
+    H, I, KP = wl.hidden, wl.inter, wl.k_pad
+    gub, dnb = gu[0].nbytes, dn[0].nbytes
+    gu_d, dn_d = to_dev(gu.ravel()), to_dev(dn.ravel())
+    ids_all, logits_all = synth.routing(wl.seed, 4, wl.n_experts, wl.n_sel)
+    for t in range(4):
+        ids = ids_all[t]
+        x = synth.normal_f32(wl.seed, (synth.KEY_TOKEN_X, t), (H,))
+        xq = o.quantize_q8_0(x).ravel()
+        y_gu, _ = mq.mq_gemv_q4k_grouped(gu_d, gub, wl.n_experts, to_dev(ids), to_dev(xq), 0, 2 * I, H)
+        y_gu = to_host(y_gu)
+        for s, e in enumerate(ids):
+            y_ref, s_abs = o.gemv_q4k(gu[e], 2 * I, H, xq)
+            check_tolerance(y_gu[s], y_ref, s_abs, f"token {t} slot {s} gate/up (expert {e})")
+        # down with per-slot activations and the combine
+        g = np.stack([o.quantize_q8_0(o.swiglu(y_gu[s])).ravel() for s in range(wl.n_sel)])
+        gpad = np.zeros((wl.n_sel, KP // 32 * 34), np.uint8)
+        gpad[:, :g.shape[1]] = g
+        comb = o.softmax(logits_all[t])
+        y_dn, y_out = mq.mq_gemv_q4k_grouped(dn_d, dnb, wl.n_experts, to_dev(ids), to_dev(gpad.ravel()),
+                                             gpad.shape[1], H, KP, combine=to_dev(comb))
+        y_dn, y_out = to_host(y_dn), to_host(y_out)
+        acc = np.zeros(H)
+        sab = np.zeros(H)
+        for s, e in enumerate(ids):
+            y_ref, s_abs = o.gemv_q4k(dn[e], H, I, g[s])
+            check_tolerance(y_dn[s], y_ref, s_abs, f"token {t} slot {s} down")
+            acc += np.float64(comb[s]) * y_dn[s].astype(np.float64)
+            sab += abs(float(comb[s])) * s_abs
+        assert np.array_equal(y_out, acc.astype(np.float32)), "combine differs from the slot-order f64 sum"
+        # one slot against the single-GEMV kernel: identical bits
+        single = to_host(mq.mq_gemv_q4k_q8(to_dev(dn[ids[0]].ravel()), to_dev(gpad[0]), H, KP))
+        assert np.array_equal(single.view(np.uint32), y_dn[0].copy().view(np.uint32))
+    # an out-of-range id is not read: NaN for that slot and the combine
+    bad = np.array([3, 64, 5, -1], np.int32)
+    y_b, y_o = mq.mq_gemv_q4k_grouped(dn_d, dnb, wl.n_experts, to_dev(bad), to_dev(gpad[:4].ravel()),
+                                      gpad.shape[1], H, KP, combine=to_dev(np.full(4, 0.25, np.float32)))
+    y_b, y_o = to_host(y_b), to_host(y_o)
+    assert np.all(np.isfinite(y_b[0])) and np.all(np.isnan(y_b[1])) and np.all(np.isnan(y_b[3]))
+    assert np.all(np.isnan(y_o))
+    del torch
