@@ -59,65 +59,121 @@ def sem(xs):
 
 # ------------------------------------------------------------------------------
 
-def upload_model(model, dev):
-    """Weights generated per matrix on the host, moved to HBM, host copy dropped."""
+def upload_model(model, dev, keep_host=False):
+    """Weights generated per matrix on the host and moved to HBM; the host
+    copies are kept only when the CPU baseline needs them."""
     import torch
     from block_quantized_gemv_amd import synth
     s = model.seed
     W = {"qkv": [], "o": [], "gu": [], "down": []}
+    H = {"qkv": [], "o": [], "gu": [], "down": []} if keep_host else None
     shapes = model.layer_shapes()
     for l in range(model.n_layers):
         for key, kind, (m, k) in zip(("qkv", "o", "gu", "down"), range(4), shapes):
-            W[key].append(torch.from_numpy(synth.q4k_matrix(s, (synth.KEY_LAYER, l, kind), m, k)).to(dev))
-    W["lm"] = torch.from_numpy(synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, model.hidden)).to(dev)
-    return W
+            a = synth.q4k_matrix(s, (synth.KEY_LAYER, l, kind), m, k)
+            W[key].append(torch.from_numpy(a).to(dev))
+            if keep_host:
+                H[key].append(a)
+    lm = synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, model.hidden)
+    W["lm"] = torch.from_numpy(lm).to(dev)
+    if keep_host:
+        H["lm"] = lm
+    return W, H
 
 
-def time_kernel_region(mq, model, W, dev, reps):
-    """Every q4_K GEMV of the step, in step order over all layers (each matrix
-    read once per pass, nothing reused from cache), each launch bracketed by
-    HIP events on the launching stream."""
+class HipEvents:
+    """hipEventCreate / hipEventElapsedTime on the HIP runtime torch loaded."""
+
+    def __init__(self):
+        import ctypes as C
+        import torch
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.C = C
+        self.hip = C.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.events = []
+
+    def create(self):
+        ev = self.C.c_void_p()
+        if self.hip.hipEventCreate(self.C.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.events.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.C.c_float()
+        if self.hip.hipEventElapsedTime(self.C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def gemv_kinds(model):
+    """The step's GEMV launches in order, with their kernel and algorithmic
+    bytes (weights + q8_0 activation in + output written)."""
+    from block_quantized_gemv_amd import workloads as wl
+    H, I, Q = model.hidden, model.inter, model.qkv_rows
+    tail = "mq::k_gemv_q4k<1,false>"
+    kinds = []
+    for _ in range(model.n_layers):
+        kinds += [("qkv", tail, wl.q4k_bytes(Q, H) + wl.q8_bytes(1, H) + 4 * Q),
+                  ("o", tail, wl.q4k_bytes(H, H) + wl.q8_bytes(1, H) + 4 * H),
+                  ("gate/up", "mq::k_gemv_q4k_swiglu", wl.q4k_bytes(2 * I, H) + wl.q8_bytes(1, H) + wl.q8_bytes(1, I)),
+                  ("down", tail, wl.q4k_bytes(H, I) + wl.q8_bytes(1, I) + 4 * H)]
+    kinds.append(("lm_head", "mq::k_gemv_q8_0<false>", wl.q8_bytes(model.vocab, H) + wl.q8_bytes(1, H) + 4 * model.vocab))
+    return kinds
+
+
+def time_kernels(mq, model, eager_chain, reps):
+    """Every GEMV of `reps` eager steps (the kernels and arguments the graph
+    replays), each timed by its own dispatch timestamps through
+    mq_time_next_launches, on the launching stream."""
     import torch
-    from block_quantized_gemv_amd import synth, workloads
-    H, I = model.hidden, model.inter
-    xq = {k: mq.mq_quantize_q8_0(torch.from_numpy(synth.normal_f32(99, (k,), (k,))).to(dev)) for k in (H, I)}
-    shapes = model.layer_shapes()
-    ys = [torch.empty(m, dtype=torch.float32, device=dev) for m, _ in shapes]
-    launches = []
-    for _ in range(reps):
-        for l in range(model.n_layers):
-            for i, key in enumerate(("qkv", "o", "gu", "down")):
-                m, k = shapes[i]
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                mq.mq_gemv_q4k_q8(W[key][l], xq[k], m, k, y=ys[i])
-                b.record()
-                launches.append((key, m, k, a, b))
+    kinds = gemv_kinds(model)
+    hip = HipEvents()
+    n = len(kinds) * reps
+    starts = [hip.create() for _ in range(n)]
+    stops = [hip.create() for _ in range(n)]
     torch.cuda.synchronize()
-    per = {}
-    tot_b = tot_t = 0.0
-    for key, m, k, a, b in launches:
-        us = a.elapsed_time(b) * 1e3
-        nbytes = workloads.q4k_bytes(m, k) + workloads.q8_bytes(1, k) + 4 * m
-        d = per.setdefault(key, {"m": m, "k": k, "bytes": nbytes, "us": []})
-        d["us"].append(us)
-        tot_b += nbytes
-        tot_t += us
-    n = len(launches)
-    shape_rows = {}
-    for key, d in per.items():
-        mu = float(np.mean(d["us"]))
-        shape_rows[key] = {"shape": f"{d['m']}x{d['k']}", "us": round(mu, 2), "sem_us": round(sem(d["us"]), 3),
-                           "GB_s": round(d["bytes"] / mu / 1e3, 1)}
-    avg_bytes, avg_us = tot_b / n, tot_t / n
-    achieved = avg_bytes / avg_us / 1e3
-    return {"bound": "hbm", "kernel": "mq::k_gemv_q4k<1,false>", "launches": n,
-            "bytes_per_launch": round(avg_bytes), "us_per_launch": round(avg_us, 3),
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "per_shape": shape_rows}
+    mq.mq_time_next_launches(starts, stops)
+    for _ in range(reps):
+        eager_chain.step(mq.MQ_EAGER)
+    torch.cuda.synchronize()
+    mq.mq_time_next_launches([], [])
+    us = [hip.elapsed_ms(a, b) * 1e3 for a, b in zip(starts, stops)]
+    hip.close()
+    by_kind, by_kernel = {}, {}
+    for i, u in enumerate(us):
+        name, kernel, nbytes = kinds[i % len(kinds)]
+        d = by_kind.setdefault(name, {"kernel": kernel, "bytes": nbytes, "us": []})
+        d["us"].append(u)
+        k = by_kernel.setdefault(kernel, {"bytes": 0, "us": 0.0, "n": 0})
+        k["bytes"] += nbytes
+        k["us"] += u
+        k["n"] += 1
+    dominant = max(by_kernel, key=lambda k: by_kernel[k]["us"])
+    dk = by_kernel[dominant]
+    avg_b, avg_us = dk["bytes"] / dk["n"], dk["us"] / dk["n"]
+    achieved = avg_b / avg_us / 1e3
+    per_shape = {name: {"kernel": d["kernel"], "us": round(float(np.mean(d["us"])), 3),
+                        "sem_us": round(sem(d["us"]), 4),
+                        "GB_s": round(d["bytes"] / float(np.mean(d["us"])) / 1e3, 1)}
+                 for name, d in by_kind.items()}
+    kernel_sum_ms = sum(us) / reps / 1e3
+    return {"bound": "hbm", "kernel": dominant, "launches": dk["n"], "bytes_per_launch": round(avg_b),
+            "us_per_launch": round(avg_us, 3), "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "timing": "hipExtLaunchKernelGGL dispatch events around each launch, eager steps",
+            "per_shape": per_shape}, kernel_sum_ms
 
 
-def cpu_baseline_decode(model, n_layers_sample):
+def cpu_baseline_decode(model, host_w, n_layers_sample):
     """The oracle, single thread, on the first layers of the step (all four
     GEMVs with their glue) plus the same fraction of lm_head rows."""
     import oracle
@@ -125,12 +181,8 @@ def cpu_baseline_decode(model, n_layers_sample):
     o = oracle.Oracle()
     s = model.seed
     H, I, eps = model.hidden, model.inter, model.eps
-    mats = []
-    for l in range(n_layers_sample):
-        mats.append([synth.q4k_matrix(s, (synth.KEY_LAYER, l, kind), m, k)
-                     for kind, (m, k) in enumerate(model.layer_shapes())])
     lm_rows = int(round(model.vocab * n_layers_sample / model.n_layers))
-    lm = synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, H)[:lm_rows]
+    lm = host_w["lm"][:lm_rows]
     h = synth.normal_f32(s, (synth.KEY_STEP_INPUTS,), (1, H))[0]
     try:
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
@@ -138,7 +190,8 @@ def cpu_baseline_decode(model, n_layers_sample):
         pass
     t0 = time.perf_counter()
     nbytes = 0
-    for qkv, ow, gu, dn in mats:
+    for l in range(n_layers_sample):
+        qkv, ow, gu, dn = (host_w[k][l] for k in ("qkv", "o", "gu", "down"))
         a = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel()
         t, _ = o.gemv_q4k(qkv, model.qkv_rows, H, a)
         b = o.quantize_q8_0(o.rmsnorm(t[:H], eps)).ravel()
@@ -155,9 +208,10 @@ def cpu_baseline_decode(model, n_layers_sample):
     frac = n_layers_sample / model.n_layers
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tok_per_s": round(frac / dt, 6), "seconds": round(dt, 2),
-            "sample": f"{n_layers_sample} of {model.n_layers} layers (4 GEMVs + glue each) and "
-                      f"{lm_rows} of {model.vocab} lm_head rows, single thread; tok/s scaled by "
-                      f"{model.n_layers}/{n_layers_sample}",
+            "sample": (f"{n_layers_sample} of {model.n_layers} layers (4 GEMVs + glue each) and "
+                       f"{lm_rows} of {model.vocab} lm_head rows of one decode step, single thread pinned to one core"
+                       + ("" if n_layers_sample == model.n_layers else
+                          f"; tok/s scaled by {model.n_layers}/{n_layers_sample}")),
             "cpu": _cpu_model()}
 
 
@@ -177,16 +231,14 @@ def run_decode(args, model, cpu_layers):
     from block_quantized_gemv_amd import synth
     dev = torch.device("cuda:0")
     log(f"generating and uploading {model.weight_bytes() / 1e9:.2f} GB of weights")
-    W = upload_model(model, dev)
+    W, host_w = upload_model(model, dev, keep_host=not args.no_cpu_baseline)
     X = torch.from_numpy(synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (16, model.hidden))).to(dev)
     chain = mq.DecodeChain(model, W, X)
+    eager = mq.DecodeChain(model, W, X, flags=mq.MQ_EAGER_ONLY)
     info = chain.info()
-    eager = mq.DecodeChain(model, W, X, flags=mq.MQ_EAGER_ONLY) if args.eager else None
     log(f"chain captured={info['captured']} nodes={info['n_nodes']}")
     for _ in range(args.warmup):
         chain.step(mq.MQ_GRAPH)
-        if eager:
-            eager.step(mq.MQ_EAGER)
     torch.cuda.synchronize()
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -202,8 +254,8 @@ def run_decode(args, model, cpu_layers):
     ms = wall * 1e3 / args.steps
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
-    eager_ms = None
-    if eager:
+    ab = None
+    if args.eager:
         # interleaved A/B on one binary: graph and eager steps alternate
         ga, ea = [], []
         for _ in range(args.steps):
@@ -216,12 +268,13 @@ def run_decode(args, model, cpu_layers):
         torch.cuda.synchronize()
         ga = [a.elapsed_time(b) for a, b in ga]
         ea = [a.elapsed_time(b) for a, b in ea]
-        eager_ms = {"graph_ms": round(float(np.mean(ga)), 4), "graph_sem_ms": round(sem(ga), 5),
-                    "eager_ms": round(float(np.mean(ea)), 4), "eager_sem_ms": round(sem(ea), 5)}
-        log(f"interleaved A/B: {eager_ms}")
+        ab = {"graph_ms": round(float(np.mean(ga)), 4), "graph_sem_ms": round(sem(ga), 5),
+              "eager_ms": round(float(np.mean(ea)), 4), "eager_sem_ms": round(sem(ea), 5)}
+        log(f"interleaved A/B: {ab}")
 
-    roof = time_kernel_region(mq, model, W, dev, args.kernel_reps)
-    log(f"q4_K GEMV: {roof['achieved']} GB/s per launch ({roof['frac'] * 100:.1f}% of 8 TB/s)")
+    roof, kernel_sum_ms = time_kernels(mq, model, eager, args.kernel_reps)
+    log(f"dominant kernel {roof['kernel']}: {roof['achieved']} GB/s per launch "
+        f"({roof['frac'] * 100:.1f}% of 8 TB/s); GEMV kernel sum {kernel_sum_ms:.3f} ms/step")
     nbytes = model.algorithmic_bytes()
     value = nbytes / (ms * 1e-3) / 1e9
     out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -233,17 +286,17 @@ def run_decode(args, model, cpu_layers):
                       "graph_nodes": info["n_nodes"], "bytes_per_step": nbytes},
            "tok_per_s": round(1e3 / ms, 2), "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
            "step_event_ms": round(float(np.mean(per_step)), 4), "step_event_sem_ms": round(sem(per_step), 5),
+           "gemv_kernel_sum_ms": round(kernel_sum_ms, 4),
            "roofline": roof}
-    if eager_ms:
-        out["ab_graph_vs_eager"] = eager_ms
+    if ab:
+        out["ab_graph_vs_eager"] = ab
     chain.close()
-    if eager:
-        eager.close()
+    eager.close()
     del W
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
-        out["cpu_baseline"] = cpu_baseline_decode(model, cpu_layers)
+        out["cpu_baseline"] = cpu_baseline_decode(model, host_w, cpu_layers)
     return out
 
 
@@ -383,9 +436,9 @@ def main():
         return
     from block_quantized_gemv_amd import workloads
     if args.workload == "7b":
-        out = run_decode(args, workloads.DECODE_7B, cpu_layers=2)
+        out = run_decode(args, workloads.DECODE_7B, cpu_layers=workloads.DECODE_7B.n_layers)
     elif args.workload == "05b":
-        out = run_decode(args, workloads.DECODE_05B, cpu_layers=8)
+        out = run_decode(args, workloads.DECODE_05B, cpu_layers=workloads.DECODE_05B.n_layers)
     elif args.workload == "single":
         out = run_single(args)
     elif args.workload == "batched":

@@ -70,6 +70,7 @@ SIGNATURES = {
     "mq_moe_create": ([C.POINTER(MoEDesc), _vp, C.POINTER(_vp)], _int),
     "mq_moe_step": ([_vp, _int, _vp], _int),
     "mq_test_set_fault": ([_u32], _int),
+    "mq_time_next_launches": ([C.POINTER(_vp), C.POINTER(_vp), _int], _int),
 }
 
 _LIB = None
@@ -128,6 +129,14 @@ def version() -> str:
 
 def mq_test_set_fault(mask: int):
     _check(lib().mq_test_set_fault(mask))
+
+
+def mq_time_next_launches(starts, stops):
+    """Arm dispatch-timestamp events for this thread's next len(starts) GEMV
+    launches (raw hipEvent_t handles as ints); empty lists clear the hook."""
+    n = len(starts)
+    a, b = (_vp * max(n, 1))(*starts), (_vp * max(n, 1))(*stops)
+    _check(lib().mq_time_next_launches(a, b, n))
 
 
 def mq_quantize_q8_0(x, xq=None, stream=None):

@@ -164,14 +164,20 @@ int enqueue(mq_chain* c, hipStream_t s) {
 }
 
 // Warm run, counter reset, then capture; failure to capture leaves an eager chain.
+int zero_counters(mq_chain* c, hipStream_t stream) {
+    hipError_t e = launch_set_i64(c->step, 0, stream);
+    if (e == hipSuccess && c->cur) e = launch_set_i64(c->cur, 0, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return hip_status(e, "counter reset");
+}
+
 int chain_finish(mq_chain* c, hipStream_t stream, bool eager_only) {
-    int rc = enqueue(c, stream);
+    int rc = zero_counters(c, stream);
+    if (rc == MQ_OK) rc = enqueue(c, stream);
     if (rc != MQ_OK) return rc;
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_status(e, "chain warm-up step");
-    if ((e = launch_set_i64(c->step, 0, stream)) != hipSuccess) return hip_status(e, "counter reset");
-    if (c->cur && (e = launch_set_i64(c->cur, 0, stream)) != hipSuccess) return hip_status(e, "counter reset");
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_status(e, "counter reset");
+    if ((rc = zero_counters(c, stream)) != MQ_OK) return rc;
     if (eager_only) return ok();
 
     const char* why = nullptr;
@@ -219,6 +225,13 @@ extern "C" {
 
 const char* mq_last_error(void) { return g_err.c_str(); }
 const char* mq_version(void) { return "libmq 0.1 (gfx950)"; }
+
+int mq_time_next_launches(const hipEvent_t* starts, const hipEvent_t* stops, int n) {
+    CHECK_ARG(n >= 0 && n <= 65536, "n=%d out of range", n);
+    CHECK_ARG(n == 0 || (starts && stops), "null event arrays");
+    set_next_launch_events(starts, stops, n);
+    return ok();
+}
 
 int mq_test_set_fault(unsigned fault_mask) {
     g_fault = fault_mask;
@@ -282,7 +295,7 @@ int mq_rmsnorm_quantize_q8_0(const float* x, void* xq, int64_t k, float eps, hip
     CHECK_ARG(x && xq && aligned(x, 4) && aligned(xq, 2), "null or misaligned pointer");
     CHECK_SHAPE(k >= 32 && k % 32 == 0 && k <= kMaxK, "k must be a positive multiple of 32");
     CHECK_ARG(eps >= 0.0f, "eps must be >= 0");
-    return hip_status(launch_rmsnorm_quantize(x, xq, k, eps, nullptr, 1, stream), "rmsnorm launch");
+    return hip_status(launch_rmsnorm_quantize(x, xq, k, eps, nullptr, 1, nullptr, stream), "rmsnorm launch");
 }
 
 int mq_swiglu_quantize_q8_0(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
@@ -355,6 +368,10 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     int64_t* step = c->step;
     const float* x_table = d->x_table;
     const int n_inputs = d->n_inputs;
+    // Per layer: RMSNorm->Q8 kernels feed QKV, O and gate/up; gate/up carries
+    // the SwiGLU->Q8 glue in its epilogue.  The first kernel of the step picks
+    // the input row with the device step counter; the last glue kernel
+    // advances it.
     const float* h_prev = nullptr;
     for (int l = 0; l < L; ++l) {
         uint8_t* q8 = c->q8_trace + (keep ? l * q8_layer : 0);
@@ -362,16 +379,16 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         uint8_t *qa = q8, *qb = q8 + qH, *qc = q8 + 2 * qH, *qg = q8 + 3 * qH;
         float *t = f, *o = f + QKV, *gu = f + QKV + H, *h = f + QKV + H + 2 * I;
         const void *wq = d->w_qkv[l], *wo = d->w_o[l], *wg = d->w_gu[l], *wd = d->w_down[l];
+        float* gu_keep = keep ? gu : nullptr;
         if (l == 0)
-            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(x_table, qa, H, eps, step, n_inputs, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(x_table, qa, H, eps, step, n_inputs, nullptr, s); });
         else
-            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qa, H, eps, nullptr, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qa, H, eps, nullptr, 1, nullptr, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, nullptr, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wg, qc, 0, gu, nullptr, nullptr, 2 * I, H, 1, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, qg, I, 1, I, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, nullptr, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, qc, gu_keep, qg, I, H, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s); });
         h_prev = h;
     }
@@ -379,7 +396,7 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const void* wlm = d->w_lm;
     float* logits = d->logits;
     const int64_t V = d->vocab;
-    c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qz, H, eps, nullptr, 1, s); });
+    c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qz, H, eps, nullptr, 1, step, s); });
     c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0(wlm, qz, logits, nullptr, V, H, s); });
     if (!keep) c->q8_bytes = c->f32_count = 0;
 

@@ -12,8 +12,22 @@
 // Lane work: a super-block (144 B = 16 B header + 128 B nibbles) is shared
 // by 4 lanes; lane j takes nibble chunk j (32 bytes = sub-blocks 2j, 2j+1:
 // low nibbles pair with q8_0 block 8sb+2j, high nibbles with 8sb+2j+1) plus
-// the 16-byte header, which the 4 lanes read as one broadcast.
+// the 16-byte header, which the 4 lanes read as one broadcast.  A row gets
+// an aligned slot of S lanes (S/4 super-blocks per pass, `passes` passes);
+// a wave holds 64/S rows (a tile).
+//
+// Streaming: each wave walks its (tile, pass) items with two register
+// buffers in ping-pong, so the loads of the next item are in flight while
+// the current one computes.  Loads are never skipped (lanes past the end
+// read a clamped, in-bounds address and contribute zero; items past a
+// wave's last one read the matrix's first bytes, one shared cache line),
+// which lets the compiler wait only for the item it is about to use.
+#include <hip/hip_ext.h>
+
+#include <vector>
+
 #include "common.hpp"
+#include "glue.hpp"
 #include "launch.hpp"
 
 namespace mq {
@@ -22,31 +36,33 @@ struct SBLoad {
     u32x4 hdr, qa, qb;
 };
 
-__device__ __forceinline__ void load_sb(const uint8_t* __restrict__ blk, int j, SBLoad& L) {
-    L.hdr = __builtin_nontemporal_load((const u32x4*)blk);
-    L.qa = __builtin_nontemporal_load((const u32x4*)(blk + 16 + 32 * j));
-    L.qb = __builtin_nontemporal_load((const u32x4*)(blk + 32 + 32 * j));
+// blk: super-block start; jo = 32*j, the lane's nibble chunk.  Ordinary
+// (temporal) loads: the three loads of a super-block touch the same cache
+// lines at different times, and a non-temporal hint lets those lines leave
+// the cache in between, which costs a second fetch from HBM (measured: 37%
+// longer on the 37888x3584 matrix).
+__device__ __forceinline__ void load_sb(const uint8_t* __restrict__ blk, int jo, SBLoad& L) {
+    L.hdr = *(const u32x4*)blk;
+    L.qa = *(const u32x4*)(blk + 16 + jo);
+    L.qb = *(const u32x4*)(blk + 32 + jo);
 }
 
 // Scales and mins of sub-blocks 2j and 2j+1 from the header.  Bytes s[0..3]
 // are hdr.y, s[4..7] hdr.z, s[8..11] hdr.w; sub-blocks j' < 4 keep sc and m
 // in the low six bits of s[j'] and s[j'+4]; j' >= 4 take their low four bits
 // from the nibbles of s[j'+4] and their top two from the top bits of s[j'-4]
-// (scale) and s[j'] (min).  The two sub-blocks of a lane sit in one 16-bit
-// half of each dword, so both are decoded at once.
+// (scale) and s[j'] (min).  A lane's two sub-blocks sit in one 16-bit half
+// of each dword, so both are decoded at once.
 struct SBScales {
     double d, dmin, m0, m1;
     int sc0, sc1;
 };
-__device__ __forceinline__ void decode_scales(const u32x4& hdr, int j, SBScales& s) {
-    const int sh = (j & 1) * 16;
+__device__ __forceinline__ void decode_scales(const u32x4& hdr, int sh, bool low, SBScales& s) {
     const uint32_t a2 = (hdr.y >> sh) & 0xFFFFu;
     const uint32_t b2 = (hdr.z >> sh) & 0xFFFFu;
     const uint32_t c2 = (hdr.w >> sh) & 0xFFFFu;
-    const uint32_t sc_lo = a2 & 0x3F3Fu, m_lo = b2 & 0x3F3Fu;
-    const uint32_t sc_hi = (c2 & 0x0F0Fu) | ((a2 & 0xC0C0u) >> 2);
-    const uint32_t m_hi = ((c2 >> 4) & 0x0F0Fu) | ((b2 & 0xC0C0u) >> 2);
-    const uint32_t scp = j < 2 ? sc_lo : sc_hi, mp = j < 2 ? m_lo : m_hi;
+    const uint32_t scp = low ? (a2 & 0x3F3Fu) : ((c2 & 0x0F0Fu) | ((a2 & 0xC0C0u) >> 2));
+    const uint32_t mp = low ? (b2 & 0x3F3Fu) : (((c2 >> 4) & 0x0F0Fu) | ((b2 & 0xC0C0u) >> 2));
     s.sc0 = (int)(scp & 0xFFu);
     s.sc1 = (int)(scp >> 8);
     s.m0 = (double)(int)(mp & 0xFFu);
@@ -68,143 +84,192 @@ __device__ __forceinline__ void sb_isums(const SBLoad& L, const StagedPair& x, i
     i1 = b;
 }
 
-// acc += d8_0*(d*sc0*i0 - dmin*m0*ysum_0) + d8_1*(d*sc1*i1 - dmin*m1*ysum_1).
-// Each product is exact in f64 (sc*isum < 2^22, d8*ysum < 2^24 significant
-// bits), so only the additions round.
-__device__ __forceinline__ double sb_fixup(const SBScales& s, const StagedPair& x, int i0, int i1,
-                                           double acc) {
-    const double t = fma((double)(s.sc1 * i1), x.d1, (double)(s.sc0 * i0) * x.d0);
+// d8_0*(d*sc0*i0 - dmin*m0*ysum_0) + d8_1*(d*sc1*i1 - dmin*m1*ysum_1) in f64.
+// Every product is exact (sc*isum < 2^22 and d8*ysum < 2^24 significant
+// bits against 53), so only the additions round.
+__device__ __forceinline__ double sb_value(const SBScales& s, const StagedPair& x, int i0, int i1) {
+    const double t = fma((double)__mul24(s.sc1, i1), x.d1, (double)__mul24(s.sc0, i0) * x.d0);
     const double u = fma(s.m1, x.ds1, s.m0 * x.ds0);
-    acc = fma(s.d, t, acc);
-    return fma(-s.dmin, u, acc);
+    return fma(s.d, t, -s.dmin * u);
+}
+
+// Per-lane constants of the lane layout.
+struct Lanes {
+    int lane, log2s, S, R, gpp, row_local, g, j, sh;
+    bool low;
+    __device__ Lanes(int log2s_) {
+        lane = threadIdx.x & 63;
+        log2s = log2s_;
+        S = 1 << log2s;
+        R = 64 >> log2s;
+        gpp = S >> 2;
+        row_local = lane >> log2s;
+        g = (lane & (S - 1)) >> 2;
+        j = lane & 3;
+        sh = (j & 1) * 16;
+        low = j < 2;
+    }
+};
+
+// LDS byte offset of the staged pair that lane (g, j) needs in pass p:
+// pair P = 4*(p*gpp + g) + j.
+__device__ __forceinline__ int pair_of(const Lanes& ln, int p) { return 4 * (p * ln.gpp + ln.g) + ln.j; }
+
+// One q4_K super-block item for NC activation columns: adds the lane's
+// contribution to acc[] (masked by `valid`).
+template <int NC, bool DUMP>
+__device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P, bool valid,
+                                        const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
+                                        int32_t* __restrict__ dump, int64_t dump_row_off) {
+    SBScales s;
+    decode_scales(L.hdr, ln.sh, ln.low, s);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        StagedPair x;
+        read_pair(lds + c * col_bytes, P, x, true);
+        int i0, i1;
+        sb_isums(L, x, i0, i1);
+        const double v = sb_value(s, x, i0, i1);
+        acc[c] += valid ? v : 0.0;
+        if (DUMP && valid) {
+            dump[dump_row_off + 2 * P] = i0;
+            dump[dump_row_off + 2 * P + 1] = i1;
+        }
+    }
 }
 
 // --------------------------------------------------------------------------
-// Full staging: all ncols activation columns live in LDS; each wave walks its
-// (tile, pass) items with the next item's loads in flight while the current
-// one computes.
+// Full staging: all NC activation columns live in LDS.  Wave w owns tiles
+// w, w+W, w+2W, ... (W = waves in the grid); its items are (tile, pass) in
+// that order.
 template <int NC, bool DUMP>
 __global__ __launch_bounds__(256) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
     int M, int nsb, int log2s, int passes, int n_tiles) {
     extern __shared__ __align__(16) uint8_t lds[];
+    const Lanes ln(log2s);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
+    const int W = gridDim.x * (blockDim.x >> 6);
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
+    const int n_items = my_tiles * passes;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+
+    auto where = [&](int i, const uint8_t*& p, bool& valid, int& row, int& pass) {
+        if (i >= n_items) { p = w; valid = false; row = M; pass = 0; return; }
+        const int t = wave + (i / passes) * W;
+        pass = i % passes;
+        row = t * ln.R + ln.row_local;
+        const int sb = pass * ln.gpp + ln.g;
+        valid = row < M && sb < nsb;
+        p = valid ? w + row * row_bytes + sb * kQ4KBytes : w;
+    };
+
+    SBLoad A, B;
+    const uint8_t* pa;
+    bool va = false;
+    int ra = 0, pa_pass = 0;
+    if (n_items > 0) {
+        where(0, pa, va, ra, pa_pass);
+        load_sb(pa, 32 * ln.j, A);
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
         stage_q8(xq + c * xq_col_bytes, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x,
                  (DUMP && blockIdx.x == 0 && c == 0) ? dump_ysum : nullptr);
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
-    const int S = 1 << log2s, R = 64 >> log2s, gpp = S >> 2;
-    const int row_local = lane >> log2s, g = (lane & (S - 1)) >> 2, j = lane & 3;
-    const int wave_stride = gridDim.x * (blockDim.x >> 6);
-    int tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (tile >= n_tiles) return;
-
-    int p = 0;
-    SBLoad cur, nxt;
-    int row = tile * R + row_local, sb = g;
-    bool ok = row < M && sb < nsb;
-    if (ok) load_sb(w + ((int64_t)row * nsb + sb) * kQ4KBytes, j, cur);
     double acc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.0;
 
-    while (true) {
-        int ntile = tile, np = p + 1;
-        if (np == passes) { np = 0; ntile = tile + wave_stride; }
-        const bool more = ntile < n_tiles;
-        const int nrow = ntile * R + row_local, nsbi = np * gpp + g;
-        const bool nok = more && nrow < M && nsbi < nsb;
-        if (nok) load_sb(w + ((int64_t)nrow * nsb + nsbi) * kQ4KBytes, j, nxt);
+    auto finish = [&](int row, int pass) {
+        if (pass != passes - 1) return;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const double v = group_sum_f64(acc[c], ln.log2s);
+            if ((ln.lane & (ln.S - 1)) == 0 && row < M) y[(int64_t)row * NC + c] = (float)v;
+            acc[c] = 0.0;
+        }
+    };
 
-        if (ok) {
-            SBScales s;
-            decode_scales(cur.hdr, j, s);
-            const int P = 4 * sb + j;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                StagedPair x;
-                read_pair(lds + c * col_bytes, P, x, true);
-                int i0, i1;
-                sb_isums(cur, x, i0, i1);
-                acc[c] = sb_fixup(s, x, i0, i1, acc[c]);
-                if (DUMP) {
-                    dump_isum[((int64_t)c * M + row) * nb + 2 * P] = i0;
-                    dump_isum[((int64_t)c * M + row) * nb + 2 * P + 1] = i1;
-                }
-            }
+    for (int i = 0; i < n_items; i += 2) {
+        const uint8_t* pb;
+        bool vb;
+        int rb, pb_pass;
+        where(i + 1, pb, vb, rb, pb_pass);
+        load_sb(pb, 32 * ln.j, B);
+        sb_item<NC, DUMP>(A, ln, pair_of(ln, pa_pass), va, lds, col_bytes, acc, dump_isum, (int64_t)ra * nb);
+        finish(ra, pa_pass);
+        where(i + 2, pa, va, ra, pa_pass);
+        load_sb(pa, 32 * ln.j, A);
+        if (i + 1 < n_items) {
+            sb_item<NC, DUMP>(B, ln, pair_of(ln, pb_pass), vb, lds, col_bytes, acc, dump_isum, (int64_t)rb * nb);
+            finish(rb, pb_pass);
         }
-        if (p == passes - 1) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const double v = group_sum_f64(acc[c], log2s);
-                if ((lane & (S - 1)) == 0 && row < M) y[(int64_t)row * NC + c] = (float)v;
-                acc[c] = 0.0;
-            }
-        }
-        if (!more) break;
-        tile = ntile; p = np; row = nrow; sb = nsbi; ok = nok; cur = nxt;
     }
 }
 
 // --------------------------------------------------------------------------
 // Split-k: workgroup column s covers super-blocks [16s, 16s+16) of every row
-// (one staging group per activation column), one row per wave tile; the f64
-// partial of each (split, row, column) goes to `part` and a second kernel
+// (one staging group per activation column), rows in slots of 64 lanes; the
+// f64 partial of each (split, row, column) goes to `part` and a second kernel
 // sums the splits in order.
 template <int NC>
 __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     double* __restrict__ part, int M, int nsb) {
     extern __shared__ __align__(16) uint8_t lds[];
+    const Lanes ln(6);
     const int split = blockIdx.y;
     const int sb0 = 16 * split;
     const int nsb_s = min(16, nsb - sb0);
+    const int W = gridDim.x * (blockDim.x >> 6);
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int n_items = wave < M ? (M - 1 - wave) / W + 1 : 0;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+    const bool lane_ok = ln.g < nsb_s;
+
+    auto where = [&](int i, const uint8_t*& p, int& row) {
+        if (i >= n_items) { p = w; row = 0; return; }
+        row = wave + i * W;
+        p = w + row * row_bytes + (lane_ok ? (sb0 + ln.g) * kQ4KBytes : 0);
+    };
+    SBLoad A, B;
+    const uint8_t* pa;
+    int ra = 0;
+    if (n_items > 0) {
+        where(0, pa, ra);
+        load_sb(pa, 32 * ln.j, A);
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
         stage_q8(xq + c * xq_col_bytes, 8 * sb0, 8 * nsb_s, lds + c * kStageGroupBytes, threadIdx.x,
                  blockDim.x, nullptr);
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, g = lane >> 2, j = lane & 3;
-    const int wave_stride = gridDim.x * (blockDim.x >> 6);
-    int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const bool active = g < nsb_s;
-    SBLoad cur, nxt;
-    if (active) load_sb(w + ((int64_t)row * nsb + sb0 + g) * kQ4KBytes, j, cur);
-    while (true) {
-        const int nrow = row + wave_stride;
-        const bool more = nrow < M;
-        if (more && active) load_sb(w + ((int64_t)nrow * nsb + sb0 + g) * kQ4KBytes, j, nxt);
+    auto item = [&](const SBLoad& L, int row) {
         double acc[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[c] = 0.0;
-        if (active) {
-            SBScales s;
-            decode_scales(cur.hdr, j, s);
-            const int P = 4 * g + j;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                StagedPair x;
-                read_pair(lds + c * kStageGroupBytes, P, x, true);
-                int i0, i1;
-                sb_isums(cur, x, i0, i1);
-                acc[c] = sb_fixup(s, x, i0, i1, 0.0);
-            }
-        }
+        sb_item<NC, false>(L, ln, pair_of(ln, 0), lane_ok, lds, kStageGroupBytes, acc, nullptr, 0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const double v = wave_sum_f64(acc[c]);
-            if (lane == 0) part[((int64_t)split * M + row) * NC + c] = v;
+            if (ln.lane == 0) part[((int64_t)split * M + row) * NC + c] = v;
         }
-        if (!more) break;
-        row = nrow;
-        cur = nxt;
+    };
+    for (int i = 0; i < n_items; i += 2) {
+        const uint8_t* pb;
+        int rb;
+        where(i + 1, pb, rb);
+        load_sb(pb, 32 * ln.j, B);
+        item(A, ra);
+        where(i + 2, pa, ra);
+        load_sb(pa, 32 * ln.j, A);
+        if (i + 1 < n_items) item(B, rb);
     }
 }
 
@@ -218,11 +283,12 @@ __global__ void k_splitk_finalize(const double* __restrict__ part, float* __rest
 }
 
 // --------------------------------------------------------------------------
-// Grouped GEMV for routed experts.  Without a combine, each wave work item
-// is (slot, tile); with one, a wave computes a tile for every slot in slot
-// order and forms sum_s combine[s]*y_s in f64.  Per slot the lane layout,
-// arithmetic and reduction are those of k_gemv_q4k, so a slot's result
-// equals the single GEMV on that expert.
+// Grouped GEMV for routed experts.  Without a combine, the wave work items
+// are (slot, tile, pass); with one, a wave owns a tile and walks (slot, pass)
+// in slot order, forming sum_s combine[s]*y_s in f64 at the end of each
+// slot.  Per slot the lane layout, arithmetic and reduction are those of
+// k_gemv_q4k with the same layout, so a slot's result equals the single GEMV
+// on that expert.
 template <bool COMBINE>
 __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
     const uint8_t* __restrict__ w_all, int64_t expert_bytes, int n_experts,
@@ -231,61 +297,190 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
     const int64_t* __restrict__ out_row, int64_t out_rows, int M, int nsb, int log2s, int passes,
     int n_tiles) {
     extern __shared__ __align__(16) uint8_t lds[];
+    const Lanes ln(log2s);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
     const int n_cols = xq_stride ? n_sel : 1;
+    const int W = gridDim.x * (blockDim.x >> 6);
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    // COMBINE: units are tiles, each of n_sel*passes items; else units are
+    // (slot, tile) pairs of `passes` items.
+    const int n_units = COMBINE ? n_tiles : n_tiles * n_sel;
+    const int per_unit = COMBINE ? n_sel * passes : passes;
+    const int my_units = wave < n_units ? (n_units - 1 - wave) / W + 1 : 0;
+    const int n_items = my_units * per_unit;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+    float* yo = y_out;
+
+    struct Meta {
+        int row, pass, slot;
+        bool valid, slot_ok;
+    };
+    auto where = [&](int i, const uint8_t*& p, Meta& m) {
+        if (i >= n_items) { p = w_all; m = Meta{M, 0, 0, false, false}; return; }
+        const int u = wave + (i / per_unit) * W;
+        const int r = i % per_unit;
+        const int tile = COMBINE ? u : u % n_tiles;
+        m.slot = COMBINE ? r / passes : u / n_tiles;
+        m.pass = r % passes;
+        m.row = tile * ln.R + ln.row_local;
+        const int sb = m.pass * ln.gpp + ln.g;
+        const int e = ids[m.slot];
+        m.slot_ok = e >= 0 && e < n_experts;
+        m.valid = m.slot_ok && m.row < M && sb < nsb;
+        p = m.valid ? w_all + e * expert_bytes + m.row * row_bytes + sb * kQ4KBytes : w_all;
+    };
+
+    SBLoad A, B;
+    const uint8_t* pa;
+    Meta ma{0, 0, 0, false, false};
+    if (n_items > 0) {
+        where(0, pa, ma);
+        load_sb(pa, 32 * ln.j, A);
+    }
     for (int c = 0; c < n_cols; ++c)
         stage_q8(xq + c * xq_stride, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x, nullptr);
     __syncthreads();
-
-    const int lane = threadIdx.x & 63;
-    const int S = 1 << log2s, R = 64 >> log2s, gpp = S >> 2;
-    const int row_local = lane >> log2s, g = (lane & (S - 1)) >> 2, j = lane & 3;
-    const int wave_stride = gridDim.x * (blockDim.x >> 6);
-    const int n_items = COMBINE ? n_tiles : n_tiles * n_sel;
-    float* yo = y_out;
+    if (n_items == 0) return;
     if (COMBINE && out_row) yo += (int64_t)(*out_row % out_rows) * M;
 
-    for (int item = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); item < n_items;
-         item += wave_stride) {
-        const int tile = COMBINE ? item : item % n_tiles;
-        const int s_begin = COMBINE ? 0 : item / n_tiles;
-        const int s_end = COMBINE ? n_sel : s_begin + 1;
-        const int row = tile * R + row_local;
-        double comb = 0.0;
-        for (int s = s_begin; s < s_end; ++s) {
-            const int e = ids[s];
-            const bool valid = e >= 0 && e < n_experts;
-            const uint8_t* wb = w_all + (int64_t)(valid ? e : 0) * expert_bytes;
-            const uint8_t* xs = lds + (xq_stride ? s : 0) * col_bytes;
-            double acc = 0.0;
-            for (int p = 0; p < passes; ++p) {
-                const int sb = p * gpp + g;
-                if (valid && row < M && sb < nsb) {
-                    SBLoad L;
-                    load_sb(wb + ((int64_t)row * nsb + sb) * kQ4KBytes, j, L);
-                    SBScales sc;
-                    decode_scales(L.hdr, j, sc);
-                    StagedPair x;
-                    read_pair(xs, 4 * sb + j, x, true);
-                    int i0, i1;
-                    sb_isums(L, x, i0, i1);
-                    acc = sb_fixup(sc, x, i0, i1, acc);
-                }
-            }
-            const double v = group_sum_f64(acc, log2s);
-            const float ys = valid ? (float)v : __builtin_nanf("");
-            if ((lane & (S - 1)) == 0 && row < M) {
-                if (y) y[(int64_t)s * M + row] = ys;
-                if (COMBINE) comb += (double)combine[s] * (double)ys;
+    double acc[1] = {0.0};
+    double comb = 0.0;
+    auto item = [&](const SBLoad& L, const Meta& m) {
+        const uint8_t* xs = lds + (xq_stride ? m.slot : 0) * col_bytes;
+        sb_item<1, false>(L, ln, pair_of(ln, m.pass), m.valid, xs, col_bytes, acc, nullptr, 0);
+        if (m.pass != passes - 1) return;
+        const double v = group_sum_f64(acc[0], ln.log2s);
+        acc[0] = 0.0;
+        const float ys = m.slot_ok ? (float)v : __builtin_nanf("");
+        const bool writer = (ln.lane & (ln.S - 1)) == 0 && m.row < M;
+        if (writer && y) y[(int64_t)m.slot * M + m.row] = ys;
+        if (COMBINE) {
+            comb += (double)combine[m.slot] * (double)ys;
+            if (m.slot == n_sel - 1) {
+                if (writer) yo[m.row] = (float)comb;
+                comb = 0.0;
             }
         }
-        if (COMBINE && (lane & (S - 1)) == 0 && row < M) yo[row] = (float)comb;
+    };
+    for (int i = 0; i < n_items; i += 2) {
+        const uint8_t* pb;
+        Meta mb;
+        where(i + 1, pb, mb);
+        load_sb(pb, 32 * ln.j, B);
+        item(A, ma);
+        where(i + 2, pa, ma);
+        load_sb(pa, 32 * ln.j, A);
+        if (i + 1 < n_items) item(B, mb);
+    }
+}
+
+
+// --------------------------------------------------------------------------
+// Gate/up GEMV with the SwiGLU stand-in fused.  Workgroup u owns outputs
+// [32u, 32u+32): gate rows 32u..32u+31 and up rows inter+32u..+31, so it can
+// finish whole q8_0 blocks itself.  Rows use 16-lane slots (4 rows a tile);
+// wave q takes gate rows 32u+8q..+7 and the matching up rows (4 tiles).
+// The per-row arithmetic and reduction are those of k_gemv_q4k with 16-lane
+// slots, so gate and up values are the ones the plain GEMV would write.
+__global__ __launch_bounds__(256) void k_gemv_q4k_swiglu(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* __restrict__ gu_out,
+    uint8_t* __restrict__ g_q8, int inter, int nsb) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ float gu_s[64];
+    const Lanes ln(4);
+    const int nb = nsb * 8;
+    const int passes = (nsb + 3) / 4;
+    const int n_items = 4 * passes;
+    const int u = blockIdx.x, q = threadIdx.x >> 6;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+
+    // item i: tile st = i / passes (0,1: gate rows; 2,3: up rows), pass i % passes
+    auto row_of = [&](int st) { return (st >> 1) * inter + 32 * u + 8 * q + 4 * (st & 1) + ln.row_local; };
+    auto where = [&](int i, const uint8_t*& p, bool& valid, int& st, int& pass) {
+        if (i >= n_items) { p = w; valid = false; st = 0; pass = 0; return; }
+        st = i / passes;
+        pass = i % passes;
+        const int sb = pass * ln.gpp + ln.g;
+        valid = sb < nsb;
+        p = valid ? w + row_of(st) * row_bytes + sb * kQ4KBytes : w;
+    };
+
+    SBLoad A, B;
+    const uint8_t* pa;
+    bool va;
+    int sa, pa_pass;
+    where(0, pa, va, sa, pa_pass);
+    load_sb(pa, 32 * ln.j, A);
+    stage_q8(xq, 0, nb, lds, threadIdx.x, blockDim.x, nullptr);
+    __syncthreads();
+
+    double acc[1] = {0.0};
+    auto item = [&](const SBLoad& L, bool valid, int st, int pass) {
+        sb_item<1, false>(L, ln, pair_of(ln, pass), valid, lds, 0, acc, nullptr, 0);
+        if (pass != passes - 1) return;
+        const float v = (float)group_sum_f64(acc[0], 4);
+        acc[0] = 0.0;
+        if ((ln.lane & 15) == 0) {
+            gu_s[(st >> 1) * 32 + 8 * q + 4 * (st & 1) + ln.row_local] = v;
+            if (gu_out) gu_out[row_of(st)] = v;
+        }
+    };
+    for (int i = 0; i < n_items; i += 2) {
+        const uint8_t* pb;
+        bool vb;
+        int sb_, pb_pass;
+        where(i + 1, pb, vb, sb_, pb_pass);
+        load_sb(pb, 32 * ln.j, B);
+        item(A, va, sa, pa_pass);
+        where(i + 2, pa, va, sa, pa_pass);
+        load_sb(pa, 32 * ln.j, A);
+        if (i + 1 < n_items) item(B, vb, sb_, pb_pass);
+    }
+    __syncthreads();
+    if (q == 0) {
+        const int i = ln.lane;
+        const float a = i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
+        quantize_lane(a, g_q8 + (int64_t)u * kQ8Bytes, i & 31, i < 32);
     }
 }
 
 // --------------------------------------------------------------------------
 // Host side.
+
+struct LaunchEvents {
+    std::vector<hipEvent_t> starts, stops;
+    size_t next = 0;
+};
+static thread_local LaunchEvents t_events;
+
+void set_next_launch_events(const hipEvent_t* starts, const hipEvent_t* stops, int n) {
+    t_events.starts.assign(starts, starts + n);
+    t_events.stops.assign(stops, stops + n);
+    t_events.next = 0;
+}
+
+bool take_next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+    if (t_events.next >= t_events.starts.size()) return false;
+    *start = t_events.starts[t_events.next];
+    *stop = t_events.stops[t_events.next];
+    ++t_events.next;
+    return true;
+}
+
+// Launch through hipExtLaunchKernelGGL when a measurement hook is armed.
+// The stream is drained first: a dispatch queued behind a running kernel
+// would otherwise take its start timestamp before it can begin executing.
+#define MQ_LAUNCH(kernel, grid, block, lds, stream, ...)                                         \
+    do {                                                                                        \
+        hipEvent_t ev0_, ev1_;                                                                  \
+        if (take_next_launch_events(&ev0_, &ev1_)) {                                            \
+            (void)hipStreamSynchronize(stream);                                                 \
+            hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev0_, ev1_, 0, __VA_ARGS__); \
+        } else {                                                                                \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                  \
+        }                                                                                       \
+    } while (0)
 
 int device_cu_count() {
     static int cached[64] = {0};
@@ -300,28 +495,59 @@ int device_cu_count() {
     return cached[dev];
 }
 
+// Resident 256-thread workgroups per CU for a kernel with `lds` bytes of
+// dynamic LDS (occupancy query, cached).
+static int blocks_per_cu(const void* fn, int lds) {
+    struct Entry { const void* fn; int lds, n; };
+    static Entry cache[256];
+    static int used = 0;
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn && cache[i].lds == lds) return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, lds) != hipSuccess || n <= 0) n = 2;
+    if (used < 256) cache[used++] = Entry{fn, lds, n};
+    return n;
+}
+
 static int ceil_log2(int v) {
     int l = 0;
     while ((1 << l) < v) ++l;
     return l;
 }
 
-Q4KPlan plan_q4k(int64_t m, int nsb) {
-    Q4KPlan p;
-    p.log2s = ceil_log2(4 * nsb);
-    if (p.log2s < 2) p.log2s = 2;
-    if (p.log2s > 6) p.log2s = 6;
-    p.rows_per_tile = 64 >> p.log2s;
-    const int gpp = (1 << p.log2s) / 4;
-    p.passes = (nsb + gpp - 1) / gpp;
-    p.n_tiles = (int)((m + p.rows_per_tile - 1) / p.rows_per_tile);
-    return p;
+// Lane layout for m rows of nsb super-blocks, `mult` independent copies
+// (grouped slots): prefer enough tiles to give every CU ~16 waves, then few
+// idle lanes, then the narrowest slot (cheapest row reduction).
+Q4KPlan plan_q4k_mult(int64_t m, int nsb, int mult) {
+    const int64_t target = (int64_t)device_cu_count() * 16;
+    Q4KPlan best{6, 1, 1, 1};
+    double best_score = -1.0;
+    const int lo = nsb < 4 ? ceil_log2(4 * nsb) : 4;
+    for (int l = (lo < 2 ? 2 : lo); l <= 6; ++l) {
+        const int gpp = (1 << l) / 4;
+        const int passes = (nsb + gpp - 1) / gpp;
+        const double used = (double)nsb / (passes * gpp);
+        const int64_t tiles = (m + (64 >> l) - 1) / (64 >> l);
+        const double work = (double)(tiles * mult < target ? tiles * mult : target);
+        const double score = work * used;
+        if (score > best_score * 1.0001) {
+            best_score = score;
+            best = Q4KPlan{l, 64 >> l, passes, (int)tiles};
+        }
+    }
+    return best;
 }
 
-static int grid_for(int n_waves) {
-    const int cap = device_cu_count() * 8;
-    int g = (n_waves + 3) / 4;
-    return g < cap ? (g > 0 ? g : 1) : cap;
+Q4KPlan plan_q4k(int64_t m, int nsb) { return plan_q4k_mult(m, nsb, 1); }
+
+// Waves to launch for `units` equal work units: all resident at once and
+// every wave with the same number of units (or one fewer).
+static int balanced_grid(int64_t units, const void* fn, int lds) {
+    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, lds) * 4;
+    const int64_t k = (units + wmax - 1) / wmax;
+    const int64_t waves = (units + k - 1) / k;
+    const int64_t grid = (waves + 3) / 4;
+    return (int)(grid > 0 ? grid : 1);
 }
 
 template <int NC, bool DUMP>
@@ -330,9 +556,10 @@ static hipError_t launch_nc(const void* w, const void* xq, int64_t xq_col_bytes,
                             hipStream_t stream) {
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = NC * stage_bytes(nsb * 8);
-    hipLaunchKernelGGL((k_gemv_q4k<NC, DUMP>), dim3(grid_for(p.n_tiles)), dim3(256), lds, stream,
-                       (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, y, dump_isum, dump_ysum,
-                       (int)m, nsb, p.log2s, p.passes, p.n_tiles);
+    const void* fn = (const void*)k_gemv_q4k<NC, DUMP>;
+    MQ_LAUNCH((k_gemv_q4k<NC, DUMP>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds, stream,
+              (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, y, dump_isum, dump_ysum, (int)m, nsb,
+              p.log2s, p.passes, p.n_tiles);
     return hipGetLastError();
 }
 
@@ -361,11 +588,12 @@ static hipError_t launch_split_nc(const void* w, const void* xq, int64_t xq_col_
                                   double* part, int64_t m, int nsb, hipStream_t stream) {
     const int n_split = (nsb + 15) / 16;
     const int lds = NC * kStageGroupBytes;
-    const int cap = device_cu_count() * 8;
-    int gx = (int)((m + 3) / 4);
-    const int per_split_cap = (cap + n_split - 1) / n_split;
-    if (gx > per_split_cap) gx = per_split_cap;
-    hipLaunchKernelGGL((k_gemv_q4k_splitk<NC>), dim3(gx, n_split), dim3(256), lds, stream,
+    const void* fn = (const void*)k_gemv_q4k_splitk<NC>;
+    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, lds) * 4 / n_split;
+    const int64_t k = (m + (wmax > 0 ? wmax : 1) - 1) / (wmax > 0 ? wmax : 1);
+    const int64_t waves = (m + k - 1) / k;
+    const int gx = (int)((waves + 3) / 4);
+    MQ_LAUNCH((k_gemv_q4k_splitk<NC>), dim3(gx, n_split), dim3(256), lds, stream,
                        (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, part, (int)m, nsb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -391,25 +619,37 @@ hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_
     }
 }
 
+hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, float* gu_out, void* g_q8, int64_t inter,
+                                  int64_t k, hipStream_t stream) {
+    const int nsb = (int)(k / 256);
+    const int lds = stage_bytes(nsb * 8);
+    MQ_LAUNCH(k_gemv_q4k_swiglu, dim3((unsigned)(inter / 32)), dim3(256), lds, stream, (const uint8_t*)w,
+                       (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,
                                    const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
                                    float* y, const float* combine, float* y_out,
                                    const int64_t* out_row, int64_t out_rows, int64_t m, int64_t k,
                                    hipStream_t stream) {
     const int nsb = (int)(k / 256);
-    const Q4KPlan p = plan_q4k(m, nsb);
+    const Q4KPlan p = plan_q4k_mult(m, nsb, combine ? 1 : n_sel);
     const int lds = (xq_stride ? n_sel : 1) * stage_bytes(nsb * 8);
-    const int n_items = combine ? p.n_tiles : p.n_tiles * n_sel;
-    if (combine)
-        hipLaunchKernelGGL((k_gemv_q4k_grouped<true>), dim3(grid_for(n_items)), dim3(256), lds, stream,
+    const int64_t units = combine ? p.n_tiles : (int64_t)p.n_tiles * n_sel;
+    if (combine) {
+        const void* fn = (const void*)k_gemv_q4k_grouped<true>;
+        MQ_LAUNCH((k_gemv_q4k_grouped<true>), dim3(balanced_grid(units, fn, lds)), dim3(256), lds, stream,
                            (const uint8_t*)w_all, expert_bytes, n_experts, ids, n_sel,
                            (const uint8_t*)xq, xq_stride, y, combine, y_out, out_row, out_rows, (int)m,
                            nsb, p.log2s, p.passes, p.n_tiles);
-    else
-        hipLaunchKernelGGL((k_gemv_q4k_grouped<false>), dim3(grid_for(n_items)), dim3(256), lds, stream,
+    } else {
+        const void* fn = (const void*)k_gemv_q4k_grouped<false>;
+        MQ_LAUNCH((k_gemv_q4k_grouped<false>), dim3(balanced_grid(units, fn, lds)), dim3(256), lds, stream,
                            (const uint8_t*)w_all, expert_bytes, n_experts, ids, n_sel,
                            (const uint8_t*)xq, xq_stride, y, combine, y_out, out_row, out_rows, (int)m,
                            nsb, p.log2s, p.passes, p.n_tiles);
+    }
     return hipGetLastError();
 }
 

@@ -4,12 +4,54 @@
 // aligned because rows hold an even number of blocks): four 16-byte loads
 // plus one dword.  The first block's codes start 2 bytes into the pair and
 // are realigned with v_alignbyte; the second block's codes are aligned.
-// Rows get aligned lane slots as in the q4_K kernel; the activation is
-// staged in LDS with the same layout.
+// Rows get aligned slots of S lanes, a wave holds 64/S rows; the activation
+// is staged in LDS with the same layout as the q4_K kernels, and items are
+// streamed with the same ping-pong register buffers.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mq {
+
+struct PairLoad {
+    u32x4 v0, v1, v2, v3;
+    uint32_t v4;
+};
+
+// Ordinary loads: neighbouring lanes' pairs share cache lines across the
+// five instructions, so a non-temporal hint would cost re-fetches.
+__device__ __forceinline__ void load_pair(const uint8_t* __restrict__ p, PairLoad& L) {
+    L.v0 = *(const u32x4_a4*)(p);
+    L.v1 = *(const u32x4_a4*)(p + 16);
+    L.v2 = *(const u32x4_a4*)(p + 32);
+    L.v3 = *(const u32x4_a4*)(p + 48);
+    L.v4 = *(const uint32_t*)(p + 64);
+}
+
+template <bool DUMP>
+__device__ __forceinline__ double pair_item(const PairLoad& L, const uint8_t* __restrict__ lds, int P,
+                                            int32_t* __restrict__ dump, int64_t dump_off, bool valid) {
+    const uint32_t dw[17] = {L.v0.x, L.v0.y, L.v0.z, L.v0.w, L.v1.x, L.v1.y, L.v1.z, L.v1.w,
+                             L.v2.x, L.v2.y, L.v2.z, L.v2.w, L.v3.x, L.v3.y, L.v3.z, L.v3.w, L.v4};
+    StagedPair x;
+    read_pair(lds, P, x, false);
+    int ia = 0, ib = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        ia = dot4(__builtin_amdgcn_alignbyte(dw[k + 1], dw[k], 2), x.c[k], ia);
+        ib = dot4(dw[9 + k], x.c[8 + k], ib);
+    }
+    if (DUMP && valid) {
+        dump[dump_off + 2 * P] = ia;
+        dump[dump_off + 2 * P + 1] = ib;
+    }
+    // d_w*d_x has < 24 significant bits and |isum| < 2^20: each product is
+    // exact in f64, only the addition rounds.
+    const double da = (double)f16_to_f32(dw[0]) * x.d0;
+    const double db = (double)f16_to_f32(dw[8] >> 16) * x.d1;
+    return fma((double)ia, da, (double)ib * db);
+}
 
 template <bool DUMP>
 __global__ __launch_bounds__(256) void k_gemv_q8_0(const uint8_t* __restrict__ w,
@@ -18,54 +60,62 @@ __global__ __launch_bounds__(256) void k_gemv_q8_0(const uint8_t* __restrict__ w
                                                   int M, int npairs, int log2s, int passes,
                                                   int n_tiles) {
     extern __shared__ __align__(16) uint8_t lds[];
-    stage_q8(xq, 0, 2 * npairs, lds, threadIdx.x, blockDim.x, nullptr);
-    __syncthreads();
-
     const int lane = threadIdx.x & 63;
     const int S = 1 << log2s, R = 64 >> log2s;
     const int row_local = lane >> log2s, slot = lane & (S - 1);
-    const int wave_stride = gridDim.x * (blockDim.x >> 6);
-    for (int tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tile < n_tiles;
-         tile += wave_stride) {
-        const int row = tile * R + row_local;
-        double acc = 0.0;
-        for (int p = 0; p < passes; ++p) {
-            const int P = p * S + slot;
-            if (row < M && P < npairs) {
-                const uint8_t* base = w + ((int64_t)row * npairs + P) * (2 * kQ8Bytes);
-                const u32x4 v0 = __builtin_nontemporal_load((const u32x4_a4*)(base));
-                const u32x4 v1 = __builtin_nontemporal_load((const u32x4_a4*)(base + 16));
-                const u32x4 v2 = __builtin_nontemporal_load((const u32x4_a4*)(base + 32));
-                const u32x4 v3 = __builtin_nontemporal_load((const u32x4_a4*)(base + 48));
-                const uint32_t v4 = __builtin_nontemporal_load((const uint32_t*)(base + 64));
-                const uint32_t dw[17] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                                         v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w, v4};
-                StagedPair x;
-                read_pair(lds, P, x, false);
-                int ia = 0, ib = 0;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    ia = dot4(__builtin_amdgcn_alignbyte(dw[k + 1], dw[k], 2), x.c[k], ia);
-                    ib = dot4(dw[9 + k], x.c[8 + k], ib);
-                }
-                const double da = (double)f16_to_f32(dw[0]);
-                const double db = (double)f16_to_f32(dw[8] >> 16);
-                // d_w*d_x has < 24 significant bits and |isum| < 2^20: each
-                // product is exact in f64.
-                acc += (double)ia * (da * x.d0);
-                acc += (double)ib * (db * x.d1);
-                if (DUMP) {
-                    dump_isum[(int64_t)row * 2 * npairs + 2 * P] = ia;
-                    dump_isum[(int64_t)row * 2 * npairs + 2 * P + 1] = ib;
-                }
-            }
-        }
-        const double v = group_sum_f64(acc, log2s);
-        if (slot == 0 && row < M) y[row] = (float)v;
+    const int W = gridDim.x * (blockDim.x >> 6);
+    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
+    const int n_items = my_tiles * passes;
+    const int64_t row_bytes = (int64_t)npairs * 2 * kQ8Bytes;
+
+    auto where = [&](int i, const uint8_t*& p, bool& valid, int& row, int& pass, int& P) {
+        if (i >= n_items) { p = w; valid = false; row = M; pass = 0; P = 0; return; }
+        const int t = wave + (i / passes) * W;
+        pass = i % passes;
+        row = t * R + row_local;
+        P = pass * S + slot;
+        valid = row < M && P < npairs;
+        p = valid ? w + row * row_bytes + P * (2 * kQ8Bytes) : w;
+    };
+
+    PairLoad A, B;
+    const uint8_t* pa;
+    bool va = false;
+    int ra = 0, passa = 0, Pa = 0;
+    if (n_items > 0) {
+        where(0, pa, va, ra, passa, Pa);
+        load_pair(pa, A);
+    }
+    stage_q8(xq, 0, 2 * npairs, lds, threadIdx.x, blockDim.x, nullptr);
+    __syncthreads();
+    if (n_items == 0) return;
+
+    double acc = 0.0;
+    auto item = [&](const PairLoad& L, bool valid, int row, int pass, int P) {
+        const double v = pair_item<DUMP>(L, lds, valid ? P : 0, dump_isum, (int64_t)row * 2 * npairs, valid);
+        acc += valid ? v : 0.0;
+        if (pass != passes - 1) return;
+        const double s = group_sum_f64(acc, log2s);
+        acc = 0.0;
+        if (slot == 0 && row < M) y[row] = (float)s;
+    };
+    for (int i = 0; i < n_items; i += 2) {
+        const uint8_t* pb;
+        bool vb;
+        int rb, passb, Pb;
+        where(i + 1, pb, vb, rb, passb, Pb);
+        load_pair(pb, B);
+        item(A, va, ra, passa, Pa);
+        where(i + 2, pa, va, ra, passa, Pa);
+        load_pair(pa, A);
+        if (i + 1 < n_items) item(B, vb, rb, passb, Pb);
     }
 }
 
 Q8Plan plan_q8_0(int64_t m, int npairs) {
+    // Slot of S lanes per row: one pass when the row fits in 64 lanes;
+    // otherwise 64 lanes and several passes.
     Q8Plan p;
     int l = 0;
     while ((1 << l) < npairs) ++l;
@@ -78,17 +128,36 @@ Q8Plan plan_q8_0(int64_t m, int npairs) {
     return p;
 }
 
+static int q8_blocks_per_cu(const void* fn, int lds) {
+    static const void* cfn[8];
+    static int clds[8], cn[8], used = 0;
+    for (int i = 0; i < used; ++i)
+        if (cfn[i] == fn && clds[i] == lds) return cn[i];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, lds) != hipSuccess || n <= 0) n = 2;
+    if (used < 8) { cfn[used] = fn; clds[used] = lds; cn[used] = n; ++used; }
+    return n;
+}
+
 hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* dump_isum, int64_t m,
                             int64_t k, hipStream_t stream) {
     const int npairs = (int)(k / 64);
     const Q8Plan p = plan_q8_0(m, npairs);
     const int lds = stage_bytes(2 * npairs);
-    const int cap = device_cu_count() * 8;
-    int grid = (p.n_tiles + 3) / 4;
-    if (grid > cap) grid = cap;
+    const void* fn = dump_isum ? (const void*)k_gemv_q8_0<true> : (const void*)k_gemv_q8_0<false>;
+    const int64_t wmax = (int64_t)device_cu_count() * q8_blocks_per_cu(fn, lds) * 4;
+    const int64_t per = (p.n_tiles + wmax - 1) / wmax;
+    const int64_t waves = (p.n_tiles + per - 1) / per;
+    const int grid = (int)((waves + 3) / 4);
+    hipEvent_t e0, e1;
+    const bool timed = take_next_launch_events(&e0, &e1);
+    if (timed) (void)hipStreamSynchronize(stream);   // start on an idle stream (see MQ_LAUNCH)
     if (dump_isum)
         hipLaunchKernelGGL(k_gemv_q8_0<true>, dim3(grid), dim3(256), lds, stream, (const uint8_t*)w,
                            (const uint8_t*)xq, y, dump_isum, (int)m, npairs, p.log2s, p.passes, p.n_tiles);
+    else if (timed)
+        hipExtLaunchKernelGGL(k_gemv_q8_0<false>, dim3(grid), dim3(256), lds, stream, e0, e1, 0, (const uint8_t*)w,
+                              (const uint8_t*)xq, y, nullptr, (int)m, npairs, p.log2s, p.passes, p.n_tiles);
     else
         hipLaunchKernelGGL(k_gemv_q8_0<false>, dim3(grid), dim3(256), lds, stream, (const uint8_t*)w,
                            (const uint8_t*)xq, y, nullptr, (int)m, npairs, p.log2s, p.passes, p.n_tiles);

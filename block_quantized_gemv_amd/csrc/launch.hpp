@@ -24,12 +24,21 @@ Q8Plan plan_q8_0(int64_t m, int npairs);
 
 int device_cu_count();
 
+// Events for the next GEMV launches of this thread (see mq_time_next_launches).
+void set_next_launch_events(const hipEvent_t* starts, const hipEvent_t* stops, int n);
+bool take_next_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
 // Largest LDS a workgroup of the full-staging kernels may take.
 constexpr int kMaxStageLds = 64 * 1024;
 
 hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                            int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
                            hipStream_t stream);
+// Gate/up GEMV with the SwiGLU stand-in fused: rows [0, inter) are gate rows,
+// [inter, 2*inter) up rows; writes Q8(silu(gate)*up) (inter/32 blocks) and,
+// if gu_out is set, the f32 GEMV outputs.  inter % 32 == 0.
+hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, float* gu_out, void* g_q8, int64_t inter,
+                                  int64_t k, hipStream_t stream);
 // Split-k variant for shapes whose activation does not fit in LDS; `part`
 // holds n_split*m*ncols doubles.
 int gemv_q4k_splitk_nsplit(int64_t k);
@@ -44,10 +53,11 @@ hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* du
                             int64_t k, hipStream_t stream);
 
 hipError_t launch_quantize_q8_0(const float* x, void* xq, int64_t k, int n_cols, hipStream_t stream);
-// x row: if step != NULL, row (step % n_inputs) of x (x_table) is used and the
-// counter is advanced by one inside the kernel.
-hipError_t launch_rmsnorm_quantize(const float* x, void* xq, int64_t k, float eps, int64_t* step,
-                                   int n_inputs, hipStream_t stream);
+// x row: if sel_step != NULL, row (sel_step % n_inputs) of x (x_table) is
+// used; if inc_step != NULL, that counter is advanced by one (a kernel may
+// not do both: its workgroups read the counter at different times).
+hipError_t launch_rmsnorm_quantize(const float* x, void* xq, int64_t k, float eps, const int64_t* sel_step,
+                                   int n_inputs, int64_t* inc_step, hipStream_t stream);
 hipError_t launch_swiglu_quantize(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
                                   hipStream_t stream);
 // Routed-expert token set-up: token t = step % n_tokens (step advanced by one);

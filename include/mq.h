@@ -252,6 +252,23 @@ int mq_moe_create(const mq_moe_desc* desc, hipStream_t stream, mq_chain** out);
 int mq_moe_step(mq_chain* c, int mode, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Measurement hook: the next n GEMV kernels (q4_K, batched, grouped, fused
+ * chain GEMVs, q8_0) that the calling thread launches, through entry points
+ * or eager chain steps, record starts[i] when dispatch i begins executing
+ * and stops[i] when it completes: the kernels' own dispatch timestamps, as a
+ * kernel trace reports them, with no marker packets between the kernels.
+ * Before each timed launch the library synchronizes `stream`, so the
+ * dispatch starts on an idle stream and its start timestamp is the kernel's
+ * own (a dispatch queued behind a running kernel is stamped early).
+ * starts/stops: HOST arrays of n events created by the caller
+ * (hipEventCreate); they are copied, so they may be freed after this call.
+ * n = 0 clears the hook.  Graph replays are not timed (their kernels were
+ * recorded at capture); never arm it while the stream is being captured.
+ * 0 <= n <= 65536.
+ */
+int mq_time_next_launches(const hipEvent_t* starts, const hipEvent_t* stops, int n);
+
+/* ---------------------------------------------------------------------------
  * Test hook, never read from the environment (environment variables are
  * process-global and leak across tests — '07 · R3', §3.3).
  * MQ_FAULT_CAPTURE makes the next chain creations behave as if graph
