@@ -8,10 +8,12 @@ in HBM.  Prints one JSON line (rank 0):
 
   value      = algorithmic bytes per step / step time, GB/s
   tok_per_s  = decode steps per second
-  roofline   = the q4_K GEMV kernel (the dominant kernel): average
-               algorithmic bytes per launch / average launch duration, the
-               durations taken with HIP events around each launch on the
-               launching stream, against 8 TB/s
+  roofline   = the GEMV kernel with the largest share of step time: its
+               average algorithmic bytes per launch / average launch
+               duration, each launch timed by its own dispatch events on the
+               launching stream (eager steps, the same kernels and arguments
+               the graph replays), against 8 TB/s; `traffic` is the HBM bytes
+               per launch the committed rocprofv3 counter record measured
   cpu_baseline = the reference oracle on the host, on a bounded sample
 
 Other workloads (--workload 05b|single|batched|moe) print their own line.
@@ -114,6 +116,34 @@ class HipEvents:
         self.events = []
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_q4k_gemv_7b_decode_step.txt")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter record (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
+    None when there is no record for that kernel and workload or the kernel
+    sources changed since it was taken."""
+    import hashlib
+    try:
+        rec = dict(ln.split(": ", 1) for ln in open(TRAFFIC_RECORD).read().splitlines() if ": " in ln)
+    except OSError:
+        return None
+    if rec.get("dominant_kernel", "").strip() != kernel.split(" ")[0]:
+        return None
+    if rec.get("workload", "").strip() != workload:
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("kernel_sources", "").split():
+        try:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        except OSError:
+            return None
+    if h.hexdigest()[:16] != rec.get("kernel_sources_sha256_16", "").strip():
+        return None
+    return int(float(rec["traffic_bytes_per_launch"]))
+
+
 def gemv_kinds(model):
     """The step's GEMV launches in order, with their kernel and algorithmic
     bytes (weights + q8_0 activation in + output written)."""
@@ -168,8 +198,9 @@ def time_kernels(mq, model, eager_chain, reps):
     kernel_sum_ms = sum(us) / reps / 1e3
     return {"bound": "hbm", "kernel": dominant, "launches": dk["n"], "bytes_per_launch": round(avg_b),
             "us_per_launch": round(avg_us, 3), "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "timing": "hipExtLaunchKernelGGL dispatch events around each launch, eager steps",
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant, model.name),
+            "timing": "dispatch events of each launch (hipExtLaunchKernelGGL), launched from an idle stream "
+                      "in eager steps; includes the dispatch latency a graph replay hides",
             "per_shape": per_shape}, kernel_sum_ms
 
 
