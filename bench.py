@@ -145,18 +145,19 @@ def measured_traffic(kernel, workload):
 
 
 def gemv_kinds(model):
-    """The step's GEMV launches in order, with their kernel and algorithmic
-    bytes (weights + q8_0 activation in + output written)."""
+    """The step's kernels in order, with their names and algorithmic bytes:
+    weights + activation in (f32 where the kernel forms Q8(RMSNorm(x)) in its
+    prologue, q8_0 otherwise) + output written (f32, or q8_0 after SwiGLU)."""
     from block_quantized_gemv_amd import workloads as wl
     H, I, Q = model.hidden, model.inter, model.qkv_rows
-    tail = "mq::k_gemv_q4k<1,false>"
+    norm = "mq::k_gemv_q4k<1,false,true>"
     kinds = []
     for _ in range(model.n_layers):
-        kinds += [("qkv", tail, wl.q4k_bytes(Q, H) + wl.q8_bytes(1, H) + 4 * Q),
-                  ("o", tail, wl.q4k_bytes(H, H) + wl.q8_bytes(1, H) + 4 * H),
-                  ("gate/up", "mq::k_gemv_q4k_swiglu", wl.q4k_bytes(2 * I, H) + wl.q8_bytes(1, H) + wl.q8_bytes(1, I)),
-                  ("down", tail, wl.q4k_bytes(H, I) + wl.q8_bytes(1, I) + 4 * H)]
-    kinds.append(("lm_head", "mq::k_gemv_q8_0<false>", wl.q8_bytes(model.vocab, H) + wl.q8_bytes(1, H) + 4 * model.vocab))
+        kinds += [("qkv", norm, wl.q4k_bytes(Q, H) + 4 * H + 4 * Q),
+                  ("o", norm, wl.q4k_bytes(H, H) + 4 * H + 4 * H),
+                  ("gate/up", "mq::k_gemv_q4k_swiglu<true>", wl.q4k_bytes(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
+                  ("down", "mq::k_gemv_q4k<1,false,false>", wl.q4k_bytes(H, I) + wl.q8_bytes(1, I) + 4 * H)]
+    kinds.append(("lm_head", "mq::k_gemv_q8_0<false,true>", wl.q8_bytes(model.vocab, H) + 4 * H + 4 * model.vocab))
     return kinds
 
 

@@ -331,14 +331,16 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     CHECK_SHAPE(d->n_layers >= 1 && d->n_layers <= 4096, "n_layers out of range");
     CHECK_SHAPE(d->hidden >= 256 && d->hidden % 256 == 0 && d->hidden <= kMaxK, "hidden must be a multiple of 256");
     CHECK_SHAPE(d->inter >= 256 && d->inter % 256 == 0 && d->inter <= kMaxK, "inter must be a multiple of 256");
-    CHECK_SHAPE(d->qkv_rows >= d->hidden && d->qkv_rows <= kMaxRows, "qkv_rows must be >= hidden");
+    CHECK_SHAPE(d->qkv_rows >= d->hidden && d->qkv_rows <= kMaxRows && d->qkv_rows % 4 == 0,
+                "qkv_rows must be >= hidden and a multiple of 4");
     CHECK_SHAPE(d->vocab >= 1 && d->vocab <= kMaxRows, "vocab out of range");
     CHECK_SHAPE(stage_bytes((int)(d->inter / 32)) <= kMaxStageLds, "inter too large");
     CHECK_ARG(d->w_qkv && d->w_o && d->w_gu && d->w_down && d->w_lm && d->x_table && d->logits,
               "null pointer in the descriptor");
     CHECK_ARG(d->n_inputs >= 1, "n_inputs must be >= 1");
     CHECK_ARG(d->eps >= 0.0f, "eps must be >= 0");
-    CHECK_ARG(aligned(d->w_lm, 4) && aligned(d->x_table, 4) && aligned(d->logits, 4), "misaligned pointer");
+    CHECK_ARG(aligned(d->w_lm, 4) && aligned(d->x_table, 16) && aligned(d->logits, 4),
+              "misaligned pointer (x_table must be 16-byte aligned)");
     for (int l = 0; l < d->n_layers; ++l)
         CHECK_ARG(d->w_qkv[l] && d->w_o[l] && d->w_gu[l] && d->w_down[l] && aligned(d->w_qkv[l], 16) &&
                       aligned(d->w_o[l], 16) && aligned(d->w_gu[l], 16) && aligned(d->w_down[l], 16),
@@ -368,10 +370,12 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     int64_t* step = c->step;
     const float* x_table = d->x_table;
     const int n_inputs = d->n_inputs;
-    // Per layer: RMSNorm->Q8 kernels feed QKV, O and gate/up; gate/up carries
-    // the SwiGLU->Q8 glue in its epilogue.  The first kernel of the step picks
-    // the input row with the device step counter; the last glue kernel
-    // advances it.
+    // Per layer four kernels.  QKV, O and gate/up form their q8_0 input
+    // Q8(RMSNorm(.)) in their own prologues; gate/up carries the SwiGLU->Q8
+    // glue in its epilogue and down reads that.  The first kernel of the step
+    // picks the input row with the device step counter; the lm_head kernel,
+    // the last one, advances it.  The q8_0 vectors formed in prologues are
+    // written out (by one workgroup) only when intermediates are kept.
     const float* h_prev = nullptr;
     for (int l = 0; l < L; ++l) {
         uint8_t* q8 = c->q8_trace + (keep ? l * q8_layer : 0);
@@ -380,15 +384,13 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         float *t = f, *o = f + QKV, *gu = f + QKV + H, *h = f + QKV + H + 2 * I;
         const void *wq = d->w_qkv[l], *wo = d->w_o[l], *wg = d->w_gu[l], *wd = d->w_down[l];
         float* gu_keep = keep ? gu : nullptr;
-        if (l == 0)
-            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(x_table, qa, H, eps, step, n_inputs, nullptr, s); });
-        else
-            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qa, H, eps, nullptr, 1, nullptr, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, nullptr, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, nullptr, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, qc, gu_keep, qg, I, H, s); });
+        const NormIn na = l == 0 ? NormIn{x_table, step, n_inputs, eps, keep ? qa : nullptr, nullptr}
+                                 : NormIn{h_prev, nullptr, 1, eps, keep ? qa : nullptr, nullptr};
+        const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr};
+        const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr};
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s); });
         h_prev = h;
     }
@@ -396,8 +398,8 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const void* wlm = d->w_lm;
     float* logits = d->logits;
     const int64_t V = d->vocab;
-    c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(h_prev, qz, H, eps, nullptr, 1, step, s); });
-    c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0(wlm, qz, logits, nullptr, V, H, s); });
+    const NormIn nz{h_prev, nullptr, 1, eps, keep ? qz : nullptr, step};
+    c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0_norm(wlm, nz, logits, V, H, s); });
     if (!keep) c->q8_bytes = c->f32_count = 0;
 
     rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);

@@ -141,12 +141,15 @@ __device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P,
 // --------------------------------------------------------------------------
 // Full staging: all NC activation columns live in LDS.  Wave w owns tiles
 // w, w+W, w+2W, ... (W = waves in the grid); its items are (tile, pass) in
-// that order.
-template <int NC, bool DUMP>
-__global__ __launch_bounds__(256) void k_gemv_q4k(
+// that order.  With NORM the single activation column is Q8(RMSNorm(x)) of
+// the f32 vector `nin` describes, formed by each workgroup in its prologue
+// (workgroups of up to 1024 threads, about one per CU, so that the
+// normalization is done once per CU); otherwise xq holds q8_0 columns.
+template <int NC, bool DUMP, bool NORM>
+__global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
-    int M, int nsb, int log2s, int passes, int n_tiles) {
+    int M, int nsb, int log2s, int passes, int n_tiles, NormIn nin) {
     extern __shared__ __align__(16) uint8_t lds[];
     const Lanes ln(log2s);
     const int nb = nsb * 8;
@@ -175,10 +178,15 @@ __global__ __launch_bounds__(256) void k_gemv_q4k(
         where(0, pa, va, ra, pa_pass);
         load_sb(pa, 32 * ln.j, A);
     }
+    if constexpr (NORM) {
+        __shared__ double sh[16];
+        stage_norm_input(nin, nsb * 256, lds, sh);
+    } else {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-        stage_q8(xq + c * xq_col_bytes, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x,
-                 (DUMP && blockIdx.x == 0 && c == 0) ? dump_ysum : nullptr);
+        for (int c = 0; c < NC; ++c)
+            stage_q8(xq + c * xq_col_bytes, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x,
+                     (DUMP && blockIdx.x == 0 && c == 0) ? dump_ysum : nullptr);
+    }
     __syncthreads();
 
     double acc[NC];
@@ -380,23 +388,31 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
 // Gate/up GEMV with the SwiGLU stand-in fused.  Workgroup u owns outputs
 // [32u, 32u+32): gate rows 32u..32u+31 and up rows inter+32u..+31, so it can
 // finish whole q8_0 blocks itself.  Rows use 16-lane slots (4 rows a tile);
-// wave q takes gate rows 32u+8q..+7 and the matching up rows (4 tiles).
-// The per-row arithmetic and reduction are those of k_gemv_q4k with 16-lane
-// slots, so gate and up values are the ones the plain GEMV would write.
-__global__ __launch_bounds__(256) void k_gemv_q4k_swiglu(
+// with WV waves, wave q takes gate rows 32u + (32/WV)q .. +32/WV-1 and the
+// matching up rows, 8/WV tiles of each.  The per-row arithmetic and
+// reduction are those of k_gemv_q4k with 16-lane slots, so gate and up
+// values are the ones the plain GEMV would write.  With NORM the input is
+// Q8(RMSNorm(x)) formed in the prologue (8 waves, so that fewer
+// workgroups repeat it); otherwise xq (4 waves).
+template <bool NORM>
+__global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* __restrict__ gu_out,
-    uint8_t* __restrict__ g_q8, int inter, int nsb) {
+    uint8_t* __restrict__ g_q8, int inter, int nsb, NormIn nin) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
+    constexpr int WV = NORM ? 8 : 4;        // waves per workgroup
+    constexpr int TPH = 8 / WV;             // tiles per half (gate or up) per wave
     const Lanes ln(4);
     const int nb = nsb * 8;
     const int passes = (nsb + 3) / 4;
-    const int n_items = 4 * passes;
+    const int n_items = 2 * TPH * passes;
     const int u = blockIdx.x, q = threadIdx.x >> 6;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
 
-    // item i: tile st = i / passes (0,1: gate rows; 2,3: up rows), pass i % passes
-    auto row_of = [&](int st) { return (st >> 1) * inter + 32 * u + 8 * q + 4 * (st & 1) + ln.row_local; };
+    // item i: tile st = i / passes (st / TPH: 0 gate, 1 up; st % TPH: which
+    // tile of the half), pass i % passes
+    auto local_of = [&](int st) { return (32 / WV) * q + 4 * (st % TPH) + ln.row_local; };
+    auto row_of = [&](int st) { return (st / TPH) * inter + 32 * u + local_of(st); };
     auto where = [&](int i, const uint8_t*& p, bool& valid, int& st, int& pass) {
         if (i >= n_items) { p = w; valid = false; st = 0; pass = 0; return; }
         st = i / passes;
@@ -412,7 +428,12 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_swiglu(
     int sa, pa_pass;
     where(0, pa, va, sa, pa_pass);
     load_sb(pa, 32 * ln.j, A);
-    stage_q8(xq, 0, nb, lds, threadIdx.x, blockDim.x, nullptr);
+    if constexpr (NORM) {
+        __shared__ double sh[16];
+        stage_norm_input(nin, nsb * 256, lds, sh);
+    } else {
+        stage_q8(xq, 0, nb, lds, threadIdx.x, blockDim.x, nullptr);
+    }
     __syncthreads();
 
     double acc[1] = {0.0};
@@ -422,7 +443,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_swiglu(
         const float v = (float)group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
         if ((ln.lane & 15) == 0) {
-            gu_s[(st >> 1) * 32 + 8 * q + 4 * (st & 1) + ln.row_local] = v;
+            gu_s[(st / TPH) * 32 + local_of(st)] = v;
             if (gu_out) gu_out[row_of(st)] = v;
         }
     };
@@ -556,10 +577,35 @@ static hipError_t launch_nc(const void* w, const void* xq, int64_t xq_col_bytes,
                             hipStream_t stream) {
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = NC * stage_bytes(nsb * 8);
-    const void* fn = (const void*)k_gemv_q4k<NC, DUMP>;
-    MQ_LAUNCH((k_gemv_q4k<NC, DUMP>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds, stream,
+    const void* fn = (const void*)k_gemv_q4k<NC, DUMP, false>;
+    MQ_LAUNCH((k_gemv_q4k<NC, DUMP, false>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds, stream,
               (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, y, dump_isum, dump_ysum, (int)m, nsb,
-              p.log2s, p.passes, p.n_tiles);
+              p.log2s, p.passes, p.n_tiles, NormIn{});
+    return hipGetLastError();
+}
+
+// Grid of a GEMV whose workgroups each repeat a prologue: at most one
+// workgroup per CU (up to 16 waves each), every wave with the same number
+// of units (or one fewer).
+void prologue_grid(int64_t units, int* grid, int* threads) {
+    const int64_t cus = device_cu_count();
+    const int64_t per = (units + cus * 16 - 1) / (cus * 16);
+    const int64_t waves = (units + per - 1) / per;
+    const int64_t wpg = (waves + cus - 1) / cus;
+    *grid = (int)((waves + wpg - 1) / wpg);
+    *threads = (int)(64 * wpg);
+}
+
+hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
+                                hipStream_t stream) {
+    const int nsb = (int)(k / 256);
+    const Q4KPlan p = plan_q4k(m, nsb);
+    const int lds = stage_bytes(nsb * 8);
+    int grid = 1, threads = 64;
+    prologue_grid(p.n_tiles, &grid, &threads);
+    MQ_LAUNCH((k_gemv_q4k<1, false, true>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
+              (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb,
+              p.log2s, p.passes, p.n_tiles, nin);
     return hipGetLastError();
 }
 
@@ -619,12 +665,16 @@ hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_
     }
 }
 
-hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, float* gu_out, void* g_q8, int64_t inter,
-                                  int64_t k, hipStream_t stream) {
+hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
+                                  int64_t inter, int64_t k, hipStream_t stream) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
-    MQ_LAUNCH(k_gemv_q4k_swiglu, dim3((unsigned)(inter / 32)), dim3(256), lds, stream, (const uint8_t*)w,
-                       (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb);
+    if (nin)
+        MQ_LAUNCH(k_gemv_q4k_swiglu<true>, dim3((unsigned)(inter / 32)), dim3(512), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin);
+    else
+        MQ_LAUNCH(k_gemv_q4k_swiglu<false>, dim3((unsigned)(inter / 32)), dim3(256), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb, NormIn{});
     return hipGetLastError();
 }
 

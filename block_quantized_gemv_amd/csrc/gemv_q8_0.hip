@@ -10,6 +10,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
+#include "glue.hpp"
 #include "launch.hpp"
 
 namespace mq {
@@ -53,12 +54,16 @@ __device__ __forceinline__ double pair_item(const PairLoad& L, const uint8_t* __
     return fma((double)ia, da, (double)ib * db);
 }
 
-template <bool DUMP>
-__global__ __launch_bounds__(256) void k_gemv_q8_0(const uint8_t* __restrict__ w,
-                                                  const uint8_t* __restrict__ xq,
-                                                  float* __restrict__ y, int32_t* __restrict__ dump_isum,
-                                                  int M, int npairs, int log2s, int passes,
-                                                  int n_tiles) {
+// With NORM the activation is Q8(RMSNorm(x)) of the f32 vector `nin`
+// describes, formed in each workgroup's prologue (workgroups of up to 1024
+// threads, about one per CU); otherwise xq holds it.
+template <bool DUMP, bool NORM>
+__global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* __restrict__ w,
+                                                                const uint8_t* __restrict__ xq,
+                                                                float* __restrict__ y,
+                                                                int32_t* __restrict__ dump_isum, int M,
+                                                                int npairs, int log2s, int passes,
+                                                                int n_tiles, NormIn nin) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
     const int S = 1 << log2s, R = 64 >> log2s;
@@ -87,7 +92,12 @@ __global__ __launch_bounds__(256) void k_gemv_q8_0(const uint8_t* __restrict__ w
         where(0, pa, va, ra, passa, Pa);
         load_pair(pa, A);
     }
-    stage_q8(xq, 0, 2 * npairs, lds, threadIdx.x, blockDim.x, nullptr);
+    if constexpr (NORM) {
+        __shared__ double sh[16];
+        stage_norm_input(nin, 64 * npairs, lds, sh);
+    } else {
+        stage_q8(xq, 0, 2 * npairs, lds, threadIdx.x, blockDim.x, nullptr);
+    }
     __syncthreads();
     if (n_items == 0) return;
 
@@ -144,7 +154,7 @@ hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* du
     const int npairs = (int)(k / 64);
     const Q8Plan p = plan_q8_0(m, npairs);
     const int lds = stage_bytes(2 * npairs);
-    const void* fn = dump_isum ? (const void*)k_gemv_q8_0<true> : (const void*)k_gemv_q8_0<false>;
+    const void* fn = dump_isum ? (const void*)k_gemv_q8_0<true, false> : (const void*)k_gemv_q8_0<false, false>;
     const int64_t wmax = (int64_t)device_cu_count() * q8_blocks_per_cu(fn, lds) * 4;
     const int64_t per = (p.n_tiles + wmax - 1) / wmax;
     const int64_t waves = (p.n_tiles + per - 1) / per;
@@ -153,14 +163,38 @@ hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* du
     const bool timed = take_next_launch_events(&e0, &e1);
     if (timed) (void)hipStreamSynchronize(stream);   // start on an idle stream (see MQ_LAUNCH)
     if (dump_isum)
-        hipLaunchKernelGGL(k_gemv_q8_0<true>, dim3(grid), dim3(256), lds, stream, (const uint8_t*)w,
-                           (const uint8_t*)xq, y, dump_isum, (int)m, npairs, p.log2s, p.passes, p.n_tiles);
+        hipLaunchKernelGGL((k_gemv_q8_0<true, false>), dim3(grid), dim3(256), lds, stream, (const uint8_t*)w,
+                           (const uint8_t*)xq, y, dump_isum, (int)m, npairs, p.log2s, p.passes, p.n_tiles,
+                           NormIn{});
     else if (timed)
-        hipExtLaunchKernelGGL(k_gemv_q8_0<false>, dim3(grid), dim3(256), lds, stream, e0, e1, 0, (const uint8_t*)w,
-                              (const uint8_t*)xq, y, nullptr, (int)m, npairs, p.log2s, p.passes, p.n_tiles);
+        hipExtLaunchKernelGGL((k_gemv_q8_0<false, false>), dim3(grid), dim3(256), lds, stream, e0, e1, 0,
+                              (const uint8_t*)w, (const uint8_t*)xq, y, (int32_t*)nullptr, (int)m, npairs,
+                              p.log2s, p.passes, p.n_tiles, NormIn{});
     else
-        hipLaunchKernelGGL(k_gemv_q8_0<false>, dim3(grid), dim3(256), lds, stream, (const uint8_t*)w,
-                           (const uint8_t*)xq, y, nullptr, (int)m, npairs, p.log2s, p.passes, p.n_tiles);
+        hipLaunchKernelGGL((k_gemv_q8_0<false, false>), dim3(grid), dim3(256), lds, stream, (const uint8_t*)w,
+                           (const uint8_t*)xq, y, (int32_t*)nullptr, (int)m, npairs, p.log2s, p.passes,
+                           p.n_tiles, NormIn{});
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
+                                 hipStream_t stream) {
+    const int npairs = (int)(k / 64);
+    const Q8Plan p = plan_q8_0(m, npairs);
+    const int lds = stage_bytes(2 * npairs);
+    int grid = 1, threads = 64;
+    prologue_grid(p.n_tiles, &grid, &threads);
+    hipEvent_t e0, e1;
+    if (take_next_launch_events(&e0, &e1)) {
+        (void)hipStreamSynchronize(stream);
+        hipExtLaunchKernelGGL((k_gemv_q8_0<false, true>), dim3(grid), dim3(threads), lds, stream, e0, e1, 0,
+                              (const uint8_t*)w, (const uint8_t*)nullptr, y, (int32_t*)nullptr, (int)m, npairs,
+                              p.log2s, p.passes, p.n_tiles, nin);
+    } else {
+        hipLaunchKernelGGL((k_gemv_q8_0<false, true>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
+                           (const uint8_t*)nullptr, y, (int32_t*)nullptr, (int)m, npairs, p.log2s, p.passes,
+                           p.n_tiles, nin);
+    }
     return hipGetLastError();
 }
 

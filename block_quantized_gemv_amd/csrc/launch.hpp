@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "glue.hpp"
+
 namespace mq {
 
 // Lane layout of the q4_K kernels for a row of nsb super-blocks: rows get
@@ -34,11 +36,19 @@ constexpr int kMaxStageLds = 64 * 1024;
 hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                            int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
                            hipStream_t stream);
+// The q4_K GEMV of one activation Q8(RMSNorm(x)) formed in the kernel's
+// prologue from the f32 input nin describes (the decode-step chain).
+hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
+                                hipStream_t stream);
 // Gate/up GEMV with the SwiGLU stand-in fused: rows [0, inter) are gate rows,
 // [inter, 2*inter) up rows; writes Q8(silu(gate)*up) (inter/32 blocks) and,
-// if gu_out is set, the f32 GEMV outputs.  inter % 32 == 0.
-hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, float* gu_out, void* g_q8, int64_t inter,
-                                  int64_t k, hipStream_t stream);
+// if gu_out is set, the f32 GEMV outputs.  inter % 32 == 0.  The activation
+// is xq, or Q8(RMSNorm(x)) formed in the prologue when nin is set.
+hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
+                                  int64_t inter, int64_t k, hipStream_t stream);
+// Workgroups and threads per workgroup for `units` equal work units of a
+// kernel whose workgroups each repeat a prologue (about one per CU).
+void prologue_grid(int64_t units, int* grid, int* threads);
 // Split-k variant for shapes whose activation does not fit in LDS; `part`
 // holds n_split*m*ncols doubles.
 int gemv_q4k_splitk_nsplit(int64_t k);
@@ -51,6 +61,8 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
                                    hipStream_t stream);
 hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* dump_isum, int64_t m,
                             int64_t k, hipStream_t stream);
+hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
+                                 hipStream_t stream);
 
 hipError_t launch_quantize_q8_0(const float* x, void* xq, int64_t k, int n_cols, hipStream_t stream);
 // x row: if sel_step != NULL, row (sel_step % n_inputs) of x (x_table) is

@@ -170,6 +170,9 @@ int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t
  * and be advanced inside the captured region (Lecture 08, §2).
  * Inputs are declared before the step starts and nothing is filled from
  * the host inside it, so the step is one split ('07 · R3', §2).
+ * The step is 4 kernels per layer plus the lm_head: each Q8(RMSNorm(.)) is
+ * formed in the prologue of the GEMV that consumes it, and Q8(SwiGLU(gu)) in
+ * the epilogue of the gate/up GEMV.
  */
 typedef struct mq_chain mq_chain;
 
@@ -178,13 +181,13 @@ enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
 
 typedef struct {
     int n_layers;                      /* >= 1 */
-    int64_t hidden, qkv_rows, inter, vocab;   /* hidden, inter % 256 == 0; qkv_rows >= hidden */
+    int64_t hidden, qkv_rows, inter, vocab;   /* hidden, inter % 256 == 0; qkv_rows >= hidden, % 4 == 0 */
     const void* const* w_qkv;          /* HOST arrays of n_layers device pointers (q4_K) */
     const void* const* w_o;
     const void* const* w_gu;
     const void* const* w_down;
     const void* w_lm;                  /* device q8_0 [vocab][hidden/32] */
-    const float* x_table;              /* device f32 [n_inputs][hidden] */
+    const float* x_table;              /* device f32 [n_inputs][hidden], 16-byte aligned */
     int n_inputs;                      /* >= 1 */
     float* logits;                     /* device f32 [vocab] */
     float eps;

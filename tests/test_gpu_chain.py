@@ -85,7 +85,7 @@ def test_graph_equals_eager_over_replays(mq, o, small_model):
     e = mq.DecodeChain(model, Wd, xd, flags=keep | mq.MQ_EAGER_ONLY)
     info = g.info()
     log(f"captured={info['captured']} nodes={info['n_nodes']}")
-    assert info["captured"] and info["n_nodes"] == 7 * model.n_layers + 2
+    assert info["captured"] and info["n_nodes"] == 4 * model.n_layers + 1
     assert not e.info()["captured"]
     # A/A first: two eager runs of one chain object agree with themselves
     e.reset(0)
