@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmq.so")
 
 MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_HIP, MQ_ERR_CAPTURE, MQ_ERR_NOMEM = 0, -1, -2, -3, -4, -5
-MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES = 1, 2
+MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE = 1, 2, 4
 MQ_GRAPH, MQ_EAGER = 0, 1
 MQ_FAULT_NONE, MQ_FAULT_CAPTURE = 0, 1
 

@@ -353,6 +353,7 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const int64_t H = d->hidden, I = d->inter, QKV = d->qkv_rows;
     const int64_t qH = H / 32 * kQ8Bytes, qI = I / 32 * kQ8Bytes;
     const bool keep = (d->flags & MQ_KEEP_INTERMEDIATES) != 0;
+    const int exact = (d->flags & MQ_EXACT_GLUE) != 0;
     int rc = MQ_OK;
     c->step = (int64_t*)chain_alloc(c, sizeof(int64_t), &rc);
     // Q8 inputs of every GEMV and f32 outputs; with MQ_KEEP_INTERMEDIATES every
@@ -384,10 +385,10 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         float *t = f, *o = f + QKV, *gu = f + QKV + H, *h = f + QKV + H + 2 * I;
         const void *wq = d->w_qkv[l], *wo = d->w_o[l], *wg = d->w_gu[l], *wd = d->w_down[l];
         float* gu_keep = keep ? gu : nullptr;
-        const NormIn na = l == 0 ? NormIn{x_table, step, n_inputs, eps, keep ? qa : nullptr, nullptr}
-                                 : NormIn{h_prev, nullptr, 1, eps, keep ? qa : nullptr, nullptr};
-        const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr};
-        const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr};
+        const NormIn na = l == 0 ? NormIn{x_table, step, n_inputs, eps, keep ? qa : nullptr, nullptr, exact}
+                                 : NormIn{h_prev, nullptr, 1, eps, keep ? qa : nullptr, nullptr, exact};
+        const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr, exact};
+        const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr, exact};
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s); });
@@ -398,7 +399,7 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const void* wlm = d->w_lm;
     float* logits = d->logits;
     const int64_t V = d->vocab;
-    const NormIn nz{h_prev, nullptr, 1, eps, keep ? qz : nullptr, step};
+    const NormIn nz{h_prev, nullptr, 1, eps, keep ? qz : nullptr, step, exact};
     c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0_norm(wlm, nz, logits, V, H, s); });
     if (!keep) c->q8_bytes = c->f32_count = 0;
 

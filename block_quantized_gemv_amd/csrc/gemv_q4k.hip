@@ -160,27 +160,40 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
 
+    // Items past the wave's last one re-read that last item's lines (cache
+    // hits spread over the channels) and are not computed.
     auto where = [&](int i, const uint8_t*& p, bool& valid, int& row, int& pass) {
-        if (i >= n_items) { p = w; valid = false; row = M; pass = 0; return; }
-        const int t = wave + (i / passes) * W;
-        pass = i % passes;
+        const bool past = i >= n_items;
+        const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
+        const int t = wave + (ii / passes) * W;
+        pass = ii % passes;
         row = t * ln.R + ln.row_local;
         const int sb = pass * ln.gpp + ln.g;
-        valid = row < M && sb < nsb;
-        p = valid ? w + row * row_bytes + sb * kQ4KBytes : w;
+        const bool inb = n_items > 0 && row < M && sb < nsb;
+        valid = inb && !past;
+        p = inb ? w + row * row_bytes + sb * kQ4KBytes : w;
     };
 
-    SBLoad A, B;
-    const uint8_t* pa;
-    bool va = false;
-    int ra = 0, pa_pass = 0;
-    if (n_items > 0) {
-        where(0, pa, va, ra, pa_pass);
-        load_sb(pa, 32 * ln.j, A);
+    // The f32 input (NORM) is requested first, then the first two items:
+    // their weight loads are in flight while the prologue stages the
+    // activation.
+    float4 xr[kNormRegChunks];
+    const float* xin = nullptr;
+    if constexpr (NORM) {
+        xin = norm_row(nin, nsb * 256);
+        norm_load(xin, nsb * 256, xr);
     }
+    SBLoad A, B;
+    const uint8_t *pa, *pb;
+    bool va, vb;
+    int ra, pa_pass, rb, pb_pass;
+    where(0, pa, va, ra, pa_pass);
+    load_sb(pa, 32 * ln.j, A);
+    where(1, pb, vb, rb, pb_pass);
+    load_sb(pb, 32 * ln.j, B);
     if constexpr (NORM) {
         __shared__ double sh[16];
-        stage_norm_input(nin, nsb * 256, lds, sh);
+        stage_norm_input(nin, xin, nsb * 256, xr, lds, sh);
     } else {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -203,12 +216,8 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
         }
     };
 
+    // Items i (in A) and i+1 (in B) are in flight at the top of each round.
     for (int i = 0; i < n_items; i += 2) {
-        const uint8_t* pb;
-        bool vb;
-        int rb, pb_pass;
-        where(i + 1, pb, vb, rb, pb_pass);
-        load_sb(pb, 32 * ln.j, B);
         sb_item<NC, DUMP>(A, ln, pair_of(ln, pa_pass), va, lds, col_bytes, acc, dump_isum, (int64_t)ra * nb);
         finish(ra, pa_pass);
         where(i + 2, pa, va, ra, pa_pass);
@@ -217,6 +226,8 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
             sb_item<NC, DUMP>(B, ln, pair_of(ln, pb_pass), vb, lds, col_bytes, acc, dump_isum, (int64_t)rb * nb);
             finish(rb, pb_pass);
         }
+        where(i + 3, pb, vb, rb, pb_pass);
+        load_sb(pb, 32 * ln.j, B);
     }
 }
 
@@ -413,24 +424,35 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     // tile of the half), pass i % passes
     auto local_of = [&](int st) { return (32 / WV) * q + 4 * (st % TPH) + ln.row_local; };
     auto row_of = [&](int st) { return (st / TPH) * inter + 32 * u + local_of(st); };
+    // Items past the last re-read the last item's lines and are not computed.
     auto where = [&](int i, const uint8_t*& p, bool& valid, int& st, int& pass) {
-        if (i >= n_items) { p = w; valid = false; st = 0; pass = 0; return; }
-        st = i / passes;
-        pass = i % passes;
+        const bool past = i >= n_items;
+        const int ii = past ? n_items - 1 : i;
+        st = ii / passes;
+        pass = ii % passes;
         const int sb = pass * ln.gpp + ln.g;
-        valid = sb < nsb;
-        p = valid ? w + row_of(st) * row_bytes + sb * kQ4KBytes : w;
+        const bool inb = sb < nsb;
+        valid = inb && !past;
+        p = inb ? w + row_of(st) * row_bytes + sb * kQ4KBytes : w;
     };
 
+    float4 xr[kNormRegChunks];
+    const float* xin = nullptr;
+    if constexpr (NORM) {
+        xin = norm_row(nin, nsb * 256);
+        norm_load(xin, nsb * 256, xr);
+    }
     SBLoad A, B;
-    const uint8_t* pa;
-    bool va;
-    int sa, pa_pass;
+    const uint8_t *pa, *pb;
+    bool va, vb;
+    int sa, pa_pass, sb_, pb_pass;
     where(0, pa, va, sa, pa_pass);
     load_sb(pa, 32 * ln.j, A);
+    where(1, pb, vb, sb_, pb_pass);
+    load_sb(pb, 32 * ln.j, B);
     if constexpr (NORM) {
         __shared__ double sh[16];
-        stage_norm_input(nin, nsb * 256, lds, sh);
+        stage_norm_input(nin, xin, nsb * 256, xr, lds, sh);
     } else {
         stage_q8(xq, 0, nb, lds, threadIdx.x, blockDim.x, nullptr);
     }
@@ -448,15 +470,12 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
         }
     };
     for (int i = 0; i < n_items; i += 2) {
-        const uint8_t* pb;
-        bool vb;
-        int sb_, pb_pass;
-        where(i + 1, pb, vb, sb_, pb_pass);
-        load_sb(pb, 32 * ln.j, B);
         item(A, va, sa, pa_pass);
         where(i + 2, pa, va, sa, pa_pass);
         load_sb(pa, 32 * ln.j, A);
         if (i + 1 < n_items) item(B, vb, sb_, pb_pass);
+        where(i + 3, pb, vb, sb_, pb_pass);
+        load_sb(pb, 32 * ln.j, B);
     }
     __syncthreads();
     if (q == 0) {
@@ -584,15 +603,21 @@ static hipError_t launch_nc(const void* w, const void* xq, int64_t xq_col_bytes,
     return hipGetLastError();
 }
 
-// Grid of a GEMV whose workgroups each repeat a prologue: at most one
-// workgroup per CU (up to 16 waves each), every wave with the same number
-// of units (or one fewer).
-void prologue_grid(int64_t units, int* grid, int* threads) {
+// Grid of a GEMV whose workgroups each normalize a k-vector in their
+// prologue: at most one workgroup per CU, so the normalization is repeated
+// about once per CU, and enough waves (up to 16) that every thread
+// normalizes at most one 4-value chunk when k allows (the prologue is bound
+// by each wave's instruction latency, not by the CU's issue rate).  Waves
+// loop over `units` equal work units.
+void prologue_grid(int64_t units, int64_t k, int* grid, int* threads) {
     const int64_t cus = device_cu_count();
-    const int64_t per = (units + cus * 16 - 1) / (cus * 16);
-    const int64_t waves = (units + per - 1) / per;
-    const int64_t wpg = (waves + cus - 1) / cus;
-    *grid = (int)((waves + wpg - 1) / wpg);
+    const int64_t g = units < cus ? units : cus;
+    const int64_t for_units = (units + g - 1) / g;
+    const int64_t for_chunks = (k / 4 + 63) / 64;
+    int64_t wpg = for_units > for_chunks ? for_units : for_chunks;
+    if (wpg > 16) wpg = 16;
+    if (wpg < 1) wpg = 1;
+    *grid = (int)(g > 0 ? g : 1);
     *threads = (int)(64 * wpg);
 }
 
@@ -602,7 +627,7 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, &grid, &threads);
+    prologue_grid(p.n_tiles, k, &grid, &threads);
     MQ_LAUNCH((k_gemv_q4k<1, false, true>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
               (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb,
               p.log2s, p.passes, p.n_tiles, nin);

@@ -74,32 +74,41 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* 
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)npairs * 2 * kQ8Bytes;
 
+    // Items past the wave's last one re-read that last item's lines and are
+    // not computed.
     auto where = [&](int i, const uint8_t*& p, bool& valid, int& row, int& pass, int& P) {
-        if (i >= n_items) { p = w; valid = false; row = M; pass = 0; P = 0; return; }
-        const int t = wave + (i / passes) * W;
-        pass = i % passes;
+        const bool past = i >= n_items;
+        const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
+        const int t = wave + (ii / passes) * W;
+        pass = ii % passes;
         row = t * R + row_local;
         P = pass * S + slot;
-        valid = row < M && P < npairs;
-        p = valid ? w + row * row_bytes + P * (2 * kQ8Bytes) : w;
+        const bool inb = n_items > 0 && row < M && P < npairs;
+        valid = inb && !past;
+        p = inb ? w + row * row_bytes + P * (2 * kQ8Bytes) : w;
     };
 
-    PairLoad A, B;
-    const uint8_t* pa;
-    bool va = false;
-    int ra = 0, passa = 0, Pa = 0;
-    if (n_items > 0) {
-        where(0, pa, va, ra, passa, Pa);
-        load_pair(pa, A);
+    float4 xr[kNormRegChunks];
+    const float* xin = nullptr;
+    if constexpr (NORM) {
+        xin = norm_row(nin, 64 * npairs);
+        norm_load(xin, 64 * npairs, xr);
     }
+    PairLoad A, B;
+    const uint8_t *pa, *pb;
+    bool va, vb;
+    int ra, passa, Pa, rb, passb, Pb;
+    where(0, pa, va, ra, passa, Pa);
+    load_pair(pa, A);
+    where(1, pb, vb, rb, passb, Pb);
+    load_pair(pb, B);
     if constexpr (NORM) {
         __shared__ double sh[16];
-        stage_norm_input(nin, 64 * npairs, lds, sh);
+        stage_norm_input(nin, xin, 64 * npairs, xr, lds, sh);
     } else {
         stage_q8(xq, 0, 2 * npairs, lds, threadIdx.x, blockDim.x, nullptr);
     }
     __syncthreads();
-    if (n_items == 0) return;
 
     double acc = 0.0;
     auto item = [&](const PairLoad& L, bool valid, int row, int pass, int P) {
@@ -111,15 +120,12 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* 
         if (slot == 0 && row < M) y[row] = (float)s;
     };
     for (int i = 0; i < n_items; i += 2) {
-        const uint8_t* pb;
-        bool vb;
-        int rb, passb, Pb;
-        where(i + 1, pb, vb, rb, passb, Pb);
-        load_pair(pb, B);
         item(A, va, ra, passa, Pa);
         where(i + 2, pa, va, ra, passa, Pa);
         load_pair(pa, A);
         if (i + 1 < n_items) item(B, vb, rb, passb, Pb);
+        where(i + 3, pb, vb, rb, passb, Pb);
+        load_pair(pb, B);
     }
 }
 
@@ -183,7 +189,7 @@ hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int
     const Q8Plan p = plan_q8_0(m, npairs);
     const int lds = stage_bytes(2 * npairs);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, &grid, &threads);
+    prologue_grid(p.n_tiles, k, &grid, &threads);
     hipEvent_t e0, e1;
     if (take_next_launch_events(&e0, &e1)) {
         (void)hipStreamSynchronize(stream);

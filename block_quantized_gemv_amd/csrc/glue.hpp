@@ -101,7 +101,8 @@ __device__ __forceinline__ int dpp_i32(int v) {
 // (*sel_step mod n_inputs) is used; q8_copy, if set, receives the q8_0
 // vector from workgroup 0; inc_step, if set, is advanced by one by thread 0
 // of workgroup 0 after it has staged its input (the kernel must not also
-// read it through sel_step).
+// read it through sel_step); exact forces the division path of
+// stage_rmsnorm_q8 everywhere (same results; a test hook).
 struct NormIn {
     const float* x;
     const int64_t* sel_step;
@@ -109,27 +110,186 @@ struct NormIn {
     float eps;
     uint8_t* q8_copy;
     int64_t* inc_step;
+    int exact;          // take the division path for every value (test hook)
 };
+
+// ------------------------------------------- RMSNorm -> q8_0 in a prologue ----
+//
+// Each value needs two correctly rounded divisions, x/denom in f64 and
+// n/d in f32, which as division sequences cost more than the GEMV's own
+// arithmetic.  They are formed as products with a reciprocal instead, and a
+// product is accepted when it provably gives the same result:
+//
+//   t = a * r in f64 with r = 1/b correctly rounded (or within one ulp) is
+//   within 4 f64 ulps of the correctly rounded f64 quotient q.
+//
+// * The f32 value RN_f32(q): read as integers, f64 patterns of one sign are
+//   ordered like their values, and rounding to f32 maps every pattern
+//   strictly between two consecutive f32 midpoints (patterns whose low 29
+//   bits are 2^28) to the same f32.  So RN_f32(t) == RN_f32(q) when t's low
+//   29 bits are more than 16 away from 2^28 and |t| is at least 2^-125
+//   (the f32 normal range, where those patterns are the midpoints).  RN_f32(q) is the reference's x/denom (an f64 division rounded
+//   to f32) and its amax/127 (an f32 division: f64 carries more than
+//   2*24+2 bits, so rounding the quotient to f64 first changes nothing).
+// * A code roundf(RN_f32(n/d)) comes from the f32 product y = n * (1/d)
+//   (see code_checked): unless y lies within |y|*2^-21 of a half-integer,
+//   the code is y rounded half away from zero.
+//
+// When any lane of a wave meets a doubtful case the wave redoes the whole
+// chunk with the divisions themselves.
+
+// RN_f32(t), flagging t near an f32 midpoint.  The caller rules out the
+// f32 subnormal range separately.
+__device__ __forceinline__ float f32_checked(double t, bool& bad) {
+    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint64_t, t);
+    bad |= ((lo & 0x1FFFFFFFu) - (0x10000000u - 16u)) <= 32u;
+    return (float)t;
+}
+
+// clamp(roundf(RN_f32(n/d)), -127, 127) from y = n * r in f32, r within an
+// f32 ulp of 1/d: y is within 1.6*2^-23 of n/d relative, and RN_f32 moves
+// the quotient by at most 2^-24 relative, so the code is y rounded half
+// away from zero unless y lies within |y|*2^-21 of a half-integer
+// (flagged).  y must be finite.
+__device__ __forceinline__ int code_checked(float y, bool& bad) {
+    const float a = fabsf(y);
+    const float fr = a - floorf(a);
+    bad |= fabsf(fr - 0.5f) < a * 0x1p-21f;
+    const int q = min((int)(a + 0.5f), 127);
+    return y < 0.0f ? -q : q;
+}
+
+// 1/d in f32 to within an ulp: hardware estimate and a Newton step.
+__device__ __forceinline__ float recip_f32(float d) {
+    const float r = __builtin_amdgcn_rcpf(d);
+    return fmaf(r, fmaf(-d, r, 1.0f), r);
+}
+
+// One 4-value chunk of a q8_0 block: the block is 8 aligned lanes of the
+// wave (chunks 8b..8b+7), all 64 lanes active.  Gives the 4 codes (packed),
+// the f16 scale bits and the block's code sum (all 8 lanes get it).
+struct ChunkQ8 {
+    uint32_t packed, dbits;
+    int ysum;
+};
+
+__device__ __forceinline__ int code_of(float n, float d) {
+    const float rq = roundf(n / d);
+    return rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
+}
+
+__device__ __forceinline__ int block8_sum(int s) {
+    s += dpp_i32<0xB1>(s);
+    s += dpp_i32<0x4E>(s);
+    s += dpp_i32<0x141>(s);
+    return s;
+}
+
+__device__ __forceinline__ float block8_max(float a) {
+    a = fmaxf(a, dpp_f32<0xB1>(a));      // lane ^ 1
+    a = fmaxf(a, dpp_f32<0x4E>(a));      // lane ^ 2
+    a = fmaxf(a, dpp_f32<0x141>(a));     // the other quad of the 8
+    return a;
+}
+
+__device__ __forceinline__ uint32_t pack4(const int (&q)[4]) {
+    return ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) | (((uint32_t)q[2] & 0xFFu) << 16) |
+           ((uint32_t)q[3] << 24);
+}
+
+// The reference arithmetic: divisions as written.
+__device__ __forceinline__ ChunkQ8 chunk_exact(const float4& v, double denom) {
+#pragma clang fp contract(off)
+    const float n[4] = {(float)((double)v.x / denom), (float)((double)v.y / denom),
+                        (float)((double)v.z / denom), (float)((double)v.w / denom)};
+    const float amax = block8_max(fmaxf(fmaxf(fabsf(n[0]), fabsf(n[1])), fmaxf(fabsf(n[2]), fabsf(n[3]))));
+    const float d32 = amax / 127.0f;
+    ChunkQ8 o;
+    o.dbits = f32_to_f16(d32);
+    const float d = f16_to_f32(o.dbits);
+    int q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = d != 0.0f ? code_of(n[i], d) : 0;
+    o.packed = pack4(q);
+    o.ysum = block8_sum(q[0] + q[1] + q[2] + q[3]);
+    return o;
+}
+
+// The same values through reciprocal products; `bad` is set where they
+// might differ (then chunk_exact is used).  tiny = 2^-124 * denom: an |x|
+// below it could give an f32-subnormal x/denom, which the midpoint test
+// does not cover (zeros are flagged too; they are merely slower).
+__device__ __forceinline__ ChunkQ8 chunk_fast(const float4& v, double rinv, float tiny, bool& bad) {
+#pragma clang fp contract(off)
+    bad |= fminf(fminf(fabsf(v.x), fabsf(v.y)), fminf(fabsf(v.z), fabsf(v.w))) < tiny;
+    const float n[4] = {f32_checked((double)v.x * rinv, bad), f32_checked((double)v.y * rinv, bad),
+                        f32_checked((double)v.z * rinv, bad), f32_checked((double)v.w * rinv, bad)};
+    const float amax = block8_max(fmaxf(fmaxf(fabsf(n[0]), fabsf(n[1])), fmaxf(fabsf(n[2]), fabsf(n[3]))));
+    const double d64 = (double)amax * (1.0 / 127.0);
+    bad |= d64 != 0.0 && d64 < 0x1p-125;
+    float d32 = f32_checked(d64, bad);
+    // The scale is rounded to f32 and then to f16, as the reference does;
+    // the empty asm keeps the compiler from fusing the two conversions into
+    // one f64 -> f16 rounding, which differs in double-rounding cases.
+    asm volatile("" : "+v"(d32));
+    ChunkQ8 o;
+    o.dbits = f32_to_f16(d32);
+    const float d = f16_to_f32(o.dbits);
+    const bool dz = d == 0.0f;
+    const float rd = recip_f32(dz ? 1.0f : d);
+    int q[4];
+    bool bq = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = code_checked(n[i] * rd, bq);
+        q[i] = dz ? 0 : c;
+    }
+    bad |= bq && !dz;
+    o.packed = pack4(q);
+    o.ysum = block8_sum(q[0] + q[1] + q[2] + q[3]);
+    return o;
+}
+
+// Chunks of the f32 input held in registers through the prologue.
+constexpr int kNormRegChunks = 2;
 
 // Q8(RMSNorm(x)) of k values (k % 32 == 0, x 16-byte aligned), computed by
 // the whole workgroup (blockDim.x % 64 == 0) and written to lds in the
 // layout of stage_q8.  Thread t owns the 4-value chunks t, t+T, ... (T =
-// blockDim.x): it sums their squares in order, the workgroup adds the
+// blockDim.x); xr holds its first kNormRegChunks of them (loaded by
+// norm_load).  It sums their squares in order, the workgroup adds the
 // per-thread sums in the fixed order of block_sum_f64, and each value is
-// divided by sqrt(mean + eps) in f64 and rounded to f32 once.  A q8_0
-// block is then 8 consecutive chunks, i.e. 8 aligned lanes: its amax, f16
-// scale and codes are formed with exactly the operations of quantize_lane.
-// The caller synchronizes the workgroup before reading lds.
+// x/sqrt(mean + eps) in f64 rounded to f32; a q8_0 block is 8 consecutive
+// chunks, i.e. 8 aligned lanes, and its amax, f16 scale and codes follow
+// quantize_lane.  With `exact` every chunk takes the division path (a test
+// hook: the results are the same).  The caller synchronizes the workgroup
+// before reading lds.
+__device__ __forceinline__ void norm_load(const float* __restrict__ x, int k, float4 (&xr)[kNormRegChunks]) {
+    const float4* x4 = (const float4*)x;
+#pragma unroll
+    for (int r = 0; r < kNormRegChunks; ++r) {
+        const int c = r * (int)blockDim.x + (int)threadIdx.x;
+        xr[r] = c < (k >> 2) ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+}
+
 __device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, int k, float eps,
+                                                 const float4 (&xr)[kNormRegChunks], bool exact,
                                                  uint8_t* __restrict__ lds, double* sh,
                                                  uint8_t* __restrict__ q8_copy) {
 #pragma clang fp contract(off)
     const int nch = k >> 2;
     const int T = blockDim.x;
     const float4* x4 = (const float4*)x;
+    const int rounds = (nch + T - 1) / T;
+    auto chunk = [&](int r) {
+        if (r < kNormRegChunks) return xr[r];
+        const int c = r * T + (int)threadIdx.x;
+        return c < nch ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    };
     double ss = 0.0;
-    for (int c = threadIdx.x; c < nch; c += T) {
-        const float4 v = x4[c];
+    for (int r = 0; r < rounds; ++r) {
+        const float4 v = chunk(r);      // zero past the end
         ss += (double)v.x * (double)v.x;
         ss += (double)v.y * (double)v.y;
         ss += (double)v.z * (double)v.z;
@@ -137,61 +297,48 @@ __device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, in
     }
     ss = block_sum_f64(ss, sh);
     const double denom = sqrt(ss / (double)k + (double)eps);
-    const int rounds = (nch + T - 1) / T;
+    const double rinv = 1.0 / denom;
+    const float tiny = (float)(0x1p-124 * denom);
     for (int r = 0; r < rounds; ++r) {
         const int c = r * T + (int)threadIdx.x;
         const bool in = c < nch;      // whole 8-lane groups are in or out
-        const float4 v = in ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        const float n[4] = {(float)((double)v.x / denom), (float)((double)v.y / denom),
-                            (float)((double)v.z / denom), (float)((double)v.w / denom)};
-        float amax = fmaxf(fmaxf(fabsf(n[0]), fabsf(n[1])), fmaxf(fabsf(n[2]), fabsf(n[3])));
-        amax = fmaxf(amax, dpp_f32<0xB1>(amax));     // lane ^ 1
-        amax = fmaxf(amax, dpp_f32<0x4E>(amax));     // lane ^ 2
-        amax = fmaxf(amax, dpp_f32<0x141>(amax));    // the other quad of the 8
-        const float d32 = amax / 127.0f;
-        const uint32_t dbits = f32_to_f16(d32);
-        const float d = f16_to_f32(dbits);
-        uint32_t packed = 0;
-        int s = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int q = 0;
-            if (d != 0.0f) {
-                const float rq = roundf(n[i] / d);
-                q = rq > 127.0f ? 127 : (rq < -127.0f ? -127 : (int)rq);
-            }
-            packed |= ((uint32_t)q & 0xFFu) << (8 * i);
-            s += q;
-        }
-        s += dpp_i32<0xB1>(s);
-        s += dpp_i32<0x4E>(s);
-        s += dpp_i32<0x141>(s);
+        const float4 v = chunk(r);
+        bool bad = exact;
+        ChunkQ8 o = chunk_fast(v, rinv, tiny, bad);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) o = chunk_exact(v, denom);   // wave-uniform
         if (in) {
             const int b = c >> 3, cb = c & 7;
             const int P = b >> 1, half = b & 1, L = P & 63;
             uint8_t* g = lds + (P >> 6) * kStageGroupBytes;
-            *(uint32_t*)(g + ((2 * half + (cb >> 2)) * 64 + L) * 16 + (cb & 3) * 4) = packed;
+            *(uint32_t*)(g + ((2 * half + (cb >> 2)) * 64 + L) * 16 + (cb & 3) * 4) = o.packed;
             if (cb == 0) {
-                *(double*)(g + 4096 + L * 16 + half * 8) = (double)d;
-                *(double*)(g + 5120 + L * 16 + half * 8) = (double)d * (double)s;
+                const double d = (double)f16_to_f32(o.dbits);
+                *(double*)(g + 4096 + L * 16 + half * 8) = d;
+                *(double*)(g + 5120 + L * 16 + half * 8) = d * (double)o.ysum;
             }
             if (q8_copy) {
                 uint8_t* blk = q8_copy + (int64_t)b * kQ8Bytes;
-                if (cb == 0) *(uint16_t*)blk = (uint16_t)dbits;
-                *(uint16_t*)(blk + 2 + 4 * cb) = (uint16_t)(packed & 0xFFFFu);
-                *(uint16_t*)(blk + 4 + 4 * cb) = (uint16_t)(packed >> 16);
+                if (cb == 0) *(uint16_t*)blk = (uint16_t)o.dbits;
+                *(uint16_t*)(blk + 2 + 4 * cb) = (uint16_t)(o.packed & 0xFFFFu);
+                *(uint16_t*)(blk + 4 + 4 * cb) = (uint16_t)(o.packed >> 16);
             }
         }
     }
 }
 
-// Prologue of a GEMV fed by a NormIn: selects the input row, stages
-// Q8(RMSNorm(x)) into lds and advances the step counter if asked.
-__device__ __forceinline__ void stage_norm_input(const NormIn& in, int k, uint8_t* __restrict__ lds,
-                                                 double* sh) {
+// The input row of a GEMV fed by a NormIn.
+__device__ __forceinline__ const float* norm_row(const NormIn& in, int k) {
     const float* x = in.x;
     if (in.sel_step) x += (int64_t)((uint64_t)*in.sel_step % (uint64_t)in.n_inputs) * k;
-    stage_rmsnorm_q8(x, k, in.eps, lds, sh, blockIdx.x == 0 ? in.q8_copy : nullptr);
+    return x;
+}
+
+// Prologue of a GEMV fed by a NormIn (x = norm_row, xr from norm_load):
+// stages Q8(RMSNorm(x)) into lds and advances the step counter if asked.
+__device__ __forceinline__ void stage_norm_input(const NormIn& in, const float* x, int k,
+                                                 const float4 (&xr)[kNormRegChunks], uint8_t* __restrict__ lds,
+                                                 double* sh) {
+    stage_rmsnorm_q8(x, k, in.eps, xr, in.exact != 0, lds, sh, blockIdx.x == 0 ? in.q8_copy : nullptr);
     if (in.inc_step && blockIdx.x == 0 && threadIdx.x == 0) *in.inc_step += 1;
 }
 

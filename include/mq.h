@@ -176,7 +176,10 @@ int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t
  */
 typedef struct mq_chain mq_chain;
 
-enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u };
+/* MQ_EXACT_GLUE is a test hook: the RMSNorm->q8_0 prologues compute every
+ * value with the divisions themselves instead of reciprocal products that
+ * are checked to round the same way; the results are byte-identical. */
+enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u };
 enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
 
 typedef struct {
@@ -191,7 +194,7 @@ typedef struct {
     int n_inputs;                      /* >= 1 */
     float* logits;                     /* device f32 [vocab] */
     float eps;
-    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES */
+    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE */
 } mq_chain_desc;
 
 /* Validates, allocates every device buffer the step needs (nothing is

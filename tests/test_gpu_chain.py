@@ -112,6 +112,39 @@ def test_graph_equals_eager_over_replays(mq, o, small_model):
     e.close()
 
 
+def _fast_vs_exact_glue(mq, model, W_dev, xd, n_steps):
+    keep = mq.MQ_KEEP_INTERMEDIATES
+    f = mq.DecodeChain(model, W_dev, xd, flags=keep)
+    e = mq.DecodeChain(model, W_dev, xd, flags=keep | mq.MQ_EXACT_GLUE)
+    of, oe = _run_steps(mq, f, n_steps, mq.MQ_GRAPH, traces=True), _run_steps(mq, e, n_steps, mq.MQ_GRAPH, traces=True)
+    for i, (u, v) in enumerate(zip(of, oe)):
+        for part, p, q in zip(("logits", "q8 trace", "f32 trace"), u, v):
+            assert _same(p, q), f"reciprocal-product glue != division glue at step {i} ({part})"
+    f.close()
+    e.close()
+
+
+def test_glue_fast_path_equals_divisions(mq, small_model):
+    """The prologues' RMSNorm->q8_0 forms x/denom and n/d as checked
+    reciprocal products; forcing the division path everywhere must give the
+    same bytes (0.5B widths: one 4-value chunk per thread or less)."""
+    model, W, Wd, X = small_model
+    _fast_vs_exact_glue(mq, model, Wd, to_dev(X), 4)
+
+
+def test_glue_fast_path_equals_divisions_7b_width(mq):
+    """Same at hidden 3584, where threads hold one or two chunks, plus x
+    scaled by 1e-30 and 1e30 (denominators far from 1) and a row of zeros."""
+    from block_quantized_gemv_amd import synth, workloads
+    model = dataclasses.replace(workloads.DECODE_7B, n_layers=2)
+    W = model_weights(model, 2)
+    X = synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (4, model.hidden))
+    X[1] *= np.float32(1e-30)
+    X[2] *= np.float32(1e30)
+    X[3] = 0.0
+    _fast_vs_exact_glue(mq, model, _dev_weights(W), to_dev(X), 4)
+
+
 def test_graph_aa_control(mq, small_model):
     model, W, Wd, X = small_model
     xd = to_dev(X)
