@@ -151,4 +151,45 @@ __device__ __forceinline__ void read_pair(const uint8_t* __restrict__ lds, int P
     }
 }
 
+// ------------------------------------------------------- item streaming ----
+// A wave streams its work items 0..n-1 through two register buffers A and B
+// (a ping-pong): `fetch(i, buf)` issues item i's loads into buf (for i >= n
+// it must load in-bounds lines and mark the item invalid), `use(buf)`
+// computes the item held in buf.  The loads of one item are in flight while
+// the other computes, and the compiler only has to wait for the buffer it
+// is about to use.
+//
+// EARLY: the caller fetched items 0 and 1 before its prologue (whose own
+// loads were issued first), and the last round is peeled so that nothing
+// is fetched past the end.  Otherwise the caller fetched item 0 before its
+// prologue (whose loads then complete right behind it) and item i+1 is
+// fetched at the top of each round.  Memory returns in order per wave, so a
+// prologue that loads after the early fetches waits for them as well.
+template <bool EARLY, class Buf, class Fetch, class Use>
+__device__ __forceinline__ void stream_items(int n, Buf& A, Buf& B, Fetch&& fetch, Use&& use) {
+    if constexpr (EARLY) {
+        int i = 0;
+        for (; i + 3 < n; i += 2) {
+            use(A);
+            fetch(i + 2, A);
+            use(B);
+            fetch(i + 3, B);
+        }
+        if (i < n) {
+            use(A);
+            const bool more = i + 2 < n;
+            if (more) fetch(i + 2, A);
+            if (i + 1 < n) use(B);
+            if (more) use(A);
+        }
+    } else {
+        for (int i = 0; i < n; i += 2) {
+            fetch(i + 1, B);
+            use(A);
+            fetch(i + 2, A);
+            if (i + 1 < n) use(B);
+        }
+    }
+}
+
 }  // namespace mq

@@ -155,42 +155,47 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
     const int W = gridDim.x * (blockDim.x >> 6);
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    // With NORM, consecutive units go to different workgroups (one per CU),
+    // so every CU gets the same share.
+    const int wave = NORM ? (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x
+                          : blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
 
-    // Items past the wave's last one re-read that last item's lines (cache
-    // hits spread over the channels) and are not computed.
-    auto where = [&](int i, const uint8_t*& p, bool& valid, int& row, int& pass) {
+    // Items past the wave's last one re-read that item's lines and are not
+    // computed: those requests merge with the real ones in the cache,
+    // whereas one fixed address for all waves would queue thousands of
+    // requests on a single channel.
+    struct Item {
+        SBLoad L;
+        bool valid;
+        int row, pass;
+    };
+    auto fetch = [&](int i, Item& it) {
         const bool past = i >= n_items;
         const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
         const int t = wave + (ii / passes) * W;
-        pass = ii % passes;
-        row = t * ln.R + ln.row_local;
-        const int sb = pass * ln.gpp + ln.g;
-        const bool inb = n_items > 0 && row < M && sb < nsb;
-        valid = inb && !past;
-        p = inb ? w + row * row_bytes + sb * kQ4KBytes : w;
+        it.pass = ii % passes;
+        it.row = t * ln.R + ln.row_local;
+        const int sb = it.pass * ln.gpp + ln.g;
+        const bool inb = n_items > 0 && it.row < M && sb < nsb;
+        it.valid = inb && !past;
+        if (past) it.row = M;
+        load_sb(inb ? w + (int64_t)(t * ln.R + ln.row_local) * row_bytes + sb * kQ4KBytes : w, 32 * ln.j, it.L);
     };
 
-    // The f32 input (NORM) is requested first, then the first two items:
-    // their weight loads are in flight while the prologue stages the
-    // activation.
+    // With NORM the f32 input is requested first, then items 0 and 1, whose
+    // weight loads are in flight while the prologue normalizes.
     float4 xr[kNormRegChunks];
     const float* xin = nullptr;
     if constexpr (NORM) {
         xin = norm_row(nin, nsb * 256);
         norm_load(xin, nsb * 256, xr);
     }
-    SBLoad A, B;
-    const uint8_t *pa, *pb;
-    bool va, vb;
-    int ra, pa_pass, rb, pb_pass;
-    where(0, pa, va, ra, pa_pass);
-    load_sb(pa, 32 * ln.j, A);
-    where(1, pb, vb, rb, pb_pass);
-    load_sb(pb, 32 * ln.j, B);
+    Item A, B;
+    fetch(0, A);
+    if constexpr (NORM) fetch(1, B);
     if constexpr (NORM) {
         __shared__ double sh[16];
         stage_norm_input(nin, xin, nsb * 256, xr, lds, sh);
@@ -205,30 +210,17 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
     double acc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.0;
-
-    auto finish = [&](int row, int pass) {
-        if (pass != passes - 1) return;
+    stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
+        sb_item<NC, DUMP>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
+                          (int64_t)it.row * nb);
+        if (it.pass != passes - 1) return;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const double v = group_sum_f64(acc[c], ln.log2s);
-            if ((ln.lane & (ln.S - 1)) == 0 && row < M) y[(int64_t)row * NC + c] = (float)v;
+            if ((ln.lane & (ln.S - 1)) == 0 && it.row < M) y[(int64_t)it.row * NC + c] = (float)v;
             acc[c] = 0.0;
         }
-    };
-
-    // Items i (in A) and i+1 (in B) are in flight at the top of each round.
-    for (int i = 0; i < n_items; i += 2) {
-        sb_item<NC, DUMP>(A, ln, pair_of(ln, pa_pass), va, lds, col_bytes, acc, dump_isum, (int64_t)ra * nb);
-        finish(ra, pa_pass);
-        where(i + 2, pa, va, ra, pa_pass);
-        load_sb(pa, 32 * ln.j, A);
-        if (i + 1 < n_items) {
-            sb_item<NC, DUMP>(B, ln, pair_of(ln, pb_pass), vb, lds, col_bytes, acc, dump_isum, (int64_t)rb * nb);
-            finish(rb, pb_pass);
-        }
-        where(i + 3, pb, vb, rb, pb_pass);
-        load_sb(pb, 32 * ln.j, B);
-    }
+    });
 }
 
 // --------------------------------------------------------------------------
@@ -424,16 +416,22 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     // tile of the half), pass i % passes
     auto local_of = [&](int st) { return (32 / WV) * q + 4 * (st % TPH) + ln.row_local; };
     auto row_of = [&](int st) { return (st / TPH) * inter + 32 * u + local_of(st); };
-    // Items past the last re-read the last item's lines and are not computed.
-    auto where = [&](int i, const uint8_t*& p, bool& valid, int& st, int& pass) {
+    // Items past the last re-read the last item's lines (see k_gemv_q4k)
+    // and are not computed.
+    struct Item {
+        SBLoad L;
+        bool valid;
+        int st, pass;
+    };
+    auto fetch = [&](int i, Item& it) {
         const bool past = i >= n_items;
         const int ii = past ? n_items - 1 : i;
-        st = ii / passes;
-        pass = ii % passes;
-        const int sb = pass * ln.gpp + ln.g;
+        it.st = ii / passes;
+        it.pass = ii % passes;
+        const int sb = it.pass * ln.gpp + ln.g;
         const bool inb = sb < nsb;
-        valid = inb && !past;
-        p = inb ? w + row_of(st) * row_bytes + sb * kQ4KBytes : w;
+        it.valid = inb && !past;
+        load_sb(inb ? w + row_of(it.st) * row_bytes + sb * kQ4KBytes : w, 32 * ln.j, it.L);
     };
 
     float4 xr[kNormRegChunks];
@@ -442,14 +440,9 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
         xin = norm_row(nin, nsb * 256);
         norm_load(xin, nsb * 256, xr);
     }
-    SBLoad A, B;
-    const uint8_t *pa, *pb;
-    bool va, vb;
-    int sa, pa_pass, sb_, pb_pass;
-    where(0, pa, va, sa, pa_pass);
-    load_sb(pa, 32 * ln.j, A);
-    where(1, pb, vb, sb_, pb_pass);
-    load_sb(pb, 32 * ln.j, B);
+    Item A, B;
+    fetch(0, A);
+    if constexpr (NORM) fetch(1, B);
     if constexpr (NORM) {
         __shared__ double sh[16];
         stage_norm_input(nin, xin, nsb * 256, xr, lds, sh);
@@ -459,24 +452,16 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     __syncthreads();
 
     double acc[1] = {0.0};
-    auto item = [&](const SBLoad& L, bool valid, int st, int pass) {
-        sb_item<1, false>(L, ln, pair_of(ln, pass), valid, lds, 0, acc, nullptr, 0);
-        if (pass != passes - 1) return;
+    stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
+        sb_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
+        if (it.pass != passes - 1) return;
         const float v = (float)group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
         if ((ln.lane & 15) == 0) {
-            gu_s[(st / TPH) * 32 + local_of(st)] = v;
-            if (gu_out) gu_out[row_of(st)] = v;
+            gu_s[(it.st / TPH) * 32 + local_of(it.st)] = v;
+            if (gu_out) gu_out[row_of(it.st)] = v;
         }
-    };
-    for (int i = 0; i < n_items; i += 2) {
-        item(A, va, sa, pa_pass);
-        where(i + 2, pa, va, sa, pa_pass);
-        load_sb(pa, 32 * ln.j, A);
-        if (i + 1 < n_items) item(B, vb, sb_, pb_pass);
-        where(i + 3, pb, vb, sb_, pb_pass);
-        load_sb(pb, 32 * ln.j, B);
-    }
+    });
     __syncthreads();
     if (q == 0) {
         const int i = ln.lane;

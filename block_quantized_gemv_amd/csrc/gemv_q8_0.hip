@@ -69,23 +69,32 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* 
     const int S = 1 << log2s, R = 64 >> log2s;
     const int row_local = lane >> log2s, slot = lane & (S - 1);
     const int W = gridDim.x * (blockDim.x >> 6);
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    // With NORM, consecutive units go to different workgroups (one per CU).
+    const int wave = NORM ? (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x
+                          : blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)npairs * 2 * kQ8Bytes;
 
-    // Items past the wave's last one re-read that last item's lines and are
-    // not computed.
-    auto where = [&](int i, const uint8_t*& p, bool& valid, int& row, int& pass, int& P) {
+    // Items past the wave's last one re-read that item's lines and are not
+    // computed (one fixed address for all waves would queue thousands of
+    // requests on a single channel).
+    struct Item {
+        PairLoad L;
+        bool valid;
+        int row, pass, P;
+    };
+    auto fetch = [&](int i, Item& it) {
         const bool past = i >= n_items;
         const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
         const int t = wave + (ii / passes) * W;
-        pass = ii % passes;
-        row = t * R + row_local;
-        P = pass * S + slot;
-        const bool inb = n_items > 0 && row < M && P < npairs;
-        valid = inb && !past;
-        p = inb ? w + row * row_bytes + P * (2 * kQ8Bytes) : w;
+        it.pass = ii % passes;
+        it.row = t * R + row_local;
+        it.P = it.pass * S + slot;
+        const bool inb = n_items > 0 && it.row < M && it.P < npairs;
+        it.valid = inb && !past;
+        load_pair(inb ? w + (int64_t)it.row * row_bytes + it.P * (2 * kQ8Bytes) : w, it.L);
+        if (past) it.row = M;
     };
 
     float4 xr[kNormRegChunks];
@@ -94,14 +103,9 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* 
         xin = norm_row(nin, 64 * npairs);
         norm_load(xin, 64 * npairs, xr);
     }
-    PairLoad A, B;
-    const uint8_t *pa, *pb;
-    bool va, vb;
-    int ra, passa, Pa, rb, passb, Pb;
-    where(0, pa, va, ra, passa, Pa);
-    load_pair(pa, A);
-    where(1, pb, vb, rb, passb, Pb);
-    load_pair(pb, B);
+    Item A, B;
+    fetch(0, A);
+    if constexpr (NORM) fetch(1, B);
     if constexpr (NORM) {
         __shared__ double sh[16];
         stage_norm_input(nin, xin, 64 * npairs, xr, lds, sh);
@@ -111,22 +115,15 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* 
     __syncthreads();
 
     double acc = 0.0;
-    auto item = [&](const PairLoad& L, bool valid, int row, int pass, int P) {
-        const double v = pair_item<DUMP>(L, lds, valid ? P : 0, dump_isum, (int64_t)row * 2 * npairs, valid);
-        acc += valid ? v : 0.0;
-        if (pass != passes - 1) return;
+    stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
+        const double v = pair_item<DUMP>(it.L, lds, it.valid ? it.P : 0, dump_isum,
+                                         (int64_t)it.row * 2 * npairs, it.valid);
+        acc += it.valid ? v : 0.0;
+        if (it.pass != passes - 1) return;
         const double s = group_sum_f64(acc, log2s);
         acc = 0.0;
-        if (slot == 0 && row < M) y[row] = (float)s;
-    };
-    for (int i = 0; i < n_items; i += 2) {
-        item(A, va, ra, passa, Pa);
-        where(i + 2, pa, va, ra, passa, Pa);
-        load_pair(pa, A);
-        if (i + 1 < n_items) item(B, vb, rb, passb, Pb);
-        where(i + 3, pb, vb, rb, passb, Pb);
-        load_pair(pb, B);
-    }
+        if (slot == 0 && it.row < M) y[it.row] = (float)s;
+    });
 }
 
 Q8Plan plan_q8_0(int64_t m, int npairs) {
