@@ -103,6 +103,23 @@ __device__ __forceinline__ uint32_t load_q8_block(const uint8_t* blk, uint32_t (
     return shift ? (w[0] >> 16) : (w[0] & 0xFFFFu);
 }
 
+// Writes block b (relative index) of a staged vector: codes, (double)d and
+// d * (sum of codes).  Returns the code sum.
+__device__ __forceinline__ int stage_q8_block(int b, uint32_t dbits, const uint32_t (&q)[8],
+                                              uint8_t* __restrict__ lds) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot4(q[i], 0x01010101u, s);
+    const double d = (double)f16_to_f32(dbits);
+    const int P = b >> 1, half = b & 1, G = P >> 6, L = P & 63;
+    uint8_t* g = lds + G * kStageGroupBytes;
+    *(u32x4*)(g + ((2 * half + 0) * 64 + L) * 16) = u32x4{q[0], q[1], q[2], q[3]};
+    *(u32x4*)(g + ((2 * half + 1) * 64 + L) * 16) = u32x4{q[4], q[5], q[6], q[7]};
+    *(double*)(g + 4096 + L * 16 + half * 8) = d;
+    *(double*)(g + 5120 + L * 16 + half * 8) = d * (double)s;
+    return s;
+}
+
 // Stage blocks [b0, b0 + nb) of the vector at xq into the layout above at
 // lds (relative block index starts at 0).  Optionally records the int32
 // code sums (for the debug dump).
@@ -112,17 +129,38 @@ __device__ __forceinline__ void stage_q8(const uint8_t* __restrict__ xq, int b0,
     for (int b = tid; b < nb; b += nthreads) {
         uint32_t q[8];
         const uint32_t dbits = load_q8_block(xq + (int64_t)(b0 + b) * kQ8Bytes, q);
-        int s = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s = dot4(q[i], 0x01010101u, s);
-        const double d = (double)f16_to_f32(dbits);
-        const int P = b >> 1, half = b & 1, G = P >> 6, L = P & 63;
-        uint8_t* g = lds + G * kStageGroupBytes;
-        *(u32x4*)(g + ((2 * half + 0) * 64 + L) * 16) = u32x4{q[0], q[1], q[2], q[3]};
-        *(u32x4*)(g + ((2 * half + 1) * 64 + L) * 16) = u32x4{q[4], q[5], q[6], q[7]};
-        *(double*)(g + 4096 + L * 16 + half * 8) = d;
-        *(double*)(g + 5120 + L * 16 + half * 8) = d * (double)s;
+        const int s = stage_q8_block(b, dbits, q, lds);
         if (ysum_out) ysum_out[b0 + b] = s;
+    }
+}
+
+// Staging in two steps, so that a kernel can request its activation before
+// its first weights: stage_q8_load reads the thread's first kStageRegBlocks
+// blocks (b = tid + r*blockDim.x) into registers, stage_q8_store writes
+// them, and any further blocks, into lds.
+constexpr int kStageRegBlocks = 2;
+struct Q8Regs {
+    uint32_t q[kStageRegBlocks][8];
+    uint32_t d[kStageRegBlocks];
+};
+__device__ __forceinline__ void stage_q8_load(const uint8_t* __restrict__ xq, int nb, Q8Regs& r) {
+#pragma unroll
+    for (int k = 0; k < kStageRegBlocks; ++k) {
+        const int b = (int)threadIdx.x + k * (int)blockDim.x;
+        r.d[k] = load_q8_block(xq + (int64_t)(b < nb ? b : 0) * kQ8Bytes, r.q[k]);
+    }
+}
+__device__ __forceinline__ void stage_q8_store(const uint8_t* __restrict__ xq, int nb, const Q8Regs& r,
+                                               uint8_t* __restrict__ lds) {
+#pragma unroll
+    for (int k = 0; k < kStageRegBlocks; ++k) {
+        const int b = (int)threadIdx.x + k * (int)blockDim.x;
+        if (b < nb) stage_q8_block(b, r.d[k], r.q[k], lds);
+    }
+    for (int b = (int)threadIdx.x + kStageRegBlocks * (int)blockDim.x; b < nb; b += (int)blockDim.x) {
+        uint32_t q[8];
+        const uint32_t dbits = load_q8_block(xq + (int64_t)b * kQ8Bytes, q);
+        stage_q8_block(b, dbits, q, lds);
     }
 }
 

@@ -141,12 +141,19 @@ __device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P,
 // --------------------------------------------------------------------------
 // Full staging: all NC activation columns live in LDS.  Wave w owns tiles
 // w, w+W, w+2W, ... (W = waves in the grid); its items are (tile, pass) in
-// that order.  With NORM the single activation column is Q8(RMSNorm(x)) of
-// the f32 vector `nin` describes, formed by each workgroup in its prologue
-// (workgroups of up to 1024 threads, about one per CU, so that the
-// normalization is done once per CU); otherwise xq holds q8_0 columns.
-template <int NC, bool DUMP, bool NORM>
-__global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
+// that order.  Where the activation comes from (SRC):
+//   kSrcQ8       q8_0 columns at xq, staged by 256-thread workgroups
+//                (several per CU) after the first item is requested;
+//   kSrcQ8Early  one q8_0 column at xq, requested before the weights and
+//                staged by one workgroup of up to 1024 threads per CU;
+//   kSrcNorm     Q8(RMSNorm(x)) of the f32 vector `nin` describes, formed
+//                by one workgroup of up to 1024 threads per CU.
+// The last two fetch two items before the prologue and give consecutive
+// tiles to different workgroups, so that every CU gets the same share.
+constexpr int kSrcQ8 = 0, kSrcQ8Early = 1, kSrcNorm = 2;
+
+template <int NC, bool DUMP, int SRC>
+__global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
     int M, int nsb, int log2s, int passes, int n_tiles, NormIn nin) {
@@ -155,10 +162,10 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
     const int W = gridDim.x * (blockDim.x >> 6);
-    // With NORM, consecutive units go to different workgroups (one per CU),
-    // so every CU gets the same share.
-    const int wave = NORM ? (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x
-                          : blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    constexpr bool kEarly = SRC != kSrcQ8;
+    static_assert(SRC == kSrcQ8 || (NC == 1 && !DUMP), "early staging takes one column");
+    const int wave = kEarly ? (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x
+                            : blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
@@ -185,20 +192,24 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
         load_sb(inb ? w + (int64_t)(t * ln.R + ln.row_local) * row_bytes + sb * kQ4KBytes : w, 32 * ln.j, it.L);
     };
 
-    // With NORM the f32 input is requested first, then items 0 and 1, whose
-    // weight loads are in flight while the prologue normalizes.
+    // Early sources: the activation is requested first, then items 0 and
+    // 1, whose weight loads are in flight while the prologue stages it.
     float4 xr[kNormRegChunks];
+    Q8Regs qr;
     const float* xin = nullptr;
-    if constexpr (NORM) {
+    if constexpr (SRC == kSrcNorm) {
         xin = norm_row(nin, nsb * 256);
         norm_load(xin, nsb * 256, xr);
     }
+    if constexpr (SRC == kSrcQ8Early) stage_q8_load(xq, nb, qr);
     Item A, B;
     fetch(0, A);
-    if constexpr (NORM) fetch(1, B);
-    if constexpr (NORM) {
+    if constexpr (kEarly) fetch(1, B);
+    if constexpr (SRC == kSrcNorm) {
         __shared__ double sh[16];
         stage_norm_input(nin, xin, nsb * 256, xr, lds, sh);
+    } else if constexpr (SRC == kSrcQ8Early) {
+        stage_q8_store(xq, nb, qr, lds);
     } else {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q4k(
     double acc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.0;
-    stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
+    stream_items<kEarly>(n_items, A, B, fetch, [&](const Item& it) {
         sb_item<NC, DUMP>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
                           (int64_t)it.row * nb);
         if (it.pass != passes - 1) return;
@@ -581,29 +592,42 @@ static hipError_t launch_nc(const void* w, const void* xq, int64_t xq_col_bytes,
                             hipStream_t stream) {
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = NC * stage_bytes(nsb * 8);
-    const void* fn = (const void*)k_gemv_q4k<NC, DUMP, false>;
-    MQ_LAUNCH((k_gemv_q4k<NC, DUMP, false>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds, stream,
+    const void* fn = (const void*)k_gemv_q4k<NC, DUMP, kSrcQ8>;
+    MQ_LAUNCH((k_gemv_q4k<NC, DUMP, kSrcQ8>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds, stream,
               (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, y, dump_isum, dump_ysum, (int)m, nsb,
               p.log2s, p.passes, p.n_tiles, NormIn{});
     return hipGetLastError();
 }
 
-// Grid of a GEMV whose workgroups each normalize a k-vector in their
-// prologue: at most one workgroup per CU, so the normalization is repeated
-// about once per CU, and enough waves (up to 16) that every thread
-// normalizes at most one 4-value chunk when k allows (the prologue is bound
-// by each wave's instruction latency, not by the CU's issue rate).  Waves
-// loop over `units` equal work units.
-void prologue_grid(int64_t units, int64_t k, int* grid, int* threads) {
+// Grid of a GEMV whose workgroups each stage the activation in a prologue
+// of `prologue` per-thread steps: at most one workgroup per CU, so the
+// prologue is repeated about once per CU, and enough waves (up to 16) that
+// every thread takes at most one step when possible (a prologue is bound by
+// each wave's instruction latency, not by the CU's issue rate).  Waves loop
+// over `units` equal work units.
+void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads) {
     const int64_t cus = device_cu_count();
     const int64_t g = units < cus ? units : cus;
     const int64_t for_units = (units + g - 1) / g;
-    const int64_t for_chunks = (k / 4 + 63) / 64;
+    const int64_t for_chunks = (prologue + 63) / 64;
     int64_t wpg = for_units > for_chunks ? for_units : for_chunks;
     if (wpg > 16) wpg = 16;
     if (wpg < 1) wpg = 1;
     *grid = (int)(g > 0 ? g : 1);
     *threads = (int)(64 * wpg);
+}
+
+// One q8_0 column with early staging (see k_gemv_q4k).
+static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64_t m, int nsb,
+                                  hipStream_t stream) {
+    const Q4KPlan p = plan_q4k(m, nsb);
+    const int lds = stage_bytes(nsb * 8);
+    int grid = 1, threads = 64;
+    prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads);
+    MQ_LAUNCH((k_gemv_q4k<1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
+              (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb, p.log2s,
+              p.passes, p.n_tiles, NormIn{});
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
@@ -612,8 +636,8 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, k, &grid, &threads);
-    MQ_LAUNCH((k_gemv_q4k<1, false, true>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
+    prologue_grid(p.n_tiles, k / 4, &grid, &threads);
+    MQ_LAUNCH((k_gemv_q4k<1, false, kSrcNorm>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
               (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb,
               p.log2s, p.passes, p.n_tiles, nin);
     return hipGetLastError();
@@ -625,7 +649,7 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, 
     const int nsb = (int)(k / 256);
     if (dump_isum) return launch_nc<1, true>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, stream);
     switch (ncols) {
-        case 1: return launch_nc<1, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 1: return launch_q8_early(w, xq, y, m, nsb, stream);
         case 2: return launch_nc<2, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
         case 3: return launch_nc<3, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
         case 4: return launch_nc<4, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);

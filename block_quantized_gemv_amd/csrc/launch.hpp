@@ -47,8 +47,9 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
 hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
                                   int64_t inter, int64_t k, hipStream_t stream);
 // Workgroups and threads per workgroup for `units` equal work units of a
-// kernel whose workgroups each normalize a k-vector in their prologue.
-void prologue_grid(int64_t units, int64_t k, int* grid, int* threads);
+// kernel whose workgroups each run a prologue of `prologue` per-thread
+// steps (about one workgroup per CU).
+void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads);
 // Split-k variant for shapes whose activation does not fit in LDS; `part`
 // holds n_split*m*ncols doubles.
 int gemv_q4k_splitk_nsplit(int64_t k);
