@@ -150,13 +150,13 @@ def gemv_kinds(model):
     prologue, q8_0 otherwise) + output written (f32, or q8_0 after SwiGLU)."""
     from block_quantized_gemv_amd import workloads as wl
     H, I, Q = model.hidden, model.inter, model.qkv_rows
-    norm = "mq::k_gemv_q4k<1,false,true>"
+    norm = "mq::k_gemv_q4k<1,false,2>"
     kinds = []
     for _ in range(model.n_layers):
         kinds += [("qkv", norm, wl.q4k_bytes(Q, H) + 4 * H + 4 * Q),
                   ("o", norm, wl.q4k_bytes(H, H) + 4 * H + 4 * H),
                   ("gate/up", "mq::k_gemv_q4k_swiglu<true>", wl.q4k_bytes(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
-                  ("down", "mq::k_gemv_q4k<1,false,false>", wl.q4k_bytes(H, I) + wl.q8_bytes(1, I) + 4 * H)]
+                  ("down", "mq::k_gemv_q4k<1,false,1>", wl.q4k_bytes(H, I) + wl.q8_bytes(1, I) + 4 * H)]
     kinds.append(("lm_head", "mq::k_gemv_q8_0<false,true>", wl.q8_bytes(model.vocab, H) + 4 * H + 4 * model.vocab))
     return kinds
 
