@@ -278,7 +278,7 @@ int mq_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts, 
     const int lds = (xq_stride_bytes ? n_sel : 1) * stage_bytes((int)(k / 32));
     CHECK_SHAPE(lds <= kMaxStageLds, "activations need %d bytes of LDS (max %d)", lds, kMaxStageLds);
     return hip_status(launch_gemv_q4k_grouped(w_all, expert_bytes, n_experts, ids, n_sel, xq, xq_stride_bytes,
-                                              y, combine, y_out, nullptr, 1, m, k, stream),
+                                              y, combine, y_out, nullptr, 1, m, k, nullptr, stream),
                       "grouped GEMV launch");
 }
 
@@ -425,8 +425,8 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     CHECK_ARG(d->w_gu_all && d->w_dn_all && d->ids_table && d->logits_table && d->x_table && d->y_table,
               "null pointer in the descriptor");
     CHECK_ARG(aligned(d->w_gu_all, 16) && aligned(d->w_dn_all, 16) && aligned(d->ids_table, 4) &&
-                  aligned(d->logits_table, 4) && aligned(d->x_table, 4) && aligned(d->y_table, 4),
-              "misaligned pointer");
+                  aligned(d->logits_table, 4) && aligned(d->x_table, 16) && aligned(d->y_table, 4),
+              "misaligned pointer (x_table must be 16-byte aligned)");
     if (capturing(stream)) return fail(MQ_ERR_CAPTURE, "mq_moe_create cannot run inside a stream capture");
 
     mq_chain* c = new mq_chain();
@@ -437,26 +437,23 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     if (rc == MQ_OK) c->cur = (int64_t*)chain_alloc(c, sizeof(int64_t), &rc);
     int32_t* ids = rc == MQ_OK ? (int32_t*)chain_alloc(c, 64 * sizeof(int32_t), &rc) : nullptr;
     float* comb = rc == MQ_OK ? (float*)chain_alloc(c, 64 * sizeof(float), &rc) : nullptr;
-    uint8_t* xq = rc == MQ_OK ? (uint8_t*)chain_alloc(c, H / 32 * kQ8Bytes, &rc) : nullptr;
-    float* gu = rc == MQ_OK ? (float*)chain_alloc(c, (size_t)S * 2 * I * sizeof(float), &rc) : nullptr;
     const int64_t gstride = KP / 32 * kQ8Bytes;
     uint8_t* gq = rc == MQ_OK ? (uint8_t*)chain_alloc(c, (size_t)S * gstride, &rc) : nullptr;
     if (rc != MQ_OK) { chain_free(c); return rc; }
 
+    // Two kernels per token: gate/up (reads the counter, quantizes x_t in
+    // its prologue, writes the routing, the combine weights and
+    // Q8(SwiGLU)), then down with the weighted combine, which advances the
+    // counter.
     int64_t *step = c->step, *cur = c->cur;
     const mq_moe_desc dd = *d;
     c->ops.push_back([=](hipStream_t s) {
-        return launch_moe_prep(step, cur, dd.n_tokens, dd.ids_table, dd.logits_table, dd.x_table, S, H, ids,
-                               comb, xq, s);
+        return launch_moe_gate_up(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, I, H, step, dd.n_tokens,
+                                  dd.ids_table, dd.logits_table, dd.x_table, S, KP, cur, ids, comb, gq, nullptr, s);
     });
-    c->ops.push_back([=](hipStream_t s) {
-        return launch_gemv_q4k_grouped(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, ids, S, xq, 0, gu,
-                                       nullptr, nullptr, nullptr, 1, 2 * I, H, s);
-    });
-    c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, gq, I, S, KP, s); });
     c->ops.push_back([=](hipStream_t s) {
         return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,
-                                       nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, s);
+                                       nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, step, s);
     });
     rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
     if (rc != MQ_OK) { chain_free(c); return rc; }

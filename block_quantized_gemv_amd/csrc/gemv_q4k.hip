@@ -317,8 +317,9 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
     const int32_t* __restrict__ ids, int n_sel, const uint8_t* __restrict__ xq, int64_t xq_stride,
     float* __restrict__ y, const float* __restrict__ combine, float* __restrict__ y_out,
     const int64_t* __restrict__ out_row, int64_t out_rows, int M, int nsb, int log2s, int passes,
-    int n_tiles) {
+    int n_tiles, int64_t* __restrict__ inc_step) {
     extern __shared__ __align__(16) uint8_t lds[];
+    if (inc_step && blockIdx.x == 0 && threadIdx.x == 0) *inc_step += 1;
     const Lanes ln(log2s);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
@@ -478,6 +479,102 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
         const int i = ln.lane;
         const float a = i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
         quantize_lane(a, g_q8 + (int64_t)u * kQ8Bytes, i & 31, i < 32);
+    }
+}
+
+// --------------------------------------------------------------------------
+// Routed-expert gate/up with the SwiGLU epilogue, for the token t = *step mod
+// n_tokens.  Workgroup (block b = blockIdx.x, slot s = blockIdx.y) computes
+// gate rows 32b..32b+31 and up rows inter+32b..+31 of expert
+// ids_table[t][s] against Q8(x_table[t]), quantized in its prologue, and
+// writes block b of slot s of g = Q8(silu(gate)*up) (slot stride k_pad/32
+// blocks); blocks at or past inter/32 (the padding up to k_pad) and slots
+// whose expert id is out of range get zero blocks.  Workgroup (0, 0) also
+// writes cur = t, the token's ids and combine = softmax(logits_table[t])
+// (f64, slot order, rounded to f32).  Rows and arithmetic as in
+// k_gemv_q4k_swiglu<true> (8 waves, 16-lane slots).
+__global__ __launch_bounds__(512) void k_moe_gate_up(
+    const uint8_t* __restrict__ w_all, int64_t expert_bytes, int n_experts, int inter, int nsb,
+    const int64_t* __restrict__ step, int n_tokens, const int32_t* __restrict__ ids_table,
+    const float* __restrict__ logits_table, const float* __restrict__ x_table, int n_sel, int64_t k_pad,
+    int64_t* __restrict__ cur, int32_t* __restrict__ ids_out, float* __restrict__ combine_out,
+    uint8_t* __restrict__ g_q8, float* __restrict__ gu_out) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ float gu_s[64];
+    const Lanes ln(4);
+    const int nb = nsb * 8;
+    const int passes = (nsb + 3) / 4;
+    const int q = threadIdx.x >> 6;
+    const int b = blockIdx.x, slot = blockIdx.y;
+    const int64_t t = (int64_t)((uint64_t)*step % (uint64_t)n_tokens);
+    const int e = ids_table[t * n_sel + slot];
+    const bool e_ok = e >= 0 && e < n_experts;
+    const bool work = e_ok && b < inter / 32;
+    const int n_items = work ? 2 * passes : 0;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+    const uint8_t* w = w_all + (e_ok ? (int64_t)e * expert_bytes : 0);
+    const int local = 4 * q + ln.row_local;     // row within the gate or up half of the block
+    auto row_of = [&](int st) { return st * inter + 32 * b + local; };
+
+    // Items past the last re-read the last item's lines and are not computed.
+    struct Item {
+        SBLoad L;
+        bool valid;
+        int st, pass;
+    };
+    auto fetch = [&](int i, Item& it) {
+        const bool past = i >= n_items;
+        const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
+        it.st = ii / passes;
+        it.pass = ii % passes;
+        const int sb = it.pass * ln.gpp + ln.g;
+        const bool inb = n_items > 0 && sb < nsb;
+        it.valid = inb && !past;
+        load_sb(inb ? w + (int64_t)row_of(it.st) * row_bytes + sb * kQ4KBytes : w_all, 32 * ln.j, it.L);
+    };
+
+    const float* x = x_table + t * (int64_t)(nsb * 256);
+    float4 xr[kNormRegChunks];
+    if (work) norm_load(x, nsb * 256, xr);
+    Item A, B;
+    fetch(0, A);
+    fetch(1, B);
+    if (work) stage_scaled_q8(x, nsb * 256, xr, 1.0, false, lds, nullptr);
+    if (b == 0 && slot == 0 && q == 0) {
+        // combine = softmax of the router logits, in slot order like a
+        // sequential loop: lane i holds logit i, every lane adds the
+        // exponentials in slot order
+        const int i = ln.lane;
+        const double l = i < n_sel ? (double)logits_table[t * n_sel + i] : -INFINITY;
+        double mx = l;
+        for (int j = 0; j < n_sel; ++j) mx = fmax(mx, __shfl(l, j));
+        const double ex = exp(l - mx);
+        double sum = 0.0;
+        for (int j = 0; j < n_sel; ++j) sum += __shfl(ex, j);
+        if (i < n_sel) {
+            combine_out[i] = (float)(ex / sum);
+            ids_out[i] = ids_table[t * n_sel + i];
+        }
+        if (i == 0) *cur = t;
+    }
+    __syncthreads();
+
+    double acc[1] = {0.0};
+    stream_items<true>(n_items, A, B, fetch, [&](const Item& it) {
+        sb_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
+        if (it.pass != passes - 1) return;
+        const float v = (float)group_sum_f64(acc[0], 4);
+        acc[0] = 0.0;
+        if ((ln.lane & 15) == 0) {
+            gu_s[it.st * 32 + local] = v;
+            if (gu_out) gu_out[(int64_t)slot * 2 * inter + row_of(it.st)] = v;
+        }
+    });
+    __syncthreads();
+    if (q == 0) {
+        const int i = ln.lane;
+        const float a = work && i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
+        quantize_lane(a, g_q8 + ((int64_t)slot * (k_pad / 32) + b) * kQ8Bytes, i & 31, i < 32);
     }
 }
 
@@ -716,7 +813,7 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
                                    const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
                                    float* y, const float* combine, float* y_out,
                                    const int64_t* out_row, int64_t out_rows, int64_t m, int64_t k,
-                                   hipStream_t stream) {
+                                   int64_t* inc_step, hipStream_t stream) {
     const int nsb = (int)(k / 256);
     const Q4KPlan p = plan_q4k_mult(m, nsb, combine ? 1 : n_sel);
     const int lds = (xq_stride ? n_sel : 1) * stage_bytes(nsb * 8);
@@ -726,14 +823,27 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
         MQ_LAUNCH((k_gemv_q4k_grouped<true>), dim3(balanced_grid(units, fn, lds)), dim3(256), lds, stream,
                            (const uint8_t*)w_all, expert_bytes, n_experts, ids, n_sel,
                            (const uint8_t*)xq, xq_stride, y, combine, y_out, out_row, out_rows, (int)m,
-                           nsb, p.log2s, p.passes, p.n_tiles);
+                           nsb, p.log2s, p.passes, p.n_tiles, inc_step);
     } else {
         const void* fn = (const void*)k_gemv_q4k_grouped<false>;
         MQ_LAUNCH((k_gemv_q4k_grouped<false>), dim3(balanced_grid(units, fn, lds)), dim3(256), lds, stream,
                            (const uint8_t*)w_all, expert_bytes, n_experts, ids, n_sel,
                            (const uint8_t*)xq, xq_stride, y, combine, y_out, out_row, out_rows, (int)m,
-                           nsb, p.log2s, p.passes, p.n_tiles);
+                           nsb, p.log2s, p.passes, p.n_tiles, inc_step);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_experts, int64_t inter, int64_t k,
+                              const int64_t* step, int n_tokens, const int32_t* ids_table,
+                              const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
+                              int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
+                              hipStream_t stream) {
+    const int nsb = (int)(k / 256);
+    const int lds = stage_bytes(nsb * 8);
+    MQ_LAUNCH(k_moe_gate_up, dim3((unsigned)(k_pad / 32), (unsigned)n_sel), dim3(512), lds, stream,
+              (const uint8_t*)w_all, expert_bytes, n_experts, (int)inter, nsb, step, n_tokens, ids_table,
+              logits_table, x_table, n_sel, k_pad, cur, ids_out, combine_out, (uint8_t*)g_q8, gu_out);
     return hipGetLastError();
 }
 

@@ -1,6 +1,5 @@
 // Standalone glue kernels: q8_0 quantization, RMSNorm and SwiGLU fused with
-// quantization of their outputs, the routed-expert token set-up, and a
-// counter setter.  One value per lane; the arithmetic lives in glue.hpp and
+// quantization of their outputs, and a counter setter.  One value per lane; the arithmetic lives in glue.hpp and
 // is shared with the fused tails of the GEMV kernels, so both produce the
 // same bytes.
 #include "common.hpp"
@@ -48,41 +47,6 @@ __global__ __launch_bounds__(256) void k_swiglu_quantize(const float* __restrict
     quantize_lane(v, xq + (idx >> 5) * kQ8Bytes, (int)(idx & 31), in);
 }
 
-// Routed-expert token set-up (one workgroup): token t = step % n_tokens, the
-// counter advanced; ids copied; combine = softmax of the router logits (f64,
-// slot order); x_t quantized.
-__global__ __launch_bounds__(256) void k_moe_prep(int64_t* __restrict__ step, int64_t* __restrict__ cur,
-                                                 int n_tokens, const int32_t* __restrict__ ids_table,
-                                                 const float* __restrict__ logits_table,
-                                                 const float* __restrict__ x_table, int n_sel, int hidden,
-                                                 int32_t* __restrict__ ids_out,
-                                                 float* __restrict__ combine_out,
-                                                 uint8_t* __restrict__ xq_out) {
-    __shared__ int64_t t_sh;
-    if (threadIdx.x == 0) {
-        const int64_t s = *step;
-        const int64_t t = (int64_t)((uint64_t)s % (uint64_t)n_tokens);
-        t_sh = t;
-        *cur = t;
-        *step = s + 1;
-        const float* lg = logits_table + t * n_sel;
-        double mx = -INFINITY;
-        for (int i = 0; i < n_sel; ++i) mx = fmax(mx, (double)lg[i]);
-        double sum = 0.0;
-        for (int i = 0; i < n_sel; ++i) sum += exp((double)lg[i] - mx);
-        for (int i = 0; i < n_sel; ++i) combine_out[i] = (float)(exp((double)lg[i] - mx) / sum);
-    }
-    __syncthreads();
-    const int64_t t = t_sh;
-    if (threadIdx.x < n_sel) ids_out[threadIdx.x] = ids_table[t * n_sel + threadIdx.x];
-    const float* x = x_table + t * hidden;
-    for (int base = 0; base < hidden; base += blockDim.x) {
-        const int idx = base + threadIdx.x;
-        const bool in = idx < hidden;
-        quantize_lane(in ? x[idx] : 0.0f, xq_out + (int64_t)(idx >> 5) * kQ8Bytes, idx & 31, in);
-    }
-}
-
 __global__ void k_set_i64(int64_t* p, int64_t v) { *p = v; }
 
 // ------------------------------------------------------------------ host ----
@@ -106,14 +70,6 @@ hipError_t launch_swiglu_quantize(const float* gu, void* xq, int64_t inter, int 
     const int64_t n = k_pad * n_cols;
     hipLaunchKernelGGL(k_swiglu_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, gu,
                        (uint8_t*)xq, inter, n_cols, k_pad);
-    return hipGetLastError();
-}
-
-hipError_t launch_moe_prep(int64_t* step, int64_t* cur, int n_tokens, const int32_t* ids_table,
-                           const float* logits_table, const float* x_table, int n_sel, int64_t hidden,
-                           int32_t* ids_out, float* combine_out, void* xq_out, hipStream_t stream) {
-    hipLaunchKernelGGL(k_moe_prep, dim3(1), dim3(256), 0, stream, step, cur, n_tokens, ids_table,
-                       logits_table, x_table, n_sel, (int)hidden, ids_out, combine_out, (uint8_t*)xq_out);
     return hipGetLastError();
 }
 

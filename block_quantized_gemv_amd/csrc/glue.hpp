@@ -261,9 +261,9 @@ constexpr int kNormRegChunks = 2;
 // per-thread sums in the fixed order of block_sum_f64, and each value is
 // x/sqrt(mean + eps) in f64 rounded to f32; a q8_0 block is 8 consecutive
 // chunks, i.e. 8 aligned lanes, and its amax, f16 scale and codes follow
-// quantize_lane.  With `exact` every chunk takes the division path (a test
-// hook: the results are the same).  The caller synchronizes the workgroup
-// before reading lds.
+// quantize_lane (stage_scaled_q8).  With `exact` every chunk takes the
+// division path (a test hook: the results are the same).  The caller
+// synchronizes the workgroup before reading lds.
 __device__ __forceinline__ void norm_load(const float* __restrict__ x, int k, float4 (&xr)[kNormRegChunks]) {
     const float4* x4 = (const float4*)x;
 #pragma unroll
@@ -273,36 +273,24 @@ __device__ __forceinline__ void norm_load(const float* __restrict__ x, int k, fl
     }
 }
 
-__device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, int k, float eps,
-                                                 const float4 (&xr)[kNormRegChunks], bool exact,
-                                                 uint8_t* __restrict__ lds, double* sh,
-                                                 uint8_t* __restrict__ q8_copy) {
+// Q8(x / denom) of k values (k % 32 == 0) into lds in the layout of
+// stage_q8: each value is x/denom in f64 rounded to f32 (x itself when
+// denom is 1), then quantized as described above; q8_copy, if set, also
+// receives the q8_0 vector.  xr: the thread's first chunks (norm_load).
+__device__ __forceinline__ void stage_scaled_q8(const float* __restrict__ x, int k,
+                                                const float4 (&xr)[kNormRegChunks], double denom, bool exact,
+                                                uint8_t* __restrict__ lds, uint8_t* __restrict__ q8_copy) {
 #pragma clang fp contract(off)
     const int nch = k >> 2;
     const int T = blockDim.x;
     const float4* x4 = (const float4*)x;
     const int rounds = (nch + T - 1) / T;
-    auto chunk = [&](int r) {
-        if (r < kNormRegChunks) return xr[r];
-        const int c = r * T + (int)threadIdx.x;
-        return c < nch ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    };
-    double ss = 0.0;
-    for (int r = 0; r < rounds; ++r) {
-        const float4 v = chunk(r);      // zero past the end
-        ss += (double)v.x * (double)v.x;
-        ss += (double)v.y * (double)v.y;
-        ss += (double)v.z * (double)v.z;
-        ss += (double)v.w * (double)v.w;
-    }
-    ss = block_sum_f64(ss, sh);
-    const double denom = sqrt(ss / (double)k + (double)eps);
     const double rinv = 1.0 / denom;
     const float tiny = (float)(0x1p-124 * denom);
     for (int r = 0; r < rounds; ++r) {
         const int c = r * T + (int)threadIdx.x;
         const bool in = c < nch;      // whole 8-lane groups are in or out
-        const float4 v = chunk(r);
+        const float4 v = r < kNormRegChunks ? xr[r] : (in ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
         bool bad = exact;
         ChunkQ8 o = chunk_fast(v, rinv, tiny, bad);
         if (__builtin_amdgcn_ballot_w64(bad) != 0) o = chunk_exact(v, denom);   // wave-uniform
@@ -324,6 +312,28 @@ __device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, in
             }
         }
     }
+}
+
+__device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, int k, float eps,
+                                                 const float4 (&xr)[kNormRegChunks], bool exact,
+                                                 uint8_t* __restrict__ lds, double* sh,
+                                                 uint8_t* __restrict__ q8_copy) {
+#pragma clang fp contract(off)
+    const int nch = k >> 2;
+    const int T = blockDim.x;
+    const float4* x4 = (const float4*)x;
+    const int rounds = (nch + T - 1) / T;
+    double ss = 0.0;
+    for (int r = 0; r < rounds; ++r) {
+        const int c = r * T + (int)threadIdx.x;
+        const float4 v = r < kNormRegChunks ? xr[r] : (c < nch ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+        ss += (double)v.x * (double)v.x;
+        ss += (double)v.y * (double)v.y;
+        ss += (double)v.z * (double)v.z;
+        ss += (double)v.w * (double)v.w;
+    }
+    ss = block_sum_f64(ss, sh);
+    stage_scaled_q8(x, k, xr, sqrt(ss / (double)k + (double)eps), exact, lds, q8_copy);
 }
 
 // The input row of a GEMV fed by a NormIn.

@@ -59,7 +59,16 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
                                    const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
                                    float* y, const float* combine, float* y_out,
                                    const int64_t* out_row, int64_t out_rows, int64_t m, int64_t k,
-                                   hipStream_t stream);
+                                   int64_t* inc_step, hipStream_t stream);
+// One routed-expert token's gate/up GEMVs with the SwiGLU -> q8_0 epilogue
+// (k_moe_gate_up): token t = *step mod n_tokens; writes cur = t, ids_out,
+// combine_out (softmax of the router logits) and g_q8 (n_sel columns of
+// k_pad/32 blocks, zero past inter); gu_out, if set, the f32 gate/up rows.
+hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_experts, int64_t inter, int64_t k,
+                              const int64_t* step, int n_tokens, const int32_t* ids_table,
+                              const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
+                              int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
+                              hipStream_t stream);
 hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* dump_isum, int64_t m,
                             int64_t k, hipStream_t stream);
 hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
@@ -73,12 +82,6 @@ hipError_t launch_rmsnorm_quantize(const float* x, void* xq, int64_t k, float ep
                                    int n_inputs, int64_t* inc_step, hipStream_t stream);
 hipError_t launch_swiglu_quantize(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
                                   hipStream_t stream);
-// Routed-expert token set-up: token t = step % n_tokens (step advanced by one);
-// writes *cur = t, ids_out[n_sel], combine_out[n_sel] = softmax(logits_table[t]),
-// xq_out = Q8(x_table[t]).
-hipError_t launch_moe_prep(int64_t* step, int64_t* cur, int n_tokens, const int32_t* ids_table,
-                           const float* logits_table, const float* x_table, int n_sel, int64_t hidden,
-                           int32_t* ids_out, float* combine_out, void* xq_out, hipStream_t stream);
 hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t stream);
 
 }  // namespace mq

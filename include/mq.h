@@ -236,6 +236,8 @@ int mq_chain_destroy(mq_chain* c);
  * dn_expert_bytes apart.  ids/logits/x tables are device arrays of
  * n_tokens rows; y_table: f32 [n_tokens][hidden], row t written by token t.
  * Routing ids are bounds-checked on the device (see mq_gemv_q4k_grouped).
+ * A token is two kernels: gate/up with x_t quantized in its prologue and
+ * the SwiGLU -> q8_0 glue in its epilogue, then down with the combine.
  */
 typedef struct {
     int n_experts, n_sel;              /* 1 <= n_sel <= 16 */
@@ -246,7 +248,7 @@ typedef struct {
     int64_t dn_expert_bytes;
     const int32_t* ids_table;          /* device [n_tokens][n_sel] */
     const float* logits_table;         /* device [n_tokens][n_sel] */
-    const float* x_table;              /* device [n_tokens][hidden] */
+    const float* x_table;              /* device [n_tokens][hidden], 16-byte aligned */
     float* y_table;                    /* device [n_tokens][hidden] */
     int n_tokens;
     unsigned flags;                    /* MQ_EAGER_ONLY */
