@@ -483,6 +483,77 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
 }
 
 // --------------------------------------------------------------------------
+// Grouped GEMV with the weighted combine, slots in parallel: wave s of a
+// workgroup computes slot s (expert ids[s], activation column s) for the
+// workgroup's tiles [tpw*g, tpw*g + tpw) over all passes, keeping each row's
+// result in LDS; after a barrier the workgroup forms y_out[r] =
+// sum_s combine[s]*y_s[r] in f64 in slot order (the order of
+// k_gemv_q4k_grouped<true>, so the results are the same).  n_sel waves.
+__global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
+    const uint8_t* __restrict__ w_all, int64_t expert_bytes, int n_experts,
+    const int32_t* __restrict__ ids, int n_sel, const uint8_t* __restrict__ xq, int64_t xq_stride,
+    const float* __restrict__ combine, float* __restrict__ y_out, const int64_t* __restrict__ out_row,
+    int64_t out_rows, int M, int nsb, int log2s, int passes, int n_tiles, int tpw,
+    int64_t* __restrict__ inc_step) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ float res[16 * 64];          // [slot][tile in the workgroup][row in the tile]
+    if (inc_step && blockIdx.x == 0 && threadIdx.x == 0) *inc_step += 1;
+    const Lanes ln(log2s);
+    const int nb = nsb * 8;
+    const int col_bytes = stage_bytes(nb);
+    const int slot = threadIdx.x >> 6;
+    const int t0 = (int)blockIdx.x * tpw;
+    const int n_items = tpw * passes;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+    const int e = ids[slot];
+    const bool slot_ok = e >= 0 && e < n_experts;
+
+    // Items past the last re-read the last item's lines and are not computed.
+    struct Item {
+        SBLoad L;
+        bool valid;
+        int k, row, pass;
+    };
+    auto fetch = [&](int i, Item& it) {
+        const bool past = i >= n_items;
+        const int ii = past ? n_items - 1 : i;
+        it.k = ii / passes;
+        it.pass = ii % passes;
+        it.row = (t0 + it.k) * ln.R + ln.row_local;
+        const int sb = it.pass * ln.gpp + ln.g;
+        const bool inb = slot_ok && it.row < M && sb < nsb;
+        it.valid = inb && !past;
+        load_sb(inb ? w_all + e * expert_bytes + (int64_t)it.row * row_bytes + sb * kQ4KBytes : w_all,
+                32 * ln.j, it.L);
+    };
+
+    Item A, B;
+    fetch(0, A);
+    for (int c = 0; c < n_sel; ++c)
+        stage_q8(xq + c * xq_stride, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x, nullptr);
+    __syncthreads();
+
+    double acc[1] = {0.0};
+    const uint8_t* xs = lds + slot * col_bytes;
+    stream_items<false>(n_items, A, B, fetch, [&](const Item& it) {
+        sb_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, xs, col_bytes, acc, nullptr, 0);
+        if (it.pass != passes - 1) return;
+        const double v = group_sum_f64(acc[0], ln.log2s);
+        acc[0] = 0.0;
+        if ((ln.lane & (ln.S - 1)) == 0) res[(slot * tpw + it.k) * ln.R + ln.row_local] = slot_ok ? (float)v : __builtin_nanf("");
+    });
+    __syncthreads();
+    float* yo = y_out + (out_row ? (int64_t)(*out_row % out_rows) * M : 0);
+    for (int i = threadIdx.x; i < tpw * ln.R; i += blockDim.x) {
+        const int row = t0 * ln.R + i;
+        if (row >= M) continue;
+        double comb = 0.0;
+        for (int s2 = 0; s2 < n_sel; ++s2) comb += (double)combine[s2] * (double)res[s2 * tpw * ln.R + i];
+        yo[row] = (float)comb;
+    }
+}
+
+// --------------------------------------------------------------------------
 // Routed-expert gate/up with the SwiGLU epilogue, for the token t = *step mod
 // n_tokens.  Workgroup (block b = blockIdx.x, slot s = blockIdx.y) computes
 // gate rows 32b..32b+31 and up rows inter+32b..+31 of expert
@@ -818,7 +889,17 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
     const Q4KPlan p = plan_q4k_mult(m, nsb, combine ? 1 : n_sel);
     const int lds = (xq_stride ? n_sel : 1) * stage_bytes(nsb * 8);
     const int64_t units = combine ? p.n_tiles : (int64_t)p.n_tiles * n_sel;
-    if (combine) {
+    if (combine && !y && xq_stride) {
+        // slots in parallel: about two workgroups per CU, tiles split evenly
+        const int64_t want = 2 * (int64_t)device_cu_count();
+        int tpw = (int)((p.n_tiles + want - 1) / want);
+        if (tpw * p.rows_per_tile > 64) tpw = 64 / p.rows_per_tile;
+        if (tpw < 1) tpw = 1;
+        const int grid = (p.n_tiles + tpw - 1) / tpw;
+        MQ_LAUNCH(k_gemv_q4k_grouped_combine, dim3(grid), dim3(64 * n_sel), lds, stream, (const uint8_t*)w_all,
+                  expert_bytes, n_experts, ids, n_sel, (const uint8_t*)xq, xq_stride, combine, y_out, out_row,
+                  out_rows, (int)m, nsb, p.log2s, p.passes, p.n_tiles, tpw, inc_step);
+    } else if (combine) {
         const void* fn = (const void*)k_gemv_q4k_grouped<true>;
         MQ_LAUNCH((k_gemv_q4k_grouped<true>), dim3(balanced_grid(units, fn, lds)), dim3(256), lds, stream,
                            (const uint8_t*)w_all, expert_bytes, n_experts, ids, n_sel,
