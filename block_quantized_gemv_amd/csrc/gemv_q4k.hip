@@ -573,7 +573,6 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
     const Lanes ln(4);
-    const int nb = nsb * 8;
     const int passes = (nsb + 3) / 4;
     const int q = threadIdx.x >> 6;
     const int b = blockIdx.x, slot = blockIdx.y;
@@ -610,7 +609,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     Item A, B;
     fetch(0, A);
     fetch(1, B);
-    if (work) stage_scaled_q8(x, nsb * 256, xr, 1.0, false, lds, nullptr);
+    if (work) stage_scaled_q8(x, nsb * 256, xr, 1.0f, false, lds, nullptr);
     if (b == 0 && slot == 0 && q == 0) {
         // combine = softmax of the router logits, in slot order like a
         // sequential loop: lane i holds logit i, every lane adds the

@@ -27,10 +27,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quantize(const float* __restric
                                                          uint8_t* __restrict__ xq, int k, float eps,
                                                          const int64_t* __restrict__ sel_step, int n_inputs,
                                                          int64_t* __restrict__ inc_step) {
-    __shared__ double sh[4];
+    __shared__ double sh[16];
     if (sel_step) x += (int64_t)((uint64_t)*sel_step % (uint64_t)n_inputs) * k;
-    const double denom = rms_denom(x, k, eps, sh);
-    rmsnorm_quantize_range(x, denom, k, xq, blockIdx.x * blockDim.x, blockDim.x);
+    const float scale = rms_scale(x, k, eps, sh);
+    rmsnorm_quantize_range(x, scale, k, xq, blockIdx.x * blockDim.x, blockDim.x);
     if (inc_step && blockIdx.x == 0 && threadIdx.x == 0) *inc_step += 1;
 }
 

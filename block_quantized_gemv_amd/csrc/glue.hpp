@@ -5,8 +5,9 @@
 // Quantization decides integers from floats, so it runs in f32 with only
 // exactly specified operations: a max over magnitudes (order-independent,
 // 'Part 4 · Lecture 08 — Graph-Resident Decode', §8), an IEEE f32 divide,
-// f16 round-to-nearest-even of the scale and roundf.  The glue itself is
-// computed in f64 and rounded to f32 once, then quantized.
+// f16 round-to-nearest-even of the scale and roundf.  The SwiGLU stand-in
+// is computed in f64 and rounded to f32 once; RMSNorm forms its scale in
+// f64, rounds it to f32 once and multiplies each value by it in f32.
 #pragma once
 
 #include <math.h>
@@ -50,23 +51,24 @@ __device__ __forceinline__ void quantize_lane(float v, uint8_t* __restrict__ out
     }
 }
 
-// Sum over the workgroup in a fixed order: DPP/swizzle inside each wave, then
-// the wave sums in wave order.  Every workgroup of the same size that sums
-// the same per-thread values gets the same bits.
+// Sum over the workgroup (at most 16 waves) in a fixed order: a DPP/swizzle
+// tree inside each wave, then a 16-lane tree over the wave sums (zeros past
+// the last wave), which every lane forms from LDS after one barrier.  Every
+// workgroup of the same size that sums the same per-thread values gets the
+// same bits.  sh (16 doubles) must not be written again by the caller.
 __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
     v = wave_sum_f64(v);
     const int nw = blockDim.x >> 6;
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
-    double t = 0.0;
-    for (int i = 0; i < nw; ++i) t += sh[i];
-    __syncthreads();
-    return t;
+    const int l = threadIdx.x & 15;
+    return group_sum_f64(l < nw ? sh[l] : 0.0, 4);
 }
 
-// sqrt(mean(x^2) + eps) of k values in f64, summed by the workgroup in the
+// The RMSNorm scale 1/sqrt(mean(x^2) + eps) of k values, formed in f64 and
+// rounded to f32 once; the squares are summed in f64 by the workgroup in the
 // order above (thread t takes elements t, t+B, t+2B, ...).
-__device__ __forceinline__ double rms_denom(const float* __restrict__ x, int k, float eps, double* sh) {
+__device__ __forceinline__ float rms_scale(const float* __restrict__ x, int k, float eps, double* sh) {
 #pragma clang fp contract(off)
     double ss = 0.0;
 #pragma unroll 16
@@ -75,18 +77,19 @@ __device__ __forceinline__ double rms_denom(const float* __restrict__ x, int k, 
         ss += v * v;
     }
     ss = block_sum_f64(ss, sh);
-    return sqrt(ss / (double)k + (double)eps);
+    return (float)(1.0 / sqrt(ss / (double)k + (double)eps));
 }
 
 // Outputs [first, first + count) of Q8(RMSNorm(x)) by one workgroup, one
-// value per lane per round (blockDim.x must be a multiple of 64).
-__device__ __forceinline__ void rmsnorm_quantize_range(const float* __restrict__ x, double denom, int k,
+// value per lane per round (blockDim.x must be a multiple of 64); each
+// normalized value is the f32 product x * scale.
+__device__ __forceinline__ void rmsnorm_quantize_range(const float* __restrict__ x, float scale, int k,
                                                        uint8_t* __restrict__ xq, int first, int count) {
 #pragma clang fp contract(off)
     for (int base = first; base < first + count; base += blockDim.x) {
         const int idx = base + threadIdx.x;
         const bool in = idx < first + count && idx < k;
-        const float v = in ? (float)((double)x[idx] / denom) : 0.0f;
+        const float v = in ? x[idx] * scale : 0.0f;
         quantize_lane(v, xq + (int64_t)(idx >> 5) * kQ8Bytes, idx & 31, in);
     }
 }
@@ -115,25 +118,24 @@ struct NormIn {
 
 // ------------------------------------------- RMSNorm -> q8_0 in a prologue ----
 //
-// Each value needs two correctly rounded divisions, x/denom in f64 and
-// n/d in f32, which as division sequences cost more than the GEMV's own
-// arithmetic.  They are formed as products with a reciprocal instead, and a
-// product is accepted when it provably gives the same result:
+// Each normalized value n = x * scale is one f32 multiply.  Its q8_0 code
+// needs the correctly rounded f32 quotient n/d, and the block scale amax/127
+// another; as division sequences they cost more than the GEMV's own
+// arithmetic, so both are formed as products with a reciprocal and a
+// product is accepted only when it provably gives the same result:
 //
-//   t = a * r in f64 with r = 1/b correctly rounded (or within one ulp) is
-//   within 4 f64 ulps of the correctly rounded f64 quotient q.
-//
-// * The f32 value RN_f32(q): read as integers, f64 patterns of one sign are
-//   ordered like their values, and rounding to f32 maps every pattern
-//   strictly between two consecutive f32 midpoints (patterns whose low 29
-//   bits are 2^28) to the same f32.  So RN_f32(t) == RN_f32(q) when t's low
-//   29 bits are more than 16 away from 2^28 and |t| is at least 2^-125
-//   (the f32 normal range, where those patterns are the midpoints).  RN_f32(q) is the reference's x/denom (an f64 division rounded
-//   to f32) and its amax/127 (an f32 division: f64 carries more than
-//   2*24+2 bits, so rounding the quotient to f64 first changes nothing).
+// * The scale RN_f32(amax/127) from t = amax * RN_f64(1/127), which is
+//   within 4 f64 ulps of the f64 quotient (f64 carries more than 2*24+2
+//   bits, so rounding the quotient to f64 before f32 changes nothing).
+//   Read as integers, f64 patterns of one sign are ordered like their
+//   values, and rounding to f32 maps every pattern strictly between two
+//   consecutive f32 midpoints (patterns whose low 29 bits are 2^28) to the
+//   same f32.  So RN_f32(t) is the quotient's when t's low 29 bits are more
+//   than 16 away from 2^28 and t is at least 2^-125 (the f32 normal range,
+//   where those patterns are the midpoints).
 // * A code roundf(RN_f32(n/d)) comes from the f32 product y = n * (1/d)
 //   (see code_checked): unless y lies within |y|*2^-21 of a half-integer,
-//   the code is y rounded half away from zero.
+//   the code is y rounded to the nearest integer.
 //
 // When any lane of a wave meets a doubtful case the wave redoes the whole
 // chunk with the divisions themselves.
@@ -148,15 +150,17 @@ __device__ __forceinline__ float f32_checked(double t, bool& bad) {
 
 // clamp(roundf(RN_f32(n/d)), -127, 127) from y = n * r in f32, r within an
 // f32 ulp of 1/d: y is within 1.6*2^-23 of n/d relative, and RN_f32 moves
-// the quotient by at most 2^-24 relative, so the code is y rounded half
-// away from zero unless y lies within |y|*2^-21 of a half-integer
-// (flagged).  y must be finite.
+// the quotient by at most 2^-24 relative, so both lie strictly on the same
+// side of every half-integer unless y lies within |y|*2^-21 of one
+// (flagged; exact half-integers are flagged too).  Off those, rounding to
+// nearest-even and half away from zero agree.  The test needs |y - rint(y)|
+// > 0.5 - |y|*2^-21; the subtraction is exact and the threshold's rounding
+// (at most 2^-26) is covered for |y| >= 1/4, below which no half-integer
+// is near.  y must be finite.
 __device__ __forceinline__ int code_checked(float y, bool& bad) {
-    const float a = fabsf(y);
-    const float fr = a - floorf(a);
-    bad |= fabsf(fr - 0.5f) < a * 0x1p-21f;
-    const int q = min((int)(a + 0.5f), 127);
-    return y < 0.0f ? -q : q;
+    const float r = rintf(y);
+    bad |= fabsf(y - r) > fmaf(fabsf(y), -0x1p-21f, 0.5f);
+    return (int)__builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
 }
 
 // 1/d in f32 to within an ulp: hardware estimate and a Newton step.
@@ -198,10 +202,9 @@ __device__ __forceinline__ uint32_t pack4(const int (&q)[4]) {
 }
 
 // The reference arithmetic: divisions as written.
-__device__ __forceinline__ ChunkQ8 chunk_exact(const float4& v, double denom) {
+__device__ __forceinline__ ChunkQ8 chunk_exact(const float4& v, float scale) {
 #pragma clang fp contract(off)
-    const float n[4] = {(float)((double)v.x / denom), (float)((double)v.y / denom),
-                        (float)((double)v.z / denom), (float)((double)v.w / denom)};
+    const float n[4] = {v.x * scale, v.y * scale, v.z * scale, v.w * scale};
     const float amax = block8_max(fmaxf(fmaxf(fabsf(n[0]), fabsf(n[1])), fmaxf(fabsf(n[2]), fabsf(n[3]))));
     const float d32 = amax / 127.0f;
     ChunkQ8 o;
@@ -216,14 +219,10 @@ __device__ __forceinline__ ChunkQ8 chunk_exact(const float4& v, double denom) {
 }
 
 // The same values through reciprocal products; `bad` is set where they
-// might differ (then chunk_exact is used).  tiny = 2^-124 * denom: an |x|
-// below it could give an f32-subnormal x/denom, which the midpoint test
-// does not cover (zeros are flagged too; they are merely slower).
-__device__ __forceinline__ ChunkQ8 chunk_fast(const float4& v, double rinv, float tiny, bool& bad) {
+// might differ (then chunk_exact is used).
+__device__ __forceinline__ ChunkQ8 chunk_fast(const float4& v, float scale, bool& bad) {
 #pragma clang fp contract(off)
-    bad |= fminf(fminf(fabsf(v.x), fabsf(v.y)), fminf(fabsf(v.z), fabsf(v.w))) < tiny;
-    const float n[4] = {f32_checked((double)v.x * rinv, bad), f32_checked((double)v.y * rinv, bad),
-                        f32_checked((double)v.z * rinv, bad), f32_checked((double)v.w * rinv, bad)};
+    const float n[4] = {v.x * scale, v.y * scale, v.z * scale, v.w * scale};
     const float amax = block8_max(fmaxf(fmaxf(fabsf(n[0]), fabsf(n[1])), fmaxf(fabsf(n[2]), fabsf(n[3]))));
     const double d64 = (double)amax * (1.0 / 127.0);
     bad |= d64 != 0.0 && d64 < 0x1p-125;
@@ -235,18 +234,13 @@ __device__ __forceinline__ ChunkQ8 chunk_fast(const float4& v, double rinv, floa
     ChunkQ8 o;
     o.dbits = f32_to_f16(d32);
     const float d = f16_to_f32(o.dbits);
-    const bool dz = d == 0.0f;
-    const float rd = recip_f32(dz ? 1.0f : d);
+    // d == 0 only when the block is all zeros: r = 0 gives codes 0.
+    const float rd = d == 0.0f ? 0.0f : recip_f32(d);
     int q[4];
-    bool bq = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = code_checked(n[i] * rd, bq);
-        q[i] = dz ? 0 : c;
-    }
-    bad |= bq && !dz;
+    for (int i = 0; i < 4; ++i) q[i] = code_checked(n[i] * rd, bad);
     o.packed = pack4(q);
-    o.ysum = block8_sum(q[0] + q[1] + q[2] + q[3]);
+    o.ysum = block8_sum(dot4(o.packed, 0x01010101u, 0));
     return o;
 }
 
@@ -273,27 +267,25 @@ __device__ __forceinline__ void norm_load(const float* __restrict__ x, int k, fl
     }
 }
 
-// Q8(x / denom) of k values (k % 32 == 0) into lds in the layout of
-// stage_q8: each value is x/denom in f64 rounded to f32 (x itself when
-// denom is 1), then quantized as described above; q8_copy, if set, also
+// Q8(x * scale) of k values (k % 32 == 0) into lds in the layout of
+// stage_q8: each value is the f32 product x * scale (x itself when scale
+// is 1), then quantized as described above; q8_copy, if set, also
 // receives the q8_0 vector.  xr: the thread's first chunks (norm_load).
 __device__ __forceinline__ void stage_scaled_q8(const float* __restrict__ x, int k,
-                                                const float4 (&xr)[kNormRegChunks], double denom, bool exact,
+                                                const float4 (&xr)[kNormRegChunks], float scale, bool exact,
                                                 uint8_t* __restrict__ lds, uint8_t* __restrict__ q8_copy) {
 #pragma clang fp contract(off)
     const int nch = k >> 2;
     const int T = blockDim.x;
     const float4* x4 = (const float4*)x;
     const int rounds = (nch + T - 1) / T;
-    const double rinv = 1.0 / denom;
-    const float tiny = (float)(0x1p-124 * denom);
     for (int r = 0; r < rounds; ++r) {
         const int c = r * T + (int)threadIdx.x;
         const bool in = c < nch;      // whole 8-lane groups are in or out
         const float4 v = r < kNormRegChunks ? xr[r] : (in ? x4[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
         bool bad = exact;
-        ChunkQ8 o = chunk_fast(v, rinv, tiny, bad);
-        if (__builtin_amdgcn_ballot_w64(bad) != 0) o = chunk_exact(v, denom);   // wave-uniform
+        ChunkQ8 o = chunk_fast(v, scale, bad);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) o = chunk_exact(v, scale);   // wave-uniform
         if (in) {
             const int b = c >> 3, cb = c & 7;
             const int P = b >> 1, half = b & 1, L = P & 63;
@@ -333,7 +325,7 @@ __device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, in
         ss += (double)v.w * (double)v.w;
     }
     ss = block_sum_f64(ss, sh);
-    stage_scaled_q8(x, k, xr, sqrt(ss / (double)k + (double)eps), exact, lds, q8_copy);
+    stage_scaled_q8(x, k, xr, (float)(1.0 / sqrt(ss / (double)k + (double)eps)), exact, lds, q8_copy);
 }
 
 // The input row of a GEMV fed by a NormIn.

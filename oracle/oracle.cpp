@@ -236,8 +236,8 @@ void oref_isums_q8_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
 void oref_rmsnorm(const float* x, int64_t n, float eps, float* y) {
     double ss = 0.0;
     for (int64_t i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
-    const double denom = sqrt(ss / (double)n + (double)eps);
-    for (int64_t i = 0; i < n; ++i) y[i] = (float)((double)x[i] / denom);
+    const float scale = (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+    for (int64_t i = 0; i < n; ++i) y[i] = x[i] * scale;
 }
 
 void oref_swiglu(const float* gu, int64_t inter, float* y) {

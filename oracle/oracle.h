@@ -78,9 +78,12 @@ void oref_isums_q4k(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
 void oref_isums_q8_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
                      int32_t* isum);
 
-/* --- elementwise stand-ins between GEMVs (f64, rounded to f32) ------------ */
-/* y_i = x_i / sqrt(mean(x^2) + eps), unit gain. */
+/* --- elementwise stand-ins between GEMVs ------------------------------------ */
+/* RMSNorm with unit gain: scale = 1/sqrt(mean(x^2) + eps) formed in f64 (sum
+ * of squares in index order) and rounded to f32 once; y_i = x_i * scale, one
+ * f32 multiply. */
 void oref_rmsnorm(const float* x, int64_t n, float eps, float* y);
+/* (f64, rounded to f32 once) */
 /* gu = [gate(inter) | up(inter)];  y_i = silu(gate_i) * up_i, silu(g) = g/(1+e^-g). */
 void oref_swiglu(const float* gu, int64_t inter, float* y);
 /* p_i = exp(l_i - max l) / sum_j exp(l_j - max l). */

@@ -270,10 +270,13 @@ def pin_q8_gemv(o):
 # ---------------------------------------------------------------- glue ----
 
 def pin_rmsnorm(o):
-    for c, n in ((3.0, 64), (-0.5, 7), (1e-3, 128)):
+    # constant vector: mean(x^2) = c^2, scale = f32(1/sqrt(c^2 + eps)), y = c * scale in f32
+    # (n chosen so that the f64 sum of the n equal squares is exact)
+    for c, n in ((3.0, 64), (-0.5, 7), (1e-3, 16)):
         y = o.rmsnorm(np.full(n, c, np.float32), 1e-6)
-        cf = float(np.float32(c))
-        assert np.all(y == np.float32(cf / math.sqrt(cf * cf + float(np.float32(1e-6))))), "constant vector"
+        cf = np.float32(c)
+        scale = np.float32(1.0 / math.sqrt(float(cf) * float(cf) + float(np.float32(1e-6))))
+        assert np.all(y == cf * scale), "constant vector"
     n = 256
     e = np.zeros(n, np.float32)
     e[17] = 1.0
