@@ -13,7 +13,11 @@ in HBM.  Prints one JSON line (rank 0):
                duration, each launch timed by its own dispatch events on the
                launching stream (eager steps, the same kernels and arguments
                the graph replays), against 8 TB/s; `traffic` is the HBM bytes
-               per launch the committed rocprofv3 counter record measured
+               per launch the committed rocprofv3 counter record measured;
+               also as a fraction of the streaming-read probe, and the
+               byte-weighted aggregate of the four per-layer q4_K GEMVs
+  stream_probe = the rate of a plain 16-byte-load read of 4 GiB
+               (mq_probe_stream_read), measured first in the same run
   cpu_baseline = the reference oracle on the host, on a bounded sample
 
 Other workloads (--workload 05b|single|batched|moe) print their own line.
@@ -46,7 +50,6 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="7b", choices=["7b", "05b", "single", "batched", "moe"])
-    p.add_argument("--eager", action="store_true", help="also time the eager arm, interleaved")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=3, help="passes of the dominant-kernel timing region")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -197,12 +200,44 @@ def time_kernels(mq, model, eager_chain, reps):
                         "GB_s": round(d["bytes"] / float(np.mean(d["us"])) / 1e3, 1)}
                  for name, d in by_kind.items()}
     kernel_sum_ms = sum(us) / reps / 1e3
+    layer = [by_kind[k] for k in ("qkv", "o", "gate/up", "down") if k in by_kind]
+    agg_b = sum(d["bytes"] * len(d["us"]) for d in layer)
+    agg_us = sum(sum(d["us"]) for d in layer)
+    aggregate = {"what": "byte-weighted aggregate of the per-layer q4_K GEMVs (QKV, O, gate/up, down)",
+                 "GB_s": round(agg_b / agg_us / 1e3, 1), "frac": round(agg_b / agg_us / 1e3 / HBM_PEAK_GBS, 4)}
     return {"bound": "hbm", "kernel": dominant, "launches": dk["n"], "bytes_per_launch": round(avg_b),
             "us_per_launch": round(avg_us, 3), "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dominant, model.name),
             "timing": "dispatch events of each launch (hipExtLaunchKernelGGL), launched from an idle stream "
                       "in eager steps; includes the dispatch latency a graph replay hides",
-            "per_shape": per_shape}, kernel_sum_ms
+            "per_shape": per_shape, "q4k_layer_aggregate": aggregate}, kernel_sum_ms
+
+
+def stream_probe(mq, gib=4, reps=5):
+    """The plain streaming-read rate (mq_probe_stream_read over `gib` GiB, a
+    few workgroup counts, best mean over `reps` timed passes each)."""
+    import torch
+    buf = torch.empty(gib << 28, dtype=torch.int32, device="cuda:0")
+    nbytes = buf.numel() * 4
+    best = None
+    for wgs in (256, 512, 1024):
+        for _ in range(2):
+            mq.mq_probe_stream_read(buf, workgroups=wgs)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            mq.mq_probe_stream_read(buf, workgroups=wgs)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"stream probe {gib} GiB, {wgs} x 1024 threads: {ms:.3f} ms, {gbs:.1f} GB/s")
+        if best is None or gbs > best["GB_s"]:
+            best = {"GB_s": round(gbs, 1), "bytes": nbytes, "workgroups": wgs, "ms": round(ms, 4)}
+    del buf
+    torch.cuda.empty_cache()
+    best["frac_of_peak"] = round(best["GB_s"] / HBM_PEAK_GBS, 4)
+    return best
 
 
 def cpu_baseline_decode(model, host_w, n_layers_sample):
@@ -262,6 +297,7 @@ def run_decode(args, model, cpu_layers):
     from block_quantized_gemv_amd import binding as mq
     from block_quantized_gemv_amd import synth
     dev = torch.device("cuda:0")
+    probe = stream_probe(mq)
     log(f"generating and uploading {model.weight_bytes() / 1e9:.2f} GB of weights")
     W, host_w = upload_model(model, dev, keep_host=not args.no_cpu_baseline)
     X = torch.from_numpy(synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (16, model.hidden))).to(dev)
@@ -286,25 +322,33 @@ def run_decode(args, model, cpu_layers):
     ms = wall * 1e3 / args.steps
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
-    ab = None
-    if args.eager:
-        # interleaved A/B on one binary: graph and eager steps alternate
-        ga, ea = [], []
-        for _ in range(args.steps):
-            for arm, out in ((chain, ga), (eager, ea)):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                arm.step(mq.MQ_GRAPH)
-                b.record()
-                out.append((a, b))
-        torch.cuda.synchronize()
-        ga = [a.elapsed_time(b) for a, b in ga]
-        ea = [a.elapsed_time(b) for a, b in ea]
-        ab = {"graph_ms": round(float(np.mean(ga)), 4), "graph_sem_ms": round(sem(ga), 5),
-              "eager_ms": round(float(np.mean(ea)), 4), "eager_sem_ms": round(sem(ea), 5)}
-        log(f"interleaved A/B: {ab}")
+    # Interleaved A/B arms on one binary, one step of each in turn: the
+    # graph, the same kernels launched eagerly, and the unfused-glue graph
+    # (standalone RMSNorm/SwiGLU->q8_0 kernels between q8_0-input GEMVs).
+    unfused = mq.DecodeChain(model, W, X, flags=mq.MQ_UNFUSED_GLUE)
+    for _ in range(args.warmup):
+        unfused.step(mq.MQ_GRAPH)
+    arms = {"graph": (chain, mq.MQ_GRAPH), "eager": (eager, mq.MQ_EAGER), "unfused_glue_graph": (unfused, mq.MQ_GRAPH)}
+    evs = {k: [] for k in arms}
+    for _ in range(args.steps):
+        for k, (arm, mode) in arms.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            arm.step(mode)
+            b.record()
+            evs[k].append((a, b))
+    torch.cuda.synchronize()
+    ab = {"steps_per_arm": args.steps, "unfused_glue_nodes": unfused.info()["n_nodes"]}
+    for k, v in evs.items():
+        t = [a.elapsed_time(b) for a, b in v]
+        ab[f"{k}_ms"] = round(float(np.mean(t)), 4)
+        ab[f"{k}_sem_ms"] = round(sem(t), 5)
+    unfused.close()
+    log(f"interleaved A/B: {ab}")
 
     roof, kernel_sum_ms = time_kernels(mq, model, eager, args.kernel_reps)
+    roof["frac_of_stream_probe"] = round(roof["achieved"] / probe["GB_s"], 4)
+    roof["q4k_layer_aggregate"]["frac_of_stream_probe"] = round(roof["q4k_layer_aggregate"]["GB_s"] / probe["GB_s"], 4)
     log(f"dominant kernel {roof['kernel']}: {roof['achieved']} GB/s per launch "
         f"({roof['frac'] * 100:.1f}% of 8 TB/s); GEMV kernel sum {kernel_sum_ms:.3f} ms/step")
     nbytes = model.algorithmic_bytes()
@@ -317,11 +361,11 @@ def run_decode(args, model, cpu_layers):
                       "seed": model.seed, "weights": "q4_K (lm_head q8_0)", "graph": bool(info["captured"]),
                       "graph_nodes": info["n_nodes"], "bytes_per_step": nbytes},
            "tok_per_s": round(1e3 / ms, 2), "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+           "pct_of_stream_probe": round(100 * value / probe["GB_s"], 2), "stream_probe": probe,
            "step_event_ms": round(float(np.mean(per_step)), 4), "step_event_sem_ms": round(sem(per_step), 5),
            "gemv_kernel_sum_ms": round(kernel_sum_ms, 4),
            "roofline": roof}
-    if ab:
-        out["ab_graph_vs_eager"] = ab
+    out["ab_interleaved"] = ab
     chain.close()
     eager.close()
     del W
@@ -434,13 +478,39 @@ def run_moe(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     us = wall * 1e6 / T
+    # interleaved arms in blocks of tokens (a token takes ~20 us, less than
+    # the host needs to submit it with per-token events, so single-token
+    # blocks would time the host): the graph and the same two kernels
+    # launched eagerly (a second chain with its own token counter)
+    eager = mq.MoEChain(wl.n_experts, wl.n_sel, H, I, gu.view(-1), gu[0].numel(), dn.view(-1), dn[0].numel(),
+                        torch.from_numpy(ids).to(dev), torch.from_numpy(logits).to(dev), torch.from_numpy(X).to(dev),
+                        flags=mq.MQ_EAGER_ONLY)
+    chain.reset(0)
+    rounds, block = 10, max(1, T // 10)
+    evs = {"graph": [], "eager": []}
+    for _ in range(rounds):
+        for k, arm, mode in (("graph", chain, mq.MQ_GRAPH), ("eager", eager, mq.MQ_EAGER)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(block):
+                arm.step(mode)
+            e1.record()
+            evs[k].append((e0, e1))
+    torch.cuda.synchronize()
+    ab = {"rounds": rounds, "tokens_per_block": block}
+    for k, v in evs.items():
+        t = [e0.elapsed_time(e1) * 1e3 / block for e0, e1 in v]
+        ab[f"{k}_us_per_token"] = round(float(np.mean(t)), 3)
+        ab[f"{k}_sem_us"] = round(sem(t), 4)
+    eager.close()
+    log(f"interleaved A/B: {ab}")
     nbytes = wl.token_weight_bytes()
     return {"metric": METRIC, "value": round(nbytes / us / 1e3, 1), "unit": "GB/s", "n_gpus": 1, "steps": T,
             "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int8", "data": "synthetic",
             "config": {"workload": wl.name, "seed": wl.seed, "tokens": T, "bytes_per_token_padded": nbytes},
             "us_per_token": round(us, 3), "event_us_per_token": round(a.elapsed_time(b) * 1e3 / T, 3),
-            "tokens_per_s": round(1e6 / us, 1)}
+            "tokens_per_s": round(1e6 / us, 1), "ab_interleaved": ab}
 
 
 def calibrate_copy(mib):

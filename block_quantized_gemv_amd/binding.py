@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmq.so")
 
 MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_HIP, MQ_ERR_CAPTURE, MQ_ERR_NOMEM = 0, -1, -2, -3, -4, -5
-MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE = 1, 2, 4
+MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE, MQ_UNFUSED_GLUE = 1, 2, 4, 8
 MQ_GRAPH, MQ_EAGER = 0, 1
 MQ_FAULT_NONE, MQ_FAULT_CAPTURE = 0, 1
 
@@ -71,6 +71,7 @@ SIGNATURES = {
     "mq_moe_step": ([_vp, _int, _vp], _int),
     "mq_test_set_fault": ([_u32], _int),
     "mq_time_next_launches": ([C.POINTER(_vp), C.POINTER(_vp), _int], _int),
+    "mq_probe_stream_read": ([_vp, _i64, _vp, _int, _vp], _int),
 }
 
 _LIB = None
@@ -137,6 +138,18 @@ def mq_time_next_launches(starts, stops):
     n = len(starts)
     a, b = (_vp * max(n, 1))(*starts), (_vp * max(n, 1))(*stops)
     _check(lib().mq_time_next_launches(a, b, n))
+
+
+def mq_probe_stream_read(buf, xor_out=None, workgroups=0, stream=None):
+    """Streaming-read probe over the bytes of `buf` (a contiguous device
+    tensor whose size is a multiple of 16); returns the uint32 device tensor
+    holding the XOR of its 32-bit words."""
+    nbytes = buf.numel() * buf.element_size()
+    if xor_out is None:
+        xor_out = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _check(lib().mq_probe_stream_read(_ptr(buf, what="buf"), nbytes, _ptr(xor_out, torch.int32, 4, "xor_out"),
+                                      int(workgroups), _stream(stream)))
+    return xor_out
 
 
 def mq_quantize_q8_0(x, xq=None, stream=None):

@@ -233,6 +233,14 @@ int mq_time_next_launches(const hipEvent_t* starts, const hipEvent_t* stops, int
     return ok();
 }
 
+int mq_probe_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int workgroups, hipStream_t stream) {
+    CHECK_ARG(xor_out && (p || bytes == 0), "null pointer (p=%p xor_out=%p)", p, (void*)xor_out);
+    CHECK_ARG(aligned(p, 16) && aligned(xor_out, 4), "p must be 16-byte aligned, xor_out 4-byte aligned");
+    CHECK_ARG(bytes >= 0 && bytes % 16 == 0, "bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+    CHECK_ARG(workgroups <= 65536, "workgroups=%d out of range", workgroups);
+    return hip_status(launch_stream_read(p, bytes, xor_out, workgroups, stream), "stream probe launch");
+}
+
 int mq_test_set_fault(unsigned fault_mask) {
     g_fault = fault_mask;
     return ok();
@@ -378,6 +386,40 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     // the last one, advances it.  The q8_0 vectors formed in prologues are
     // written out (by one workgroup) only when intermediates are kept.
     const float* h_prev = nullptr;
+    if (d->flags & MQ_UNFUSED_GLUE) {
+        // The unfused arm: glue kernels between plain q8_0-input GEMVs.
+        for (int l = 0; l < L; ++l) {
+            uint8_t* q8 = c->q8_trace + (keep ? l * q8_layer : 0);
+            float* f = c->f32_trace + (keep ? l * f32_layer : 0);
+            uint8_t *qa = q8, *qb = q8 + qH, *qc = q8 + 2 * qH, *qg = q8 + 3 * qH;
+            float *t = f, *o = f + QKV, *gu = f + QKV + H, *h = f + QKV + H + 2 * I;
+            const void *wq = d->w_qkv[l], *wo = d->w_o[l], *wg = d->w_gu[l], *wd = d->w_down[l];
+            const float* xin = l == 0 ? x_table : h_prev;
+            const int64_t* sel = l == 0 ? step : nullptr;
+            const int nin = l == 0 ? n_inputs : 1;
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(xin, qa, H, eps, sel, nin, nullptr, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, nullptr, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, nullptr, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wg, qc, 0, gu, nullptr, nullptr, 2 * I, H, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, qg, I, 1, I, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s); });
+            h_prev = h;
+        }
+        uint8_t* qz = c->q8_trace + (keep ? L * q8_layer : q8_layer);
+        const void* wlm = d->w_lm;
+        float* logits = d->logits;
+        const int64_t V = d->vocab;
+        const float* hl = h_prev;
+        c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(hl, qz, H, eps, nullptr, 1, step, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0(wlm, qz, logits, nullptr, V, H, s); });
+        if (!keep) c->q8_bytes = c->f32_count = 0;
+        rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
+        if (rc != MQ_OK) { chain_free(c); return rc; }
+        *out = c;
+        return ok();
+    }
     for (int l = 0; l < L; ++l) {
         uint8_t* q8 = c->q8_trace + (keep ? l * q8_layer : 0);
         float* f = c->f32_trace + (keep ? l * f32_layer : 0);

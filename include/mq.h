@@ -178,8 +178,14 @@ typedef struct mq_chain mq_chain;
 
 /* MQ_EXACT_GLUE is a test hook: the RMSNorm->q8_0 prologues compute every
  * value with the divisions themselves instead of reciprocal products that
- * are checked to round the same way; the results are byte-identical. */
-enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u };
+ * are checked to round the same way; the results are byte-identical.
+ * MQ_UNFUSED_GLUE builds the same step without fusion, the measurement arm
+ * the fused step is compared against (Lecture 08, §6 re-prices fusion under
+ * capture): every Q8(RMSNorm(.)) and Q8(SwiGLU(.)) is its own kernel and the
+ * GEMVs read q8_0 inputs, 8 kernels per layer plus 2.  Its RMSNorm sums the
+ * squares in another order, so codes can differ from the fused step's by
+ * one near a rounding tie; each stage still meets the oracle's bounds. */
+enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u, MQ_UNFUSED_GLUE = 8u };
 enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
 
 typedef struct {
@@ -194,7 +200,7 @@ typedef struct {
     int n_inputs;                      /* >= 1 */
     float* logits;                     /* device f32 [vocab] */
     float eps;
-    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE */
+    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE | MQ_UNFUSED_GLUE */
 } mq_chain_desc;
 
 /* Validates, allocates every device buffer the step needs (nothing is
@@ -275,6 +281,22 @@ int mq_moe_step(mq_chain* c, int mode, hipStream_t stream);
  * 0 <= n <= 65536.
  */
 int mq_time_next_launches(const hipEvent_t* starts, const hipEvent_t* stops, int n);
+
+/* ---------------------------------------------------------------------------
+ * Measurement: streaming-read probe.  Reads `bytes` at device pointer p once
+ * (plain 16-byte loads, grid-stride, four in flight per lane) and writes the
+ * XOR of all its 32-bit words to the device uint32 *xor_out (overwritten; the
+ * value lets a test check that every word was read).  It gives the read rate
+ * this GPU reaches on a large buffer, against which the GEMVs' rates are
+ * reported beside the data-sheet HBM peak (the weight stream of
+ * 'Part 4 · Lecture 08 — Graph-Resident Decode' is a pure read of this kind).
+ * p must be 16-byte aligned and bytes a multiple of 16 (0 allowed);
+ * workgroups of 1024 threads, <= 0 for one per CU, at most 65536.
+ * Asynchronous on `stream`; the caller owns both buffers.  Errors:
+ * MQ_ERR_ARG for null pointers, misalignment, a bad size or workgroup count;
+ * MQ_ERR_HIP for a failed launch. */
+int mq_probe_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int workgroups,
+                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Test hook, never read from the environment (environment variables are

@@ -59,6 +59,15 @@ def test_gemv_argument_errors(mq):
     assert L.mq_rmsnorm_quantize_q8_0(FAKE, FAKE, 64, -1.0, None) == mq.MQ_ERR_ARG
 
 
+def test_stream_probe_argument_errors(mq):
+    L = mq.lib()
+    assert L.mq_probe_stream_read(FAKE, 64, None, 0, None) == mq.MQ_ERR_ARG                  # null xor_out
+    assert L.mq_probe_stream_read(None, 64, FAKE, 0, None) == mq.MQ_ERR_ARG                  # null buffer
+    assert L.mq_probe_stream_read(C.c_void_p(0x10008), 64, FAKE, 0, None) == mq.MQ_ERR_ARG   # not 16-aligned
+    assert L.mq_probe_stream_read(FAKE, 40, FAKE, 0, None) == mq.MQ_ERR_ARG                  # not a multiple of 16
+    assert L.mq_probe_stream_read(FAKE, 64, FAKE, 70000, None) == mq.MQ_ERR_ARG              # workgroups
+
+
 def test_grouped_argument_errors(mq):
     L = mq.lib()
     # combine without y_out

@@ -169,14 +169,14 @@ def test_capture_failure_falls_back_to_eager(mq, small_model):
         assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), f"fallback differs at step {i}"
 
 
-def _chain_vs_oracle(mq, o, pool, model, n_layers, n_inputs=2):
+def _chain_vs_oracle(mq, o, pool, model, n_layers, n_inputs=2, flags=0):
     from block_quantized_gemv_amd import synth
     m = dataclasses.replace(model, n_layers=n_layers)
     log(f"generating {m.name} x{n_layers} layers")
     W = model_weights(m, n_layers)
     X = synth.normal_f32(m.seed, (synth.KEY_STEP_INPUTS,), (n_inputs, m.hidden))
     Wd = _dev_weights(W)
-    ch = mq.DecodeChain(m, Wd, to_dev(X), flags=mq.MQ_KEEP_INTERMEDIATES)
+    ch = mq.DecodeChain(m, Wd, to_dev(X), flags=mq.MQ_KEEP_INTERMEDIATES | flags)
     for step in range(n_inputs):
         logits = to_host(ch.step()).copy()
         q8t, f32t = ch.trace()
@@ -205,6 +205,27 @@ def test_chain_7b_full_depth_vs_oracle(mq, o, pool):
     """The benchmark's configuration: all 28 layers and the lm_head."""
     from block_quantized_gemv_amd import workloads
     _chain_vs_oracle(mq, o, pool, workloads.DECODE_7B, workloads.DECODE_7B.n_layers, n_inputs=1)
+
+
+def test_unfused_glue_chain_vs_oracle(mq, o, pool):
+    """The unfused measurement arm (glue kernels between q8_0-input GEMVs)
+    computes the same step: 0.5B, all layers, against the oracle."""
+    from block_quantized_gemv_amd import workloads
+    _chain_vs_oracle(mq, o, pool, workloads.DECODE_05B, workloads.DECODE_05B.n_layers, flags=mq.MQ_UNFUSED_GLUE)
+
+
+def test_unfused_glue_chain_graph_equals_eager(mq, small_model):
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    g = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_UNFUSED_GLUE)
+    e = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_UNFUSED_GLUE | mq.MQ_EAGER_ONLY)
+    assert g.info()["captured"] and g.info()["n_nodes"] == 8 * model.n_layers + 2
+    for i in range(5):
+        u, v = to_host(g.step(mq.MQ_GRAPH)).copy(), to_host(e.step(mq.MQ_EAGER)).copy()
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), f"unfused graph != eager at step {i}"
+    assert g.info()["step"] == 5
+    g.close()
+    e.close()
 
 
 # ----------------------------------------------------------- routed experts ----

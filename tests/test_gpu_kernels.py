@@ -285,3 +285,20 @@ def test_grouped_gate_up_and_down(mq, o, experts):
     assert np.all(np.isfinite(y_b[0])) and np.all(np.isnan(y_b[1])) and np.all(np.isnan(y_b[3]))
     assert np.all(np.isnan(y_o))
     del torch
+
+
+# ------------------------------------------------------ measurement probe ----
+
+def test_stream_probe_reads_every_word(mq):
+    """The streaming-read probe's XOR over all 32-bit words equals numpy's, for
+    sizes that end inside the four-load body and inside the tail loop, and for
+    an empty buffer."""
+    import torch
+    rng = np.random.default_rng(11)
+    for n16, wgs in ((0, 0), (1, 0), (4097, 3), (256 * 1024 * 4 * 2 + 12345, 0), (1000003, 700)):
+        host = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint32)
+        buf = torch.from_numpy(host.view(np.int32)).cuda() if n16 else torch.empty(0, dtype=torch.int32,
+                                                                                   device="cuda")
+        got = int(mq.mq_probe_stream_read(buf, workgroups=wgs).cpu().numpy().view(np.uint32)[0])
+        want = int(np.bitwise_xor.reduce(host)) if n16 else 0
+        assert got == want, (n16, wgs, hex(got), hex(want))
