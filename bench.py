@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="7b", choices=["7b", "05b", "single", "batched", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ab", action="store_true", help="skip the interleaved A/B arms (for counter runs)")
     p.add_argument("--kernel-reps", type=int, default=3, help="passes of the dominant-kernel timing region")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of this many MiB (counter calibration)")
@@ -292,6 +293,34 @@ def _cpu_model():
     return "unknown"
 
 
+def interleaved_arms(args, mq, model, W, X, chain, eager):
+    import torch
+    # Interleaved A/B arms on one binary, one step of each in turn: the
+    # graph, the same kernels launched eagerly, and the unfused-glue graph
+    # (standalone RMSNorm/SwiGLU->q8_0 kernels between q8_0-input GEMVs).
+    unfused = mq.DecodeChain(model, W, X, flags=mq.MQ_UNFUSED_GLUE)
+    for _ in range(args.warmup):
+        unfused.step(mq.MQ_GRAPH)
+    arms = {"graph": (chain, mq.MQ_GRAPH), "eager": (eager, mq.MQ_EAGER), "unfused_glue_graph": (unfused, mq.MQ_GRAPH)}
+    evs = {k: [] for k in arms}
+    for _ in range(args.steps):
+        for k, (arm, mode) in arms.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            arm.step(mode)
+            b.record()
+            evs[k].append((a, b))
+    torch.cuda.synchronize()
+    ab = {"steps_per_arm": args.steps, "unfused_glue_nodes": unfused.info()["n_nodes"]}
+    for k, v in evs.items():
+        t = [a.elapsed_time(b) for a, b in v]
+        ab[f"{k}_ms"] = round(float(np.mean(t)), 4)
+        ab[f"{k}_sem_ms"] = round(sem(t), 5)
+    unfused.close()
+    log(f"interleaved A/B: {ab}")
+    return ab
+
+
 def run_decode(args, model, cpu_layers):
     import torch
     from block_quantized_gemv_amd import binding as mq
@@ -322,29 +351,7 @@ def run_decode(args, model, cpu_layers):
     ms = wall * 1e3 / args.steps
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
-    # Interleaved A/B arms on one binary, one step of each in turn: the
-    # graph, the same kernels launched eagerly, and the unfused-glue graph
-    # (standalone RMSNorm/SwiGLU->q8_0 kernels between q8_0-input GEMVs).
-    unfused = mq.DecodeChain(model, W, X, flags=mq.MQ_UNFUSED_GLUE)
-    for _ in range(args.warmup):
-        unfused.step(mq.MQ_GRAPH)
-    arms = {"graph": (chain, mq.MQ_GRAPH), "eager": (eager, mq.MQ_EAGER), "unfused_glue_graph": (unfused, mq.MQ_GRAPH)}
-    evs = {k: [] for k in arms}
-    for _ in range(args.steps):
-        for k, (arm, mode) in arms.items():
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            arm.step(mode)
-            b.record()
-            evs[k].append((a, b))
-    torch.cuda.synchronize()
-    ab = {"steps_per_arm": args.steps, "unfused_glue_nodes": unfused.info()["n_nodes"]}
-    for k, v in evs.items():
-        t = [a.elapsed_time(b) for a, b in v]
-        ab[f"{k}_ms"] = round(float(np.mean(t)), 4)
-        ab[f"{k}_sem_ms"] = round(sem(t), 5)
-    unfused.close()
-    log(f"interleaved A/B: {ab}")
+    ab = None if args.no_ab else interleaved_arms(args, mq, model, W, X, chain, eager)
 
     roof, kernel_sum_ms = time_kernels(mq, model, eager, args.kernel_reps)
     roof["frac_of_stream_probe"] = round(roof["achieved"] / probe["GB_s"], 4)
@@ -365,7 +372,8 @@ def run_decode(args, model, cpu_layers):
            "step_event_ms": round(float(np.mean(per_step)), 4), "step_event_sem_ms": round(sem(per_step), 5),
            "gemv_kernel_sum_ms": round(kernel_sum_ms, 4),
            "roofline": roof}
-    out["ab_interleaved"] = ab
+    if ab:
+        out["ab_interleaved"] = ab
     chain.close()
     eager.close()
     del W
