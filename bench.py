@@ -471,8 +471,14 @@ def run_moe(args):
     T = wl.n_tokens
     ids, logits = synth.routing(wl.seed, T, wl.n_experts, wl.n_sel)
     X = synth.normal_f32(wl.seed, (synth.KEY_TOKEN_X,), (T, H))
-    chain = mq.MoEChain(wl.n_experts, wl.n_sel, H, I, gu.view(-1), gu[0].numel(), dn.view(-1), dn[0].numel(),
-                        torch.from_numpy(ids).to(dev), torch.from_numpy(logits).to(dev), torch.from_numpy(X).to(dev))
+    tables = (torch.from_numpy(ids).to(dev), torch.from_numpy(logits).to(dev), torch.from_numpy(X).to(dev))
+    per = 8    # tokens per graph launch (one launch per token is host-bound)
+
+    def make(flags=0, tpl=per):
+        return mq.MoEChain(wl.n_experts, wl.n_sel, H, I, gu.view(-1), gu[0].numel(), dn.view(-1), dn[0].numel(),
+                           *tables, flags=flags, tokens_per_launch=tpl)
+
+    chain = make()
     for _ in range(args.warmup):
         chain.step()
     chain.reset(0)
@@ -480,27 +486,26 @@ def run_moe(args):
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     a.record()
-    for _ in range(T):
+    for _ in range(T // per):
         chain.step()
     b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    us = wall * 1e6 / T
-    # interleaved arms in blocks of tokens (a token takes ~20 us, less than
-    # the host needs to submit it with per-token events, so single-token
-    # blocks would time the host): the graph and the same two kernels
-    # launched eagerly (a second chain with its own token counter)
-    eager = mq.MoEChain(wl.n_experts, wl.n_sel, H, I, gu.view(-1), gu[0].numel(), dn.view(-1), dn[0].numel(),
-                        torch.from_numpy(ids).to(dev), torch.from_numpy(logits).to(dev), torch.from_numpy(X).to(dev),
-                        flags=mq.MQ_EAGER_ONLY)
+    us = wall * 1e6 / (T // per * per)
+    # interleaved arms in blocks of 104 tokens (a token takes ~20 us, less
+    # than the host needs to submit it with events around it): graphs of 8
+    # and of 1 token per launch, and the same kernels launched eagerly (each
+    # chain with its own token counter)
+    arms = {"graph_8_per_launch": (chain, mq.MQ_GRAPH, per), "graph_1_per_launch": (make(tpl=1), mq.MQ_GRAPH, 1),
+            "eager": (make(flags=mq.MQ_EAGER_ONLY, tpl=1), mq.MQ_EAGER, 1)}
     chain.reset(0)
-    rounds, block = 10, max(1, T // 10)
-    evs = {"graph": [], "eager": []}
+    rounds, block = 10, 104
+    evs = {k: [] for k in arms}
     for _ in range(rounds):
-        for k, arm, mode in (("graph", chain, mq.MQ_GRAPH), ("eager", eager, mq.MQ_EAGER)):
+        for k, (arm, mode, tpl) in arms.items():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(block):
+            for _ in range(block // tpl):
                 arm.step(mode)
             e1.record()
             evs[k].append((e0, e1))
@@ -510,14 +515,17 @@ def run_moe(args):
         t = [e0.elapsed_time(e1) * 1e3 / block for e0, e1 in v]
         ab[f"{k}_us_per_token"] = round(float(np.mean(t)), 3)
         ab[f"{k}_sem_us"] = round(sem(t), 4)
-    eager.close()
+    for k, (arm, _, _) in arms.items():
+        if arm is not chain:
+            arm.close()
     log(f"interleaved A/B: {ab}")
     nbytes = wl.token_weight_bytes()
     return {"metric": METRIC, "value": round(nbytes / us / 1e3, 1), "unit": "GB/s", "n_gpus": 1, "steps": T,
             "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl.name, "seed": wl.seed, "tokens": T, "bytes_per_token_padded": nbytes},
-            "us_per_token": round(us, 3), "event_us_per_token": round(a.elapsed_time(b) * 1e3 / T, 3),
+            "config": {"workload": wl.name, "seed": wl.seed, "tokens": T, "tokens_per_graph_launch": per,
+                       "bytes_per_token_padded": nbytes},
+            "us_per_token": round(us, 3), "event_us_per_token": round(a.elapsed_time(b) * 1e3 / (T // per * per), 3),
             "tokens_per_s": round(1e6 / us, 1), "ab_interleaved": ab}
 
 

@@ -45,7 +45,8 @@ class MoEDesc(C.Structure):
     _fields_ = [("n_experts", C.c_int), ("n_sel", C.c_int), ("hidden", C.c_int64), ("inter", C.c_int64),
                 ("w_gu_all", _vp), ("gu_expert_bytes", C.c_int64), ("w_dn_all", _vp),
                 ("dn_expert_bytes", C.c_int64), ("ids_table", _vp), ("logits_table", _vp),
-                ("x_table", _vp), ("y_table", _vp), ("n_tokens", C.c_int), ("flags", C.c_uint)]
+                ("x_table", _vp), ("y_table", _vp), ("n_tokens", C.c_int), ("flags", C.c_uint),
+                ("tokens_per_launch", C.c_int)]
 
 
 SIGNATURES = {
@@ -299,10 +300,10 @@ class DecodeChain:
 
 
 class MoEChain:
-    """One routed-expert FFN token per step (mq_moe_create / mq_moe_step)."""
+    """Routed-expert FFN tokens, `tokens_per_launch` per step (mq_moe_create / mq_moe_step)."""
 
     def __init__(self, n_experts, n_sel, hidden, inter, w_gu_all, gu_bytes, w_dn_all, dn_bytes,
-                 ids_table, logits_table, x_table, y_table=None, flags=0, stream=None):
+                 ids_table, logits_table, x_table, y_table=None, flags=0, stream=None, tokens_per_launch=1):
         n_tokens = ids_table.shape[0]
         self.y_table = y_table if y_table is not None else torch.zeros((n_tokens, hidden), dtype=torch.float32,
                                                                        device=x_table.device)
@@ -313,7 +314,8 @@ class MoEChain:
                     _ptr(ids_table, torch.int32, 4 * n_tokens * n_sel, "ids_table"),
                     _ptr(logits_table, torch.float32, 4 * n_tokens * n_sel, "logits_table"),
                     _ptr(x_table, torch.float32, 4 * n_tokens * hidden, "x_table"),
-                    _ptr(self.y_table, torch.float32, 4 * n_tokens * hidden, "y_table"), n_tokens, flags)
+                    _ptr(self.y_table, torch.float32, 4 * n_tokens * hidden, "y_table"), n_tokens, flags,
+                    tokens_per_launch)
         h = _vp()
         _check(lib().mq_moe_create(C.byref(d), _stream(stream), C.byref(h)))
         self.handle = h

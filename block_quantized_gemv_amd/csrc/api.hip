@@ -458,6 +458,7 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     CHECK_SHAPE(d->hidden >= 256 && d->hidden % 256 == 0 && d->hidden <= kMaxK, "hidden must be a multiple of 256");
     CHECK_SHAPE(d->inter >= 32 && d->inter % 32 == 0 && d->inter <= kMaxK, "inter must be a multiple of 32");
     CHECK_SHAPE(d->n_tokens >= 1, "n_tokens must be >= 1");
+    CHECK_SHAPE(d->tokens_per_launch >= 0 && d->tokens_per_launch <= 256, "tokens_per_launch out of range [0, 256]");
     const int64_t H = d->hidden, I = d->inter, KP = (I + 255) / 256 * 256;
     CHECK_SHAPE(d->gu_expert_bytes >= 2 * I * (H / 256) * kQ4KBytes && d->gu_expert_bytes % 16 == 0,
                 "gu_expert_bytes too small or not a multiple of 16");
@@ -489,14 +490,18 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     // counter.
     int64_t *step = c->step, *cur = c->cur;
     const mq_moe_desc dd = *d;
-    c->ops.push_back([=](hipStream_t s) {
-        return launch_moe_gate_up(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, I, H, step, dd.n_tokens,
-                                  dd.ids_table, dd.logits_table, dd.x_table, S, KP, cur, ids, comb, gq, nullptr, s);
-    });
-    c->ops.push_back([=](hipStream_t s) {
-        return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,
-                                       nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, step, s);
-    });
+    const int per_launch = d->tokens_per_launch > 0 ? d->tokens_per_launch : 1;
+    for (int t = 0; t < per_launch; ++t) {
+        c->ops.push_back([=](hipStream_t s) {
+            return launch_moe_gate_up(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, I, H, step, dd.n_tokens,
+                                      dd.ids_table, dd.logits_table, dd.x_table, S, KP, cur, ids, comb, gq, nullptr,
+                                      s);
+        });
+        c->ops.push_back([=](hipStream_t s) {
+            return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,
+                                           nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, step, s);
+        });
+    }
     rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
     if (rc != MQ_OK) { chain_free(c); return rc; }
     *out = c;

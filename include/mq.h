@@ -244,6 +244,10 @@ int mq_chain_destroy(mq_chain* c);
  * Routing ids are bounds-checked on the device (see mq_gemv_q4k_grouped).
  * A token is two kernels: gate/up with x_t quantized in its prologue and
  * the SwiGLU -> q8_0 glue in its epilogue, then down with the combine.
+ * One mq_moe_step runs tokens_per_launch consecutive tokens (their kernels
+ * are captured into one graph): a graph launch costs the host about as
+ * much as one token's GPU time here, so replaying one token per launch
+ * leaves the GPU waiting on the host.
  */
 typedef struct {
     int n_experts, n_sel;              /* 1 <= n_sel <= 16 */
@@ -258,6 +262,7 @@ typedef struct {
     float* y_table;                    /* device [n_tokens][hidden] */
     int n_tokens;
     unsigned flags;                    /* MQ_EAGER_ONLY */
+    int tokens_per_launch;             /* tokens per mq_moe_step call, 1..256 (0 means 1) */
 } mq_moe_desc;
 
 /* Same life cycle and graph/eager semantics as the decode chain; each

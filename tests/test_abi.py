@@ -91,4 +91,6 @@ def test_chain_argument_errors(mq):
     assert L.mq_chain_destroy(None) == mq.MQ_OK
     m = mq.MoEDesc(64, 8, 2048, 1408, FAKE, 16, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 10, 0)
     assert L.mq_moe_create(C.byref(m), None, C.byref(out)) == mq.MQ_ERR_SHAPE          # expert bytes too small
+    m = mq.MoEDesc(64, 8, 2048, 1408, FAKE, 1 << 24, FAKE, 1 << 24, FAKE, FAKE, FAKE, FAKE, 10, 0, 257)
+    assert L.mq_moe_create(C.byref(m), None, C.byref(out)) == mq.MQ_ERR_SHAPE          # tokens_per_launch
     assert L.mq_test_set_fault(0) == mq.MQ_OK

@@ -262,3 +262,10 @@ def test_moe_chain(mq, o):
             s_abs += abs(float(c_ref[s])) * sa
         check_tolerance(yg[t], y_ref, s_abs, f"token {t}")
     assert g.info()["step"] == T
+    # several tokens per launch: the same bytes, tokens_per_launch tokens per call
+    m4 = mq.MoEChain(*args, tokens_per_launch=4)
+    assert m4.info()["captured"] and m4.info()["n_nodes"] == 8
+    for _ in range(T // 4):
+        m4.step(mq.MQ_GRAPH)
+    assert m4.info()["step"] == T
+    assert np.array_equal(to_host(m4.y_table).view(np.uint32), yg.view(np.uint32)), "4 tokens per launch != 1"
