@@ -772,13 +772,13 @@ static hipError_t launch_nc(const void* w, const void* xq, int64_t xq_col_bytes,
 // every thread takes at most one step when possible (a prologue is bound by
 // each wave's instruction latency, not by the CU's issue rate).  Waves loop
 // over `units` equal work units.
-void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads) {
+void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads, int max_waves) {
     const int64_t cus = device_cu_count();
     const int64_t g = units < cus ? units : cus;
     const int64_t for_units = (units + g - 1) / g;
     const int64_t for_chunks = (prologue + 63) / 64;
     int64_t wpg = for_units > for_chunks ? for_units : for_chunks;
-    if (wpg > 16) wpg = 16;
+    if (wpg > max_waves) wpg = max_waves;
     if (wpg < 1) wpg = 1;
     *grid = (int)(g > 0 ? g : 1);
     *threads = (int)(64 * wpg);
@@ -790,7 +790,7 @@ static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads);
+    prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads, kWavesQ8Early);
     MQ_LAUNCH((k_gemv_q4k<1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
               (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb, p.log2s,
               p.passes, p.n_tiles, NormIn{});
@@ -803,7 +803,7 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, k / 4, &grid, &threads);
+    prologue_grid(p.n_tiles, k / 4, &grid, &threads, kWavesNorm);
     MQ_LAUNCH((k_gemv_q4k<1, false, kSrcNorm>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
               (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb,
               p.log2s, p.passes, p.n_tiles, nin);

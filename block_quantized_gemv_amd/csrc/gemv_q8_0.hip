@@ -186,7 +186,7 @@ hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int
     const Q8Plan p = plan_q8_0(m, npairs);
     const int lds = stage_bytes(2 * npairs);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, k / 4, &grid, &threads);
+    prologue_grid(p.n_tiles, k / 4, &grid, &threads, kWavesQ8Norm);
     hipEvent_t e0, e1;
     if (take_next_launch_events(&e0, &e1)) {
         (void)hipStreamSynchronize(stream);

@@ -48,8 +48,17 @@ hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* n
                                   int64_t inter, int64_t k, hipStream_t stream);
 // Workgroups and threads per workgroup for `units` equal work units of a
 // kernel whose workgroups each run a prologue of `prologue` per-thread
-// steps (about one workgroup per CU).
-void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads);
+// steps: about one workgroup per CU, of at most max_waves waves.
+void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads, int max_waves);
+// Waves per CU of the one-workgroup-per-CU kernels (measured on the 7B
+// decode step: 16 waves 1.260 ms, 12: 1.249, 8: 1.215, 6: 1.334, 4: 1.433;
+// 7 for the q8_0-input GEMV, whose 3584-row down projection then gets
+// exactly two tiles per wave: 1.207).  More waves compete for each SIMD's
+// issue and lengthen every wave's turn from data arrival to its next
+// request, which costs more than their extra loads in flight buy; fewer
+// leave the K = 3584 RMSNorm prologue more chunks per thread than it keeps
+// in registers.
+constexpr int kWavesNorm = 8, kWavesQ8Early = 7, kWavesQ8Norm = 8;
 // Split-k variant for shapes whose activation does not fit in LDS; `part`
 // holds n_split*m*ncols doubles.
 int gemv_q4k_splitk_nsplit(int64_t k);
