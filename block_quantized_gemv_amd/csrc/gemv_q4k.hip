@@ -789,8 +789,12 @@ static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64
                                   hipStream_t stream) {
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
+    // waves per CU for about kItemsPerWave items each, within [7, 12]
+    const int64_t per_cu = (int64_t)device_cu_count() * kItemsPerWave;
+    const int64_t want = ((int64_t)p.n_tiles * p.passes + per_cu - 1) / per_cu;
+    const int cap = (int)(want < kWavesQ8EarlyMin ? kWavesQ8EarlyMin : want > kWavesQ8EarlyMax ? kWavesQ8EarlyMax : want);
     int grid = 1, threads = 64;
-    prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads, kWavesQ8Early);
+    prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads, cap);
     MQ_LAUNCH((k_gemv_q4k<1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
               (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb, p.log2s,
               p.passes, p.n_tiles, NormIn{});

@@ -51,14 +51,17 @@ hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* n
 // steps: about one workgroup per CU, of at most max_waves waves.
 void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads, int max_waves);
 // Waves per CU of the one-workgroup-per-CU kernels (measured on the 7B
-// decode step: 16 waves 1.260 ms, 12: 1.249, 8: 1.215, 6: 1.334, 4: 1.433;
-// 7 for the q8_0-input GEMV, whose 3584-row down projection then gets
-// exactly two tiles per wave: 1.207).  More waves compete for each SIMD's
-// issue and lengthen every wave's turn from data arrival to its next
-// request, which costs more than their extra loads in flight buy; fewer
-// leave the K = 3584 RMSNorm prologue more chunks per thread than it keeps
-// in registers.
-constexpr int kWavesNorm = 8, kWavesQ8Early = 7, kWavesQ8Norm = 8;
+// decode step: 16 waves 1.260 ms, 12: 1.249, 8: 1.215, 6: 1.334, 4: 1.433).
+// More waves compete for each SIMD's issue and lengthen every wave's turn
+// from data arrival to its next request, which costs more than their extra
+// loads in flight buy; fewer leave the K = 3584 RMSNorm prologue more chunks
+// per thread than it keeps in registers.  The q8_0-input GEMV, whose
+// prologue is short, takes about kItemsPerWave items per wave within
+// [kWavesQ8EarlyMin, kWavesQ8EarlyMax]: 7 waves for the 3584 x 18944 down
+// projection (two tiles per wave; 1.207 ms/step), 12 for a 37888 x 3584
+// matrix (15.9 against 16.5 us at 8 and 17.2 at 16).
+constexpr int kWavesNorm = 8, kWavesQ8Norm = 8;
+constexpr int kWavesQ8EarlyMin = 7, kWavesQ8EarlyMax = 12, kItemsPerWave = 10;
 // Split-k variant for shapes whose activation does not fit in LDS; `part`
 // holds n_split*m*ncols doubles.
 int gemv_q4k_splitk_nsplit(int64_t k);
