@@ -321,6 +321,65 @@ def interleaved_arms(args, mq, model, W, X, chain, eager):
     return ab
 
 
+def host_step_latency(args, mq, model, W, X, chain, ab):
+    import torch
+    # End-to-end step latency as a caller sees it: launch the step, wait for
+    # it, read the logits into host memory.  Arms interleaved step by step:
+    # readback through the library's pinned buffer, straight into pageable
+    # memory, and no readback.  Plus the one-time capture cost and the lazy
+    # capture policy's own capture.
+    # The in-graph arm's chain copies the logits into its own pinned buffer
+    # as the step's last node; its logits are in host memory when the wait
+    # returns.
+    out_p = np.empty(model.vocab, np.float32)
+    out_q = np.empty(model.vocab, np.float32)
+    in_graph = mq.DecodeChain(model, W, X, flags=mq.MQ_HOST_LOGITS)
+    assert in_graph.host_logits() is not None, "pinning the host logits failed"
+    arms = {"pinned_readback": (chain, lambda: chain.read_logits(out=out_p)),
+            "pageable_readback": (chain, lambda: chain.read_logits(out=out_q, pageable=True)),
+            "in_graph_host_copy": (in_graph, lambda: None),
+            "no_readback": (chain, lambda: None)}
+    for _ in range(args.warmup):
+        for c, f in arms.values():
+            c.step(mq.MQ_GRAPH)
+            torch.cuda.synchronize()
+            f()
+    t_sync = {k: [] for k in arms}
+    t_read = {k: [] for k in arms}
+    for _ in range(args.steps):
+        for k, (c, f) in arms.items():
+            t0 = time.perf_counter()
+            c.step(mq.MQ_GRAPH)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            f()
+            t2 = time.perf_counter()
+            t_sync[k].append((t1 - t0) * 1e3)
+            t_read[k].append((t2 - t1) * 1e3)
+    res = {"steps_per_arm": args.steps, "logits_bytes": 4 * model.vocab}
+    for k in arms:
+        tot = [a + b for a, b in zip(t_sync[k], t_read[k])]
+        res[f"{k}_step_ms"] = round(float(np.mean(tot)), 4)
+        res[f"{k}_step_sem_ms"] = round(sem(tot), 5)
+        if k in ("pinned_readback", "pageable_readback"):
+            res[f"{k}_read_us"] = round(1e3 * float(np.mean(t_read[k])), 2)
+            res[f"{k}_read_GB_s"] = round(4 * model.vocab / (float(np.mean(t_read[k])) * 1e-3) / 1e9, 2)
+    res["in_graph_host_copy_nodes"] = in_graph.info()["n_nodes"]
+    in_graph.close()
+    res["capture_ms_at_create"] = round(chain.capture_stats()["capture_ms"], 3)
+    lazy = mq.DecodeChain(model, W, X, flags=mq.MQ_LAZY_CAPTURE)
+    for _ in range(3):
+        lazy.step(mq.MQ_GRAPH)
+    torch.cuda.synchronize()
+    res["lazy_capture_ms_at_third_step"] = round(lazy.capture_stats()["capture_ms"], 3)
+    res["lazy_captured"] = bool(lazy.info()["captured"])
+    lazy.close()
+    if ab and ab["eager_ms"] > ab["graph_ms"]:
+        res["capture_break_even_steps"] = round(res["capture_ms_at_create"] / (ab["eager_ms"] - ab["graph_ms"]), 1)
+    log(f"host step latency: {res}")
+    return res
+
+
 def run_decode(args, model, cpu_layers):
     import torch
     from block_quantized_gemv_amd import binding as mq
@@ -352,6 +411,7 @@ def run_decode(args, model, cpu_layers):
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
     ab = None if args.no_ab else interleaved_arms(args, mq, model, W, X, chain, eager)
+    lat = None if args.no_ab else host_step_latency(args, mq, model, W, X, chain, ab)
 
     roof, kernel_sum_ms = time_kernels(mq, model, eager, args.kernel_reps)
     roof["frac_of_stream_probe"] = round(roof["achieved"] / probe["GB_s"], 4)
@@ -374,6 +434,8 @@ def run_decode(args, model, cpu_layers):
            "roofline": roof}
     if ab:
         out["ab_interleaved"] = ab
+    if lat:
+        out["host_step_latency"] = lat
     chain.close()
     eager.close()
     del W

@@ -11,15 +11,17 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmq.so")
 
 MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_HIP, MQ_ERR_CAPTURE, MQ_ERR_NOMEM = 0, -1, -2, -3, -4, -5
-MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE, MQ_UNFUSED_GLUE = 1, 2, 4, 8
+MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE, MQ_UNFUSED_GLUE, MQ_LAZY_CAPTURE, MQ_HOST_LOGITS = 1, 2, 4, 8, 16, 32
 MQ_GRAPH, MQ_EAGER = 0, 1
-MQ_FAULT_NONE, MQ_FAULT_CAPTURE = 0, 1
+MQ_READ_PINNED, MQ_READ_PAGEABLE = 0, 1
+MQ_FAULT_NONE, MQ_FAULT_CAPTURE, MQ_FAULT_PINNED_ALLOC = 0, 1, 2
 
 Q4K_BLOCK_BYTES, Q8_BLOCK_BYTES = 144, 34
 
@@ -65,6 +67,12 @@ SIGNATURES = {
     "mq_decode_chain": ([_vp, _int, _vp], _int),
     "mq_chain_info": ([_vp, C.POINTER(_int), C.POINTER(_int), C.POINTER(_i64)], _int),
     "mq_chain_reset": ([_vp, _i64, _vp], _int),
+    "mq_chain_capture_stats": ([_vp, C.POINTER(_i64), C.POINTER(C.c_double)], _int),
+    "mq_chain_read_logits": ([_vp, _vp, _i64, _u32, _vp], _int),
+    "mq_chain_host_logits": ([_vp, C.POINTER(_vp)], _int),
+    "mq_read_to_host": ([_vp, _vp, _i64, _u32, _vp], _int),
+    "mq_readback_stats": ([C.POINTER(_i64), C.POINTER(_i64), C.POINTER(_i64), C.POINTER(_int)], _int),
+    "mq_readback_release": ([], _int),
     "mq_chain_trace_sizes": ([_vp, C.POINTER(_i64), C.POINTER(_i64)], _int),
     "mq_chain_read_trace": ([_vp, _vp, _vp, _vp], _int),
     "mq_chain_destroy": ([_vp], _int),
@@ -151,6 +159,39 @@ def mq_probe_stream_read(buf, xor_out=None, workgroups=0, stream=None):
     _check(lib().mq_probe_stream_read(_ptr(buf, what="buf"), nbytes, _ptr(xor_out, torch.int32, 4, "xor_out"),
                                       int(workgroups), _stream(stream)))
     return xor_out
+
+
+def _host_out(out, dtype, shape, nbytes, what="out"):
+    """A writable, C-contiguous numpy array of at least nbytes (new if None)."""
+    if out is None:
+        return np.empty(shape, dtype=dtype)
+    if not isinstance(out, np.ndarray) or not out.flags.c_contiguous or not out.flags.writeable:
+        raise TypeError(f"{what} must be a writable C-contiguous numpy array")
+    if out.nbytes < nbytes:
+        raise ValueError(f"{what} holds {out.nbytes} bytes, needs {nbytes}")
+    return out
+
+
+def mq_read_to_host(src, out=None, pageable=False, stream=None):
+    """Blocking copy of the device tensor src into host memory through the
+    library's pinned buffer (or pageable memory with pageable=True); returns
+    out, a numpy array shaped like src when the caller gives none."""
+    nbytes = src.numel() * src.element_size()
+    dtype = torch.empty(0, dtype=src.dtype).numpy().dtype
+    out = _host_out(out, dtype, tuple(src.shape), nbytes)
+    flags = MQ_READ_PAGEABLE if pageable else MQ_READ_PINNED
+    _check(lib().mq_read_to_host(_ptr(src, what="src"), out.ctypes.data, nbytes, flags, _stream(stream)))
+    return out
+
+
+def mq_readback_stats():
+    b, p, q, w = _i64(), _i64(), _i64(), _int()
+    _check(lib().mq_readback_stats(C.byref(b), C.byref(p), C.byref(q), C.byref(w)))
+    return {"pinned_bytes": b.value, "pinned_reads": p.value, "pageable_reads": q.value, "warned": bool(w.value)}
+
+
+def mq_readback_release():
+    _check(lib().mq_readback_release())
 
 
 def mq_quantize_q8_0(x, xq=None, stream=None):
@@ -252,6 +293,7 @@ class DecodeChain:
     def __init__(self, model, weights, x_table, logits=None, flags=0, stream=None):
         L = model.n_layers
         self.L = L
+        self.vocab = model.vocab
         self._keep = (weights, x_table)
         arr = lambda key: (_vp * L)(*[_ptr(weights[key][i], torch.uint8, what=key) for i in range(L)])
         self._arrays = [arr("qkv"), arr("o"), arr("gu"), arr("down")]
@@ -277,6 +319,29 @@ class DecodeChain:
 
     def reset(self, step=0, stream=None):
         _check(lib().mq_chain_reset(self.handle, step, _stream(stream)))
+
+    def capture_stats(self):
+        n, ms = _i64(), C.c_double()
+        _check(lib().mq_chain_capture_stats(self.handle, C.byref(n), C.byref(ms)))
+        return {"graph_steps": n.value, "capture_ms": ms.value}
+
+    def read_logits(self, out=None, pageable=False, stream=None):
+        """Blocking readback of the last step's logits into a numpy f32 [vocab]."""
+        vocab = self.vocab
+        out = _host_out(out, np.float32, (vocab,), 4 * vocab)
+        flags = MQ_READ_PAGEABLE if pageable else MQ_READ_PINNED
+        _check(lib().mq_chain_read_logits(self.handle, out.ctypes.data, vocab, flags, _stream(stream)))
+        return out
+
+    def host_logits(self):
+        """numpy f32 [vocab] view of the chain's pinned host logits (MQ_HOST_LOGITS),
+        or None.  It is overwritten by every step: synchronize before reading and
+        copy what must outlive the next step."""
+        p = _vp()
+        _check(lib().mq_chain_host_logits(self.handle, C.byref(p)))
+        if not p.value:
+            return None
+        return np.ctypeslib.as_array(C.cast(p, C.POINTER(C.c_float)), shape=(self.vocab,))
 
     def trace(self, stream=None):
         qb, fc = _i64(), _i64()

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <chrono>
 #include <functional>
 #include <mutex>
 #include <string>
@@ -134,6 +136,13 @@ struct mq_chain {
     uint8_t* q8_trace = nullptr;
     float* f32_trace = nullptr;
     int64_t q8_bytes = 0, f32_count = 0;
+    const float* logits = nullptr;    // decode step: device f32 [vocab]
+    int64_t vocab = 0;
+    float* host_logits = nullptr;     // MQ_HOST_LOGITS: pinned f32 [vocab], written by the step's last node
+    bool lazy = false;                // MQ_LAZY_CAPTURE: capture on the third MQ_GRAPH step
+    bool capture_tried = false;
+    int64_t graph_steps = 0;
+    double capture_ms = 0.0;
 };
 
 namespace {
@@ -152,7 +161,32 @@ void chain_free(mq_chain* c) {
     if (c->exec) (void)hipGraphExecDestroy(c->exec);
     if (c->graph) (void)hipGraphDestroy(c->graph);
     for (void* p : c->allocs) (void)hipFree(p);
+    if (c->host_logits) (void)hipHostFree(c->host_logits);
     delete c;
+}
+
+// MQ_HOST_LOGITS: pins the chain's host copy of the logits and appends the
+// copy to the step.  Failure to pin leaves the chain without it (one
+// warning per process).
+void add_host_logits(mq_chain* c) {
+    static bool warned = false;
+    void* p = nullptr;
+    const size_t bytes = (size_t)c->vocab * sizeof(float);
+    const hipError_t e = (g_fault & MQ_FAULT_PINNED_ALLOC) ? hipErrorOutOfMemory
+                                                          : hipHostMalloc(&p, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (!warned) {
+            warned = true;
+            fprintf(stderr, "mq: pinning the %zu-byte host logits of a chain failed (%s); the chain has no host copy\n",
+                    bytes, hipGetErrorString(e));
+        }
+        return;
+    }
+    c->host_logits = (float*)p;
+    float* host = c->host_logits;
+    const float* dev = c->logits;
+    c->ops.push_back([=](hipStream_t s) { return hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, s); });
 }
 
 int enqueue(mq_chain* c, hipStream_t s) {
@@ -171,15 +205,11 @@ int zero_counters(mq_chain* c, hipStream_t stream) {
     return hip_status(e, "counter reset");
 }
 
-int chain_finish(mq_chain* c, hipStream_t stream, bool eager_only) {
-    int rc = zero_counters(c, stream);
-    if (rc == MQ_OK) rc = enqueue(c, stream);
-    if (rc != MQ_OK) return rc;
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_status(e, "chain warm-up step");
-    if ((rc = zero_counters(c, stream)) != MQ_OK) return rc;
-    if (eager_only) return ok();
-
+// Records the chain's kernels on a private stream (nothing runs) and
+// instantiates the graph.  Failure leaves an eager chain and logs once.
+void try_capture(mq_chain* c) {
+    c->capture_tried = true;
+    const auto t0 = std::chrono::steady_clock::now();
     const char* why = nullptr;
     hipStream_t cs = nullptr;
     if (g_fault & MQ_FAULT_CAPTURE) {
@@ -212,9 +242,62 @@ int chain_finish(mq_chain* c, hipStream_t stream, bool eager_only) {
     }
     if (cs) (void)hipStreamDestroy(cs);
     (void)hipGetLastError();
+    c->capture_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (!c->captured)
         fprintf(stderr, "mq: decode-step graph capture failed (%s); this chain runs eagerly\n", why);
+}
+
+// Creation's last stage.  Eager-only chains and eager-capture chains run
+// one warm step (first launches load code objects and set kernel
+// attributes, which must not happen inside a capture) and reset the
+// counters; eager-capture chains then capture.  Lazy chains only reset the
+// counters: their first two steps run eagerly and warm them.
+int chain_finish(mq_chain* c, hipStream_t stream, unsigned flags) {
+    const bool eager_only = (flags & MQ_EAGER_ONLY) != 0;
+    c->lazy = !eager_only && (flags & MQ_LAZY_CAPTURE) != 0;
+    int rc = zero_counters(c, stream);
+    if (rc != MQ_OK || c->lazy) return rc;
+    if ((rc = enqueue(c, stream)) != MQ_OK) return rc;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "chain warm-up step");
+    if ((rc = zero_counters(c, stream)) != MQ_OK) return rc;
+    if (!eager_only) try_capture(c);
     return ok();
+}
+
+// The process-wide pinned staging buffer of mq_read_to_host.
+struct PinnedReadback {
+    std::mutex mu;
+    void* buf = nullptr;
+    size_t bytes = 0;
+    int64_t pinned_reads = 0, pageable_reads = 0;
+    bool warned = false;
+};
+PinnedReadback g_rb;
+constexpr size_t kReadbackMinBytes = (size_t)4 << 20;
+
+// Makes g_rb.buf hold at least `bytes`; false if pinning failed (warned once).
+bool readback_reserve(size_t bytes) {
+    if (g_rb.buf && g_rb.bytes >= bytes) return true;
+    if (g_rb.buf) (void)hipHostFree(g_rb.buf);
+    g_rb.buf = nullptr;
+    g_rb.bytes = 0;
+    const size_t want = std::max(bytes, kReadbackMinBytes);
+    void* p = nullptr;
+    const hipError_t e = (g_fault & MQ_FAULT_PINNED_ALLOC) ? hipErrorOutOfMemory
+                                                          : hipHostMalloc(&p, want, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (!g_rb.warned) {
+            g_rb.warned = true;
+            fprintf(stderr, "mq: pinning a %zu-byte readback buffer failed (%s); reading back through pageable memory\n",
+                    want, hipGetErrorString(e));
+        }
+        return false;
+    }
+    g_rb.buf = p;
+    g_rb.bytes = want;
+    return true;
 }
 
 }  // namespace
@@ -239,6 +322,48 @@ int mq_probe_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int wo
     CHECK_ARG(bytes >= 0 && bytes % 16 == 0, "bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
     CHECK_ARG(workgroups <= 65536, "workgroups=%d out of range", workgroups);
     return hip_status(launch_stream_read(p, bytes, xor_out, workgroups, stream), "stream probe launch");
+}
+
+int mq_read_to_host(const void* src, void* host_dst, int64_t bytes, unsigned flags, hipStream_t stream) {
+    CHECK_ARG((flags & ~(unsigned)MQ_READ_PAGEABLE) == 0, "unknown flags %#x", flags);
+    CHECK_ARG(bytes >= 0, "bytes=%lld must be >= 0", (long long)bytes);
+    CHECK_ARG(bytes == 0 || (src && host_dst), "null pointer (src=%p host_dst=%p)", src, host_dst);
+    if (capturing(stream)) return fail(MQ_ERR_CAPTURE, "a blocking readback cannot run inside a stream capture");
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "waiting for the stream before the readback");
+    if (bytes == 0) return ok();
+    std::lock_guard<std::mutex> lock(g_rb.mu);
+    if (!(flags & MQ_READ_PAGEABLE) && readback_reserve((size_t)bytes)) {
+        e = hipMemcpyAsync(g_rb.buf, src, (size_t)bytes, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_status(e, "pinned readback copy");
+        memcpy(host_dst, g_rb.buf, (size_t)bytes);
+        ++g_rb.pinned_reads;
+        return ok();
+    }
+    e = hipMemcpyAsync(host_dst, src, (size_t)bytes, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "pageable readback copy");
+    ++g_rb.pageable_reads;
+    return ok();
+}
+
+int mq_readback_stats(int64_t* pinned_bytes, int64_t* pinned_reads, int64_t* pageable_reads, int* warned) {
+    std::lock_guard<std::mutex> lock(g_rb.mu);
+    if (pinned_bytes) *pinned_bytes = (int64_t)g_rb.bytes;
+    if (pinned_reads) *pinned_reads = g_rb.pinned_reads;
+    if (pageable_reads) *pageable_reads = g_rb.pageable_reads;
+    if (warned) *warned = g_rb.warned ? 1 : 0;
+    return ok();
+}
+
+int mq_readback_release(void) {
+    std::lock_guard<std::mutex> lock(g_rb.mu);
+    hipError_t e = hipSuccess;
+    if (g_rb.buf) e = hipHostFree(g_rb.buf);
+    g_rb.buf = nullptr;
+    g_rb.bytes = 0;
+    return hip_status(e, "freeing the pinned readback buffer");
 }
 
 int mq_test_set_fault(unsigned fault_mask) {
@@ -357,6 +482,8 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
 
     mq_chain* c = new mq_chain();
     c->kind = 0;
+    c->logits = d->logits;
+    c->vocab = d->vocab;
     const int L = d->n_layers;
     const int64_t H = d->hidden, I = d->inter, QKV = d->qkv_rows;
     const int64_t qH = H / 32 * kQ8Bytes, qI = I / 32 * kQ8Bytes;
@@ -414,8 +541,9 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         const float* hl = h_prev;
         c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(hl, qz, H, eps, nullptr, 1, step, s); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0(wlm, qz, logits, nullptr, V, H, s); });
+        if (d->flags & MQ_HOST_LOGITS) add_host_logits(c);
         if (!keep) c->q8_bytes = c->f32_count = 0;
-        rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
+        rc = chain_finish(c, stream, d->flags);
         if (rc != MQ_OK) { chain_free(c); return rc; }
         *out = c;
         return ok();
@@ -443,9 +571,10 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const int64_t V = d->vocab;
     const NormIn nz{h_prev, nullptr, 1, eps, keep ? qz : nullptr, step, exact};
     c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0_norm(wlm, nz, logits, V, H, s); });
+    if (d->flags & MQ_HOST_LOGITS) add_host_logits(c);
     if (!keep) c->q8_bytes = c->f32_count = 0;
 
-    rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
+    rc = chain_finish(c, stream, d->flags);
     if (rc != MQ_OK) { chain_free(c); return rc; }
     *out = c;
     return ok();
@@ -502,7 +631,7 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
                                            nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, step, s);
         });
     }
-    rc = chain_finish(c, stream, (d->flags & MQ_EAGER_ONLY) != 0);
+    rc = chain_finish(c, stream, d->flags);
     if (rc != MQ_OK) { chain_free(c); return rc; }
     *out = c;
     return ok();
@@ -511,6 +640,10 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
 static int chain_step(mq_chain* c, int mode, hipStream_t stream) {
     CHECK_ARG(c, "null chain");
     CHECK_ARG(mode == MQ_GRAPH || mode == MQ_EAGER, "mode must be MQ_GRAPH or MQ_EAGER");
+    if (mode == MQ_GRAPH && !capturing(stream)) {
+        ++c->graph_steps;
+        if (c->lazy && !c->capture_tried && c->graph_steps >= 3) try_capture(c);
+    }
     if (mode == MQ_GRAPH && c->captured) return hip_status(hipGraphLaunch(c->exec, stream), "hipGraphLaunch");
     return enqueue(c, stream);
 }
@@ -534,6 +667,27 @@ int mq_chain_info(const mq_chain* c, int* captured, int* n_nodes, int64_t* step)
         if (e == hipSuccess) e = hipMemcpy(step, c->step, sizeof(int64_t), hipMemcpyDeviceToHost);
         if (e != hipSuccess) return hip_status(e, "reading the step counter");
     }
+    return ok();
+}
+
+int mq_chain_capture_stats(const mq_chain* c, int64_t* graph_steps, double* capture_ms) {
+    CHECK_ARG(c, "null chain");
+    if (graph_steps) *graph_steps = c->graph_steps;
+    if (capture_ms) *capture_ms = c->capture_ms;
+    return ok();
+}
+
+int mq_chain_read_logits(const mq_chain* c, float* host_out, int64_t n, unsigned flags, hipStream_t stream) {
+    CHECK_ARG(c && host_out, "null chain or host_out");
+    CHECK_ARG(c->kind == 0, "not a decode-step chain");
+    CHECK_SHAPE(n == c->vocab, "n=%lld must equal the chain's vocab %lld", (long long)n, (long long)c->vocab);
+    return mq_read_to_host(c->logits, host_out, n * (int64_t)sizeof(float), flags, stream);
+}
+
+int mq_chain_host_logits(const mq_chain* c, const float** host_logits) {
+    CHECK_ARG(c && host_logits, "null chain or out-param");
+    CHECK_ARG(c->kind == 0, "not a decode-step chain");
+    *host_logits = c->host_logits;
     return ok();
 }
 

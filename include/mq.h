@@ -185,7 +185,22 @@ typedef struct mq_chain mq_chain;
  * GEMVs read q8_0 inputs, 8 kernels per layer plus 2.  Its RMSNorm sums the
  * squares in another order, so codes can differ from the fused step's by
  * one near a rounding tie; each stage still meets the oracle's bounds. */
-enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u, MQ_UNFUSED_GLUE = 8u };
+/* MQ_LAZY_CAPTURE is the capture policy of '07 · R3' §2: capture costs a
+ * one-time host bill (recording plus instantiation, milliseconds) that only
+ * repeated use pays back, so the chain is created without a warm step and
+ * without a graph, its first two MQ_GRAPH steps run eagerly, and the third
+ * captures the step and replays it from then on.  A chain used once or twice
+ * never pays for a capture.  Without the flag the chain warms and captures
+ * at creation. */
+/* MQ_HOST_LOGITS ends the step with a copy of the logits into a pinned host
+ * buffer that the chain owns (4*vocab bytes, allocated at creation), so the
+ * readback is a node of the captured step instead of a separate blocking
+ * copy, and the caller reads the values in place (mq_chain_host_logits) with
+ * no host-side copy: a host copy that follows a DMA reads cold memory and
+ * costs more than the DMA.  If pinning fails the chain is created without
+ * the copy (mq_chain_host_logits gives NULL) and one warning is printed. */
+enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u, MQ_UNFUSED_GLUE = 8u,
+       MQ_LAZY_CAPTURE = 16u, MQ_HOST_LOGITS = 32u };
 enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
 
 typedef struct {
@@ -200,15 +215,17 @@ typedef struct {
     int n_inputs;                      /* >= 1 */
     float* logits;                     /* device f32 [vocab] */
     float eps;
-    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE | MQ_UNFUSED_GLUE */
+    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE | MQ_UNFUSED_GLUE
+                                          | MQ_LAZY_CAPTURE | MQ_HOST_LOGITS */
 } mq_chain_desc;
 
 /* Validates, allocates every device buffer the step needs (nothing is
  * allocated later: allocation inside a capture is illegal — Lecture 08,
  * §3), runs one eager warm step on `stream` and synchronizes it, resets the
  * step counter to 0, then captures the step into a hipGraph on a private
- * stream.  A capture failure is not an error: it is logged once to stderr
- * and the chain runs eagerly (captured = 0).  Weight, table and logits
+ * stream (with MQ_LAZY_CAPTURE: only resets the counter; see above).  A
+ * capture failure is not an error: it is logged once to stderr and the
+ * chain runs eagerly (captured = 0).  Weight, table and logits
  * pointers are baked into the chain: keep them alive and unmoved until
  * mq_chain_destroy.  *out receives the chain (host object owned by the
  * library). */
@@ -216,11 +233,29 @@ int mq_chain_create(const mq_chain_desc* desc, hipStream_t stream, mq_chain** ou
 /* One decode step on `stream`: MQ_GRAPH replays the graph (falls back to
  * eager launches when not captured), MQ_EAGER launches the same kernels with
  * the same arguments one by one.  The two are byte-identical by
- * construction. */
+ * construction.  Under MQ_LAZY_CAPTURE the third MQ_GRAPH call captures
+ * first (on a private stream; the capture records and runs nothing), then
+ * replays; a MQ_GRAPH call made while `stream` is itself being captured
+ * neither counts nor captures. */
 int mq_decode_chain(mq_chain* c, int mode, hipStream_t stream);
 /* Host out-params (any may be NULL): whether a graph exists, its node count,
  * and the device step counter (this call synchronizes the chain's copy). */
 int mq_chain_info(const mq_chain* c, int* captured, int* n_nodes, int64_t* step);
+/* Host out-params of the capture policy (any may be NULL): the number of
+ * MQ_GRAPH steps issued so far and the host wall time, in milliseconds, that
+ * recording and instantiating the graph took (0 if it was never captured). */
+int mq_chain_capture_stats(const mq_chain* c, int64_t* graph_steps, double* capture_ms);
+/* Blocking read of the last step's logits into HOST memory: f32 [n], n must
+ * equal the chain's vocab (MQ_ERR_SHAPE otherwise).  Goes through
+ * mq_read_to_host with the same flags. */
+int mq_chain_read_logits(const mq_chain* c, float* host_out, int64_t n, unsigned flags, hipStream_t stream);
+/* *host_logits receives the chain's pinned host copy of the logits, f32
+ * [vocab] (NULL if the chain was created without MQ_HOST_LOGITS or pinning
+ * failed).  The library owns it until mq_chain_destroy.  It holds the
+ * logits of the last step that has completed: synchronize the stream the
+ * step ran on before reading, and do not read it while a step is in flight
+ * (that step's copy overwrites it). */
+int mq_chain_host_logits(const mq_chain* c, const float** host_logits);
 /* Set the device step counter (enqueued on `stream`, capture-safe kernel). */
 int mq_chain_reset(mq_chain* c, int64_t step, hipStream_t stream);
 /* With MQ_KEEP_INTERMEDIATES: copy the last step's intermediates into the
@@ -261,7 +296,7 @@ typedef struct {
     const float* x_table;              /* device [n_tokens][hidden], 16-byte aligned */
     float* y_table;                    /* device [n_tokens][hidden] */
     int n_tokens;
-    unsigned flags;                    /* MQ_EAGER_ONLY */
+    unsigned flags;                    /* MQ_EAGER_ONLY | MQ_LAZY_CAPTURE */
     int tokens_per_launch;             /* tokens per mq_moe_step call, 1..256 (0 means 1) */
 } mq_moe_desc;
 
@@ -304,11 +339,43 @@ int mq_probe_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int wo
                          hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Device-to-host readback through a pinned staging buffer ('07 · R3', §2 and
+ * §3.1).  A copy into pageable host memory makes the driver bounce it
+ * through a pinned buffer of its own (two hops); a copy into memory pinned
+ * once and kept skips that, and handing the result to the caller is then a
+ * plain host memcpy.
+ * mq_read_to_host waits for all work queued on `stream` (the caller wants
+ * the value now), copies `bytes` from the device pointer src into the
+ * library's pinned buffer, and copies that into host_dst (any host memory,
+ * owned by the caller).  The pinned buffer is process-wide, guarded by a
+ * mutex, allocated on first use with max(bytes, 4 MiB) (head room so that
+ * small changes of size do not reallocate) and reallocated only to grow.
+ * If pinning fails the read goes through pageable memory instead and one
+ * warning is printed to stderr for the life of the process.  Flag
+ * MQ_READ_PAGEABLE skips the pinned buffer (the comparison arm).
+ * Errors: MQ_ERR_ARG (null pointer, bytes < 0, unknown flag),
+ * MQ_ERR_CAPTURE (stream is being captured: a blocking read cannot be
+ * recorded), MQ_ERR_HIP (the wait or the copy failed).  bytes == 0 only
+ * waits for the stream. */
+enum { MQ_READ_PINNED = 0u, MQ_READ_PAGEABLE = 1u };
+int mq_read_to_host(const void* src, void* host_dst, int64_t bytes, unsigned flags, hipStream_t stream);
+/* Host out-params (any may be NULL): size of the pinned buffer (0 if none),
+ * reads served through it, reads served through pageable memory (by flag
+ * or fallback), and whether the fallback warning has been printed. */
+int mq_readback_stats(int64_t* pinned_bytes, int64_t* pinned_reads, int64_t* pageable_reads, int* warned);
+/* Frees the pinned buffer; the next pinned read allocates it again.  Safe
+ * to call at any time from the host (no read holds the buffer after it
+ * returns). */
+int mq_readback_release(void);
+
+/* ---------------------------------------------------------------------------
  * Test hook, never read from the environment (environment variables are
  * process-global and leak across tests — '07 · R3', §3.3).
  * MQ_FAULT_CAPTURE makes the next chain creations behave as if graph
- * capture failed, to exercise the eager fallback. */
-enum { MQ_FAULT_NONE = 0u, MQ_FAULT_CAPTURE = 1u };
+ * capture failed, to exercise the eager fallback.  MQ_FAULT_PINNED_ALLOC
+ * makes the pinned readback buffer's allocation fail (without trying it),
+ * to exercise the pageable fallback and its one warning. */
+enum { MQ_FAULT_NONE = 0u, MQ_FAULT_CAPTURE = 1u, MQ_FAULT_PINNED_ALLOC = 2u };
 int mq_test_set_fault(unsigned fault_mask);
 
 #ifdef __cplusplus

@@ -68,6 +68,22 @@ def test_stream_probe_argument_errors(mq):
     assert L.mq_probe_stream_read(FAKE, 64, FAKE, 70000, None) == mq.MQ_ERR_ARG              # workgroups
 
 
+def test_readback_argument_errors(mq):
+    L = mq.lib()
+    buf = (C.c_uint8 * 64)()
+    assert L.mq_read_to_host(FAKE, buf, 64, 4, None) == mq.MQ_ERR_ARG              # unknown flag
+    assert "flags" in L.mq_last_error().decode()
+    assert L.mq_read_to_host(FAKE, buf, -1, 0, None) == mq.MQ_ERR_ARG              # negative size
+    assert L.mq_read_to_host(None, buf, 64, 0, None) == mq.MQ_ERR_ARG              # null source
+    assert L.mq_read_to_host(FAKE, None, 64, mq.MQ_READ_PAGEABLE, None) == mq.MQ_ERR_ARG
+    assert L.mq_chain_read_logits(None, C.cast(buf, C.c_void_p), 16, 0, None) == mq.MQ_ERR_ARG
+    assert L.mq_chain_capture_stats(None, None, None) == mq.MQ_ERR_ARG
+    assert L.mq_chain_host_logits(None, C.byref(C.c_void_p())) == mq.MQ_ERR_ARG
+    # no pinned buffer exists before the first read; releasing none is fine
+    assert L.mq_readback_release() == mq.MQ_OK
+    assert mq.mq_readback_stats() == {"pinned_bytes": 0, "pinned_reads": 0, "pageable_reads": 0, "warned": False}
+
+
 def test_grouped_argument_errors(mq):
     L = mq.lib()
     # combine without y_out

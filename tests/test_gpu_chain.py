@@ -169,6 +169,76 @@ def test_capture_failure_falls_back_to_eager(mq, small_model):
         assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), f"fallback differs at step {i}"
 
 
+def test_lazy_capture_on_third_graph_step(mq, small_model):
+    """The capture policy of '07 · R3' §2: no graph at creation or after two
+    MQ_GRAPH steps, capture at the third, replays after; every step is
+    byte-identical to an eager-only chain on the same inputs, and an
+    eager-only chain never captures however often it is stepped."""
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    lazy = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_LAZY_CAPTURE)
+    eager = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_EAGER_ONLY)
+    assert not lazy.info()["captured"]
+    assert lazy.capture_stats() == {"graph_steps": 0, "capture_ms": 0.0}
+    for i in range(8):
+        u = to_host(lazy.step(mq.MQ_GRAPH)).copy()
+        v = to_host(eager.step(mq.MQ_GRAPH)).copy()
+        assert _same(u, v), f"lazy chain differs from the eager one at step {i}"
+        assert lazy.info()["captured"] == (i >= 2), f"step {i}"
+    st = lazy.capture_stats()
+    assert st["graph_steps"] == 8 and st["capture_ms"] > 0
+    info = lazy.info()
+    assert info["n_nodes"] == 4 * model.n_layers + 1 and info["step"] == 8
+    assert not eager.info()["captured"] and eager.capture_stats()["capture_ms"] == 0.0
+    log(f"lazy capture took {st['capture_ms']:.2f} ms")
+    # without the flag the chain pays for its capture at creation
+    assert mq.DecodeChain(model, Wd, xd).capture_stats()["capture_ms"] > 0
+
+
+def test_read_logits_pinned_and_pageable(mq, small_model):
+    model, W, Wd, X = small_model
+    g = mq.DecodeChain(model, Wd, to_dev(X))
+    for i in range(3):
+        ref = to_host(g.step()).copy()
+        assert _same(g.read_logits(), ref), f"pinned readback, step {i}"
+        assert _same(g.read_logits(pageable=True), ref), f"pageable readback, step {i}"
+    out = np.empty(model.vocab, np.float32)
+    assert g.read_logits(out=out) is out
+    assert mq.lib().mq_chain_read_logits(g.handle, out.ctypes.data, model.vocab - 1, 0, None) == mq.MQ_ERR_SHAPE
+
+
+def test_host_logits_copy_in_the_graph(mq, small_model):
+    """MQ_HOST_LOGITS: the step's last node copies the logits into the chain's
+    pinned buffer.  The buffer is poisoned before every step, so each check
+    proves that step's copy ran; graph and eager steps alike, byte-identical
+    to an eager-only chain."""
+    import torch
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    h = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_HOST_LOGITS)
+    e = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_EAGER_ONLY)
+    info = h.info()
+    assert info["captured"] and info["n_nodes"] == 4 * model.n_layers + 2
+    view = h.host_logits()
+    assert view is not None and view.shape == (model.vocab,)
+    for i in range(8):
+        view[:] = np.nan
+        dev_logits = h.step(mq.MQ_EAGER if i == 5 else mq.MQ_GRAPH)
+        torch.cuda.synchronize()
+        ref = to_host(e.step(mq.MQ_EAGER)).copy()
+        assert _same(view, ref), f"host copy differs at step {i}"
+        assert _same(to_host(dev_logits), ref), f"device logits differ at step {i}"
+    # pinning failure: no host copy and no copy node; the chain still steps
+    mq.mq_test_set_fault(mq.MQ_FAULT_PINNED_ALLOC)
+    try:
+        f = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_HOST_LOGITS)
+    finally:
+        mq.mq_test_set_fault(mq.MQ_FAULT_NONE)
+    assert f.host_logits() is None and f.info()["n_nodes"] == 4 * model.n_layers + 1
+    e.reset(0)
+    assert _same(to_host(f.step()).copy(), to_host(e.step(mq.MQ_EAGER)).copy())
+
+
 def _chain_vs_oracle(mq, o, pool, model, n_layers, n_inputs=2, flags=0):
     from block_quantized_gemv_amd import synth
     m = dataclasses.replace(model, n_layers=n_layers)
@@ -269,3 +339,10 @@ def test_moe_chain(mq, o):
         m4.step(mq.MQ_GRAPH)
     assert m4.info()["step"] == T
     assert np.array_equal(to_host(m4.y_table).view(np.uint32), yg.view(np.uint32)), "4 tokens per launch != 1"
+    # lazy capture: the third step captures, the bytes do not change
+    lz = mq.MoEChain(*args, flags=mq.MQ_LAZY_CAPTURE, tokens_per_launch=4)
+    for i in range(T // 4):
+        assert not lz.info()["captured"], f"captured before step {i + 1}"
+        lz.step(mq.MQ_GRAPH)
+    assert lz.info()["captured"] and lz.info()["step"] == T
+    assert np.array_equal(to_host(lz.y_table).view(np.uint32), yg.view(np.uint32)), "lazy capture changed the bytes"
