@@ -321,7 +321,7 @@ def interleaved_arms(args, mq, model, W, X, chain, eager):
     return ab
 
 
-def host_step_latency(args, mq, model, W, X, chain, ab):
+def host_step_latency(args, mq, model, W, X, chain):
     import torch
     # End-to-end step latency as a caller sees it: launch the step, wait for
     # it, read the logits into host memory.  Arms interleaved step by step:
@@ -374,8 +374,6 @@ def host_step_latency(args, mq, model, W, X, chain, ab):
     res["lazy_capture_ms_at_third_step"] = round(lazy.capture_stats()["capture_ms"], 3)
     res["lazy_captured"] = bool(lazy.info()["captured"])
     lazy.close()
-    if ab and ab["eager_ms"] > ab["graph_ms"]:
-        res["capture_break_even_steps"] = round(res["capture_ms_at_create"] / (ab["eager_ms"] - ab["graph_ms"]), 1)
     log(f"host step latency: {res}")
     return res
 
@@ -411,7 +409,7 @@ def run_decode(args, model, cpu_layers):
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
     ab = None if args.no_ab else interleaved_arms(args, mq, model, W, X, chain, eager)
-    lat = None if args.no_ab else host_step_latency(args, mq, model, W, X, chain, ab)
+    lat = None if args.no_ab else host_step_latency(args, mq, model, W, X, chain)
 
     roof, kernel_sum_ms = time_kernels(mq, model, eager, args.kernel_reps)
     roof["frac_of_stream_probe"] = round(roof["achieved"] / probe["GB_s"], 4)
