@@ -19,6 +19,8 @@ Distributions (the synthetic stand-in for trained weights):
   module knowing the packing; likewise every nibble is uniform 0..15.
 * q8_0 weight block (34 B): f16 ``d`` uniform in [1e-4, 1e-3], then 32 int8
   values uniform in -127..127.
+* q4_0 weight block (18 B): f16 ``d`` uniform in [1e-4, 1e-3], then 16
+  uniform random bytes (32 uniform nibbles).
 * activations: N(0, 1) drawn in f64 and rounded to f32.
 * routing: ``n_sel`` distinct expert ids drawn uniformly without
   replacement, and N(0, 1) router logits.
@@ -30,6 +32,7 @@ import numpy as np
 Q4K_BLOCK_BYTES = 144   # bytes per q4_K super-block of 256 weights
 Q4K_BLOCK_VALUES = 256
 Q8_BLOCK_BYTES = 34     # bytes per q8_0 block of 32 values
+Q4_0_BLOCK_BYTES = 18   # bytes per q4_0 block of 32 weights
 Q8_BLOCK_VALUES = 32
 
 # Tensor keys: the first element says what the tensor is.
@@ -75,6 +78,17 @@ def q8_0_matrix(seed: int, key: tuple, m: int, k: int) -> np.ndarray:
     out[:, :, 0:2] = d.view(np.uint8).reshape(m, nb, 2)
     out[:, :, 2:] = q.view(np.uint8)
     return out.reshape(m, nb * Q8_BLOCK_BYTES)
+
+
+def q4_0_matrix(seed: int, key: tuple, m: int, k: int) -> np.ndarray:
+    """``m`` rows of k/32 q4_0 blocks, uint8 ``[m, (k/32)*18]``."""
+    assert k % Q8_BLOCK_VALUES == 0
+    nb = k // Q8_BLOCK_VALUES
+    g = rng(seed, *key)
+    raw = np.frombuffer(g.bytes(m * nb * Q4_0_BLOCK_BYTES), dtype=np.uint8)
+    out = raw.reshape(m, nb, Q4_0_BLOCK_BYTES).copy()
+    out[:, :, 0:2] = _uniform_f16(g, (m, nb)).view(np.uint8).reshape(m, nb, 2)
+    return out.reshape(m, nb * Q4_0_BLOCK_BYTES)
 
 
 def normal_f32(seed: int, key: tuple, shape) -> np.ndarray:

@@ -28,7 +28,18 @@ class ChainDesc(C.Structure):
                 ("inter", C.c_int64), ("vocab", C.c_int64),
                 ("w_qkv", C.POINTER(_u8p)), ("w_o", C.POINTER(_u8p)),
                 ("w_gu", C.POINTER(_u8p)), ("w_down", C.POINTER(_u8p)),
-                ("w_lm", _u8p), ("eps", C.c_float)]
+                ("w_lm", _u8p), ("eps", C.c_float), ("weight_format", C.c_int)]
+
+
+OREF_Q4K, OREF_Q4_0 = 0, 1
+
+
+def weight_format_code(model) -> int:
+    """The oracle's code for a model's layer-weight format ("q4_K" or "q4_0")."""
+    fmt = getattr(model, "weight_format", "q4_K")
+    if fmt not in ("q4_K", "q4_0"):
+        raise ValueError(f"unknown weight format {fmt!r}")
+    return OREF_Q4_0 if fmt == "q4_0" else OREF_Q4K
 
 
 _SIGS = {
@@ -44,6 +55,10 @@ _SIGS = {
     "oref_gemv_q8_0_rows": [_u8p, _i64, _u8p, _i64p, _i64, _f32p, _f64p],
     "oref_isums_q4k": [_u8p, _i64, _i64, _u8p, _i32p, _i32p],
     "oref_isums_q8_0": [_u8p, _i64, _i64, _u8p, _i32p],
+    "oref_dequant_q4_0": [_u8p, _i64, _f64p],
+    "oref_gemv_q4_0": [_u8p, _i64, _i64, _u8p, _f32p, _f64p],
+    "oref_gemv_q4_0_rows": [_u8p, _i64, _u8p, _i64p, _i64, _f32p, _f64p],
+    "oref_isums_q4_0": [_u8p, _i64, _i64, _u8p, _i32p],
     "oref_rmsnorm": [_f32p, _i64, C.c_float, _f32p],
     "oref_swiglu": [_f32p, _i64, _f32p],
     "oref_softmax": [_f32p, _i64, _f32p],
@@ -139,7 +154,34 @@ class Oracle:
         self.lib.oref_dequant_q4k(_p(b, _u8p), n, _p(out, _f64p))
         return out
 
+    # q4_0
+    def dequant_q4_0(self, blocks: np.ndarray) -> np.ndarray:
+        b = _u8(blocks).ravel()
+        n = b.size // 18
+        out = np.empty(32 * n, np.float64)
+        self.lib.oref_dequant_q4_0(_p(b, _u8p), n, _p(out, _f64p))
+        return out
+
     # GEMV
+    def gemv_q4_0(self, w: np.ndarray, m: int, k: int, xq: np.ndarray, rows=None):
+        """Returns (y f32, s_abs f64) for all rows or the listed rows."""
+        w, xq = _u8(w), _u8(xq)
+        if rows is None:
+            y, sa = np.empty(m, np.float32), np.empty(m, np.float64)
+            self.lib.oref_gemv_q4_0(_p(w, _u8p), m, k, _p(xq, _u8p), _p(y, _f32p), _p(sa, _f64p))
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            y, sa = np.empty(rows.size, np.float32), np.empty(rows.size, np.float64)
+            self.lib.oref_gemv_q4_0_rows(_p(w, _u8p), k, _p(xq, _u8p), _p(rows, _i64p), rows.size,
+                                         _p(y, _f32p), _p(sa, _f64p))
+        return y, sa
+
+    def isums_q4_0(self, w, m, k, xq):
+        w, xq = _u8(w), _u8(xq)
+        isum = np.empty((m, k // 32), np.int32)
+        self.lib.oref_isums_q4_0(_p(w, _u8p), m, k, _p(xq, _u8p), _p(isum, _i32p))
+        return isum
+
     def gemv_q4k(self, w: np.ndarray, m: int, k: int, xq: np.ndarray, rows=None):
         """Returns (y f32, s_abs f64) for all rows or the listed rows."""
         w, xq = _u8(w), _u8(xq)
@@ -216,7 +258,7 @@ class Oracle:
         lm = _u8(weights["lm"])
         d = ChainDesc(L, model.hidden, model.qkv_rows, model.inter, model.vocab,
                       ptrs(weights["qkv"]), ptrs(weights["o"]), ptrs(weights["gu"]),
-                      ptrs(weights["down"]), _p(lm, _u8p), model.eps)
+                      ptrs(weights["down"]), _p(lm, _u8p), model.eps, weight_format_code(model))
         h0 = np.ascontiguousarray(h0, dtype=np.float32)
         logits = np.empty(model.vocab, np.float32)
         s_abs = np.empty(model.vocab, np.float64)

@@ -145,6 +145,22 @@ void oref_dequant_q4k(const uint8_t* sbs, int64_t nsb, double* w) {
     }
 }
 
+/* ---------------------------------------------------------------- q4_0 --- */
+
+/* Quants: 16 bytes; byte i holds weight i in its low nibble and weight 16+i
+ * in its high nibble. */
+static int q4_0_nibble(const uint8_t* qs, int i) {
+    return i < 16 ? (qs[i] & 0x0F) : (qs[i - 16] >> 4);
+}
+
+void oref_dequant_q4_0(const uint8_t* blocks, int64_t nblk, double* w) {
+    for (int64_t b = 0; b < nblk; ++b) {
+        const uint8_t* blk = blocks + 18 * b;
+        const double d = (double)oref_f16_to_f32(load_u16(blk));
+        for (int i = 0; i < 32; ++i) w[32 * b + i] = d * (double)(q4_0_nibble(blk + 2, i) - 8);
+    }
+}
+
 /* ---------------------------------------------------------------- GEMV --- */
 
 static void dot_row(const double* w, const double* x, int64_t k, float* y, double* s_abs) {
@@ -194,6 +210,24 @@ void oref_gemv_q8_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
     oref_gemv_q8_0_rows(w, k, xq, rows.data(), m, y, s_abs);
 }
 
+void oref_gemv_q4_0_rows(const uint8_t* w, int64_t k, const uint8_t* xq,
+                         const int64_t* rows, int64_t n_rows, float* y, double* s_abs) {
+    const int64_t nb = k / 32;
+    std::vector<double> x(k), wr(k);
+    oref_dequant_q8_0(xq, nb, x.data());
+    for (int64_t i = 0; i < n_rows; ++i) {
+        oref_dequant_q4_0(w + rows[i] * nb * 18, nb, wr.data());
+        dot_row(wr.data(), x.data(), k, &y[i], s_abs ? &s_abs[i] : nullptr);
+    }
+}
+
+void oref_gemv_q4_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
+                    float* y, double* s_abs) {
+    std::vector<int64_t> rows(m);
+    for (int64_t r = 0; r < m; ++r) rows[r] = r;
+    oref_gemv_q4_0_rows(w, k, xq, rows.data(), m, y, s_abs);
+}
+
 /* ---------------------------------------------------------- block sums --- */
 
 void oref_isums_q4k(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
@@ -226,6 +260,19 @@ void oref_isums_q8_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
             const uint8_t* wb = w + (r * nb + g) * 34;
             int32_t s = 0;
             for (int i = 0; i < 32; ++i) s += (int8_t)wb[2 + i] * (int8_t)xq[34 * g + 2 + i];
+            isum[r * nb + g] = s;
+        }
+    }
+}
+
+void oref_isums_q4_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
+                     int32_t* isum) {
+    const int64_t nb = k / 32;
+    for (int64_t r = 0; r < m; ++r) {
+        for (int64_t g = 0; g < nb; ++g) {
+            const uint8_t* blk = w + (r * nb + g) * 18;
+            int32_t s = 0;
+            for (int i = 0; i < 32; ++i) s += q4_0_nibble(blk + 2, i) * (int8_t)xq[34 * g + 2 + i];
             isum[r * nb + g] = s;
         }
     }
@@ -269,6 +316,8 @@ int64_t oref_chain_f32_trace_len(const oref_chain_desc* d) {
 void oref_chain(const oref_chain_desc* d, const float* h0, float* logits,
                 uint8_t* q8_trace, float* f32_trace, double* s_abs) {
     const int64_t H = d->hidden, I = d->inter;
+    void (*gemv)(const uint8_t*, int64_t, int64_t, const uint8_t*, float*, double*) =
+        d->weight_format == OREF_Q4_0 ? oref_gemv_q4_0 : oref_gemv_q4k;
     std::vector<float> h(h0, h0 + H), t(d->qkv_rows), o(H), gu(2 * I), nrm(I > H ? I : H);
     std::vector<uint8_t> q(I / 32 * 34 > H / 32 * 34 ? I / 32 * 34 : H / 32 * 34);
     uint8_t* q8t = q8_trace;
@@ -283,22 +332,22 @@ void oref_chain(const oref_chain_desc* d, const float* h0, float* logits,
         oref_rmsnorm(h.data(), H, d->eps, nrm.data());
         oref_quantize_q8_0(nrm.data(), H, q.data());
         keep_q8(H);
-        oref_gemv_q4k(d->w_qkv[l], d->qkv_rows, H, q.data(), t.data(), nullptr);
+        gemv(d->w_qkv[l], d->qkv_rows, H, q.data(), t.data(), nullptr);
 
         oref_rmsnorm(t.data(), H, d->eps, nrm.data());      /* first H outputs of QKV */
         oref_quantize_q8_0(nrm.data(), H, q.data());
         keep_q8(H);
-        oref_gemv_q4k(d->w_o[l], H, H, q.data(), o.data(), nullptr);
+        gemv(d->w_o[l], H, H, q.data(), o.data(), nullptr);
 
         oref_rmsnorm(o.data(), H, d->eps, nrm.data());
         oref_quantize_q8_0(nrm.data(), H, q.data());
         keep_q8(H);
-        oref_gemv_q4k(d->w_gu[l], 2 * I, H, q.data(), gu.data(), nullptr);
+        gemv(d->w_gu[l], 2 * I, H, q.data(), gu.data(), nullptr);
 
         oref_swiglu(gu.data(), I, nrm.data());
         oref_quantize_q8_0(nrm.data(), I, q.data());
         keep_q8(I);
-        oref_gemv_q4k(d->w_down[l], H, I, q.data(), h.data(), nullptr);
+        gemv(d->w_down[l], H, I, q.data(), h.data(), nullptr);
 
         keep_f32(t, d->qkv_rows);
         keep_f32(o, H);

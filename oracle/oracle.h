@@ -20,6 +20,11 @@
  *     weight = d*sc_j*q - dmin*m_j for sub-block j = index/32.
  *   q8_0 block, 32 values in 34 bytes: [0,2) f16 d, [2,34) int8 q[32];
  *     value = d*q.
+ *   q4_0 block, 32 weights in 18 bytes: [0,2) f16 d, [2,18) 16 bytes of
+ *     4-bit quants, byte i holding weight i in its low nibble and weight
+ *     16+i in its high nibble; weight = d*(q - 8).  Rows hold k/32 blocks.
+ *     The pages measure a 0.5B model in this format ('07 · R3', §5) without
+ *     laying it out; this is the plain reading of the name.
  * The pages name both formats (the MMVQ "dp4a x q8_0" decode kernel that
  * gave q4_K +37%, '07 · R3 — Small-model per-token overhead', §1) but do
  * not lay them out; the layout above is the synthetic workload's.
@@ -54,6 +59,10 @@ void oref_q4k_scale_min(const uint8_t* s12, int j, int* sc, int* m);
 /* Dequantize nsb super-blocks into 256*nsb f64 weights. */
 void oref_dequant_q4k(const uint8_t* sbs, int64_t nsb, double* w);
 
+/* --- q4_0 ---------------------------------------------------------------- */
+/* Dequantize nblk blocks into 32*nblk f64 weights. */
+void oref_dequant_q4_0(const uint8_t* blocks, int64_t nblk, double* w);
+
 /* --- GEMV: dequantize, then dot in f64, ascending index -------------------
  * Rows are stored in ceil(k/256) super-blocks; only the first k weights of
  * a row take part (k % 32 == 0).  xq holds k/32 q8_0 blocks.
@@ -68,6 +77,11 @@ void oref_gemv_q8_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
                     float* y, double* s_abs);
 void oref_gemv_q8_0_rows(const uint8_t* w, int64_t k, const uint8_t* xq,
                          const int64_t* rows, int64_t n_rows, float* y, double* s_abs);
+/* q4_0 weights: row r holds k/32 blocks of 18 bytes. */
+void oref_gemv_q4_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
+                    float* y, double* s_abs);
+void oref_gemv_q4_0_rows(const uint8_t* w, int64_t k, const uint8_t* xq,
+                         const int64_t* rows, int64_t n_rows, float* y, double* s_abs);
 
 /* --- integer block sums ---------------------------------------------------
  * isum[r*(k/32)+g] = sum over the 32 values of block g of q4*q8 (q4 = the
@@ -76,6 +90,9 @@ void oref_isums_q4k(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
                     int32_t* isum, int32_t* ysum);
 /* isum[r*(k/32)+g] = sum over block g of w8*x8. */
 void oref_isums_q8_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
+                     int32_t* isum);
+/* isum[r*(k/32)+g] = sum over block g of q4*q8 (q4 = the stored nibble 0..15). */
+void oref_isums_q4_0(const uint8_t* w, int64_t m, int64_t k, const uint8_t* xq,
                      int32_t* isum);
 
 /* --- elementwise stand-ins between GEMVs ------------------------------------ */
@@ -95,7 +112,8 @@ void oref_softmax(const float* logits, int64_t n, float* p);
  *             c = Q8(RMSNorm(o));        gu = W_gu   c   (2*inter: gate rows, then up rows)
  *             g = Q8(SwiGLU(gu));        h  = W_down g   (H)
  * Final:      z = Q8(RMSNorm(h));        logits = W_lm z (q8_0 weights, vocab rows)
- * Weight pointers are host arrays of n_layers host pointers.
+ * The four layer GEMVs take q4_K weights, or q4_0 with weight_format
+ * OREF_Q4_0.  Weight pointers are host arrays of n_layers host pointers.
  * Optional traces (NULL to skip):
  *   q8_trace: per layer the Q8 bytes of a, b, c, g, then z at the end;
  *   f32_trace: per layer t, o, gu, h.
@@ -109,7 +127,9 @@ typedef struct {
     const uint8_t* const* w_down;
     const uint8_t* w_lm;
     float eps;
+    int weight_format;      /* OREF_Q4K or OREF_Q4_0 */
 } oref_chain_desc;
+enum { OREF_Q4K = 0, OREF_Q4_0 = 1 };
 
 int64_t oref_chain_q8_trace_bytes(const oref_chain_desc* d);
 int64_t oref_chain_f32_trace_len(const oref_chain_desc* d);

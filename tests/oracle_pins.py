@@ -15,7 +15,8 @@ import os
 
 import numpy as np
 
-from qhelpers import RandomQ4K, RandomQ8, f16_value, make_q8, make_sb, pack_scales, sb_values
+from qhelpers import (RandomQ4_0, RandomQ4K, RandomQ8, f16_value, make_q4_0, make_q8, make_sb, pack_scales,
+                      q4_0_values, sb_values)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -245,6 +246,81 @@ def pin_isums(o):
     assert np.array_equal(i2[0], y2), "all-ones nibbles: isum != ysum"
 
 
+# ------------------------------------------------------------- q4_0 ----
+
+def pin_q4_0_golden(o):
+    """The hand-worked q4_0 block."""
+    lines = dict(ln.split(":", 1) for ln in _golden_lines("q4_0_gemv_worked.txt"))
+    blk = np.array([int(t, 16) for t in lines["block"].split()], np.uint8)
+    q = np.array([int(t) for t in lines["act_q"].split()], np.int64)
+    xq = np.frombuffer(np.uint16(int(lines["act_d_bits"], 16)).tobytes() + q.astype(np.int8).tobytes(), np.uint8)
+    y, sa = o.gemv_q4_0(blk, 1, 32, xq)
+    assert float(y[0]) == float(lines["y"]) and float(sa[0]) == float(lines["s_abs"]), f"worked example: {y} {sa}"
+    assert int(o.isums_q4_0(blk, 1, 32, xq)[0, 0]) == int(lines["isum"]), "worked example isum"
+
+
+def pin_q4_0_isolation(o):
+    """One quant away from 8 (weight 0) at each of the 32 positions: the
+    decoded block is zero except d*(q - 8) there (pins which nibble of which
+    byte holds each weight, and the offset)."""
+    for i in range(32):
+        q = np.full(32, 8, np.int64)
+        q[i] = (i * 5) % 16 if (i * 5) % 16 != 8 else 3
+        w = o.dequant_q4_0(np.frombuffer(make_q4_0(0.5, q), np.uint8))
+        want = np.zeros(32)
+        want[i] = 0.5 * (q[i] - 8)
+        assert np.array_equal(w, want), f"q4_0 isolation at weight {i}"
+
+
+def pin_q4_0_values(o):
+    """Dequantized weights equal the values the test built the blocks from."""
+    g = np.random.default_rng(47)
+    W = RandomQ4_0(g, 3, 256)
+    assert np.array_equal(o.dequant_q4_0(W.bytes), W.values.ravel()), "q4_0 dequant != built values"
+
+
+def pin_q4_0_closed_forms(o):
+    """All quants 8: every weight is 0, so y = 0 and S_abs = 0 exactly.  All
+    quants 0: w = -8d, so y_r = -8 * sum_b d_b * sum_{i in b} x_i."""
+    g = np.random.default_rng(53)
+    X = RandomQ8(g, 320)
+    W8 = RandomQ4_0(g, 4, 320, q_fill=8)
+    y, sa = o.gemv_q4_0(W8.bytes, 4, 320, X.bytes)
+    assert np.all(y == 0) and np.all(sa == 0), "all-8 quants"
+    W0 = RandomQ4_0(g, 5, 320, q_fill=0)
+    y, sa = o.gemv_q4_0(W0.bytes, 5, 320, X.bytes)
+    d = np.vectorize(f16_value)(W0.d)
+    want = -8.0 * (d * X.values.reshape(10, 32).sum(axis=1)[None]).sum(axis=1)
+    assert np.all(np.abs(y - want) <= 1e-9 * sa + np.abs(want) * 2.0 ** -23), "all-0 quants closed form"
+
+
+def pin_q4_0_gemv_bruteforce(o):
+    """Exact-rounded (fsum) brute force on tiny shapes; row sampling."""
+    g = np.random.default_rng(59)
+    for m, k in [(1, 32), (2, 64), (3, 256), (17, 96), (4, 512)]:
+        W, X = RandomQ4_0(g, m, k), RandomQ8(g, k)
+        y, sa = o.gemv_q4_0(W.bytes, m, k, X.bytes)
+        yr, sar = _fsum_gemv(W.values, X.values, k)
+        for r in range(m):
+            assert abs(float(y[r]) - yr[r]) <= _ulp32(yr[r]), f"q4_0 gemv {m}x{k} row {r}: {y[r]} vs {yr[r]}"
+        assert np.allclose(sa, sar, rtol=1e-12), "q4_0 s_abs"
+        rows = np.array([m - 1, 0], np.int64)
+        y2, _ = o.gemv_q4_0(W.bytes, m, k, X.bytes, rows=rows)
+        assert np.array_equal(y2, y[rows]), "row-sampled q4_0 gemv differs"
+
+
+def pin_q4_0_isums(o):
+    """Integer block sums against an integer brute force over the test's own
+    nibbles and codes; all quants 8 give 8 times the activation sums."""
+    g = np.random.default_rng(61)
+    W, X = RandomQ4_0(g, 3, 256), RandomQ8(g, 256)
+    isum = o.isums_q4_0(W.bytes, 3, 256, X.bytes)
+    q8 = X.q.reshape(8, 32)
+    assert np.array_equal(isum, (W.q * q8[None]).sum(axis=2)), "q4_0 isum brute force"
+    W8 = RandomQ4_0(g, 1, 256, q_fill=8)
+    assert np.array_equal(o.isums_q4_0(W8.bytes, 1, 256, X.bytes)[0], 8 * q8.sum(axis=1)), "all-8 isum"
+
+
 # ----------------------------------------------------- q8_0 weights (lm) ----
 
 def pin_q8_gemv(o):
@@ -354,6 +430,32 @@ def pin_chain_structure(o):
     assert np.array_equal(out["logits"], logits), "chain logits != composition"
     assert np.array_equal(out["s_abs"], sa), "chain s_abs"
     assert np.array_equal(out["q8_trace"], np.concatenate(q8s)), "chain q8 trace"
+
+
+class _TinyModelQ4_0(_TinyModel):
+    weight_format = "q4_0"
+
+
+def pin_chain_structure_q4_0(o):
+    """With q4_0 layer weights the step is the same composition, every layer
+    GEMV taken with the q4_0 product."""
+    g = np.random.default_rng(67)
+    model = _TinyModelQ4_0(2)
+    H, I, L = model.hidden, model.inter, 2
+    W = {"qkv": [RandomQ4_0(g, model.qkv_rows, H).bytes for _ in range(L)],
+         "o": [RandomQ4_0(g, H, H).bytes for _ in range(L)],
+         "gu": [RandomQ4_0(g, 2 * I, H).bytes for _ in range(L)],
+         "down": [RandomQ4_0(g, H, I).bytes for _ in range(L)],
+         "lm": np.stack([RandomQ8(g, H).bytes for _ in range(model.vocab)])}
+    h = g.standard_normal(H).astype(np.float32)
+    out = o.chain(model, W, h, traces=True)
+    for l in range(L):
+        t, _ = o.gemv_q4_0(W["qkv"][l], model.qkv_rows, H, o.quantize_q8_0(o.rmsnorm(h, model.eps)))
+        ov, _ = o.gemv_q4_0(W["o"][l], H, H, o.quantize_q8_0(o.rmsnorm(t[:H], model.eps)))
+        gu, _ = o.gemv_q4_0(W["gu"][l], 2 * I, H, o.quantize_q8_0(o.rmsnorm(ov, model.eps)))
+        h, _ = o.gemv_q4_0(W["down"][l], H, I, o.quantize_q8_0(o.swiglu(gu)))
+    logits, _ = o.gemv_q8_0(W["lm"], model.vocab, H, o.quantize_q8_0(o.rmsnorm(h, model.eps)))
+    assert np.array_equal(out["logits"], logits), "q4_0 chain logits != composition"
 
 
 # ------------------------------------------------------- routed experts ----

@@ -53,6 +53,18 @@ def sb_values(d: float, dmin: float, sc, m, q) -> np.ndarray:
     return d * np.asarray(sc, np.float64)[j] * np.asarray(q, np.float64) - dmin * np.asarray(m, np.float64)[j]
 
 
+def make_q4_0(d: float, q) -> bytes:
+    """One 18-byte q4_0 block from d and 32 nibbles: byte i = q_i | q_{16+i} << 4."""
+    q = np.asarray(q, np.int64)
+    qs = bytes(int(q[i] & 15) | (int(q[16 + i] & 15) << 4) for i in range(16))
+    return f16_bytes(d) + qs
+
+
+def q4_0_values(d: float, q) -> np.ndarray:
+    """The 32 weights of make_q4_0(...) in f64: d*(q - 8)."""
+    return f16_value(d) * (np.asarray(q, np.float64) - 8.0)
+
+
 def make_q8(d: float, q) -> bytes:
     """One 34-byte q8_0 block."""
     return f16_bytes(d) + np.asarray(q, np.int8).tobytes()
@@ -93,3 +105,21 @@ class RandomQ8:
         self.q = rng.integers(-127, 128, (nb, 32)) if q is None else np.asarray(q).reshape(nb, 32)
         self.bytes = np.frombuffer(b"".join(make_q8(self.d[b], self.q[b]) for b in range(nb)), np.uint8)
         self.values = np.concatenate([q8_values(self.d[b], self.q[b]) for b in range(nb)])
+
+
+class RandomQ4_0:
+    """A random q4_0 matrix with its known scales, nibbles and weights."""
+
+    def __init__(self, rng: np.random.Generator, m: int, k: int, q_fill=None):
+        nb = k // 32
+        self.m, self.k, self.nb = m, k, nb
+        self.d = rng.uniform(1e-4, 1e-3, (m, nb))
+        self.q = rng.integers(0, 16, (m, nb, 32)) if q_fill is None else np.full((m, nb, 32), q_fill, np.int64)
+        blob = bytearray()
+        vals = np.empty((m, k))
+        for r in range(m):
+            for b in range(nb):
+                blob += make_q4_0(self.d[r, b], self.q[r, b])
+                vals[r, 32 * b:32 * (b + 1)] = q4_0_values(self.d[r, b], self.q[r, b])
+        self.bytes = np.frombuffer(bytes(blob), np.uint8).reshape(m, nb * 18)
+        self.values = vals                       # [m, k] f64

@@ -81,8 +81,26 @@ MUTATIONS = [
      "oref_rmsnorm(t.data(), H, d->eps, nrm.data());      /* first H outputs of QKV */",
      "oref_rmsnorm(t.data() + (d->qkv_rows - H), H, d->eps, nrm.data());"),
     ("chain layer output not carried",
-     "oref_gemv_q4k(d->w_down[l], H, I, q.data(), h.data(), nullptr);",
-     "oref_gemv_q4k(d->w_down[l], H, I, q.data(), o.data(), nullptr);"),
+     "gemv(d->w_down[l], H, I, q.data(), h.data(), nullptr);",
+     "gemv(d->w_down[l], H, I, q.data(), o.data(), nullptr);"),
+    ("q4_0 nibble halves swapped",
+     "return i < 16 ? (qs[i] & 0x0F) : (qs[i - 16] >> 4);", "return i < 16 ? (qs[i] >> 4) : (qs[i - 16] & 0x0F);"),
+    ("q4_0 nibbles interleaved by byte",
+     "return i < 16 ? (qs[i] & 0x0F) : (qs[i - 16] >> 4);", "return (qs[i / 2] >> (4 * (i & 1))) & 0x0F;"),
+    ("q4_0 offset 7",
+     "w[32 * b + i] = d * (double)(q4_0_nibble(blk + 2, i) - 8);",
+     "w[32 * b + i] = d * (double)(q4_0_nibble(blk + 2, i) - 7);"),
+    ("q4_0 block stride without the scale",
+     "const uint8_t* blk = blocks + 18 * b;", "const uint8_t* blk = blocks + 16 * b;"),
+    ("q4_0 row stride of q8_0 blocks",
+     "oref_dequant_q4_0(w + rows[i] * nb * 18, nb, wr.data());",
+     "oref_dequant_q4_0(w + rows[i] * nb * 34, nb, wr.data());"),
+    ("q4_0 isum with the offset applied",
+     "s += q4_0_nibble(blk + 2, i) * (int8_t)xq[34 * g + 2 + i];",
+     "s += (q4_0_nibble(blk + 2, i) - 8) * (int8_t)xq[34 * g + 2 + i];"),
+    ("chain ignores the q4_0 weight format",
+     "d->weight_format == OREF_Q4_0 ? oref_gemv_q4_0 : oref_gemv_q4k;",
+     "d->weight_format == OREF_Q4K ? oref_gemv_q4_0 : oref_gemv_q4k;"),
     ("moe combine in reverse slot weights",
      "acc += (double)c[s] * (double)ys[(size_t)s * hidden + r];",
      "acc += (double)c[n_sel - 1 - s] * (double)ys[(size_t)s * hidden + r];"),
