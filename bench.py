@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="7b", choices=["7b", "05b", "single", "batched", "moe"])
+    p.add_argument("--workload", default="7b", choices=["7b", "05b", "05b_q4_0", "single", "batched", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ab", action="store_true", help="skip the interleaved A/B arms (for counter runs)")
     p.add_argument("--kernel-reps", type=int, default=3, help="passes of the dominant-kernel timing region")
@@ -74,9 +74,10 @@ def upload_model(model, dev, keep_host=False):
     W = {"qkv": [], "o": [], "gu": [], "down": []}
     H = {"qkv": [], "o": [], "gu": [], "down": []} if keep_host else None
     shapes = model.layer_shapes()
+    mat = synth.q4_0_matrix if model.weight_format == "q4_0" else synth.q4k_matrix
     for l in range(model.n_layers):
         for key, kind, (m, k) in zip(("qkv", "o", "gu", "down"), range(4), shapes):
-            a = synth.q4k_matrix(s, (synth.KEY_LAYER, l, kind), m, k)
+            a = mat(s, (synth.KEY_LAYER, l, kind), m, k)
             W[key].append(torch.from_numpy(a).to(dev))
             if keep_host:
                 H[key].append(a)
@@ -154,13 +155,15 @@ def gemv_kinds(model):
     prologue, q8_0 otherwise) + output written (f32, or q8_0 after SwiGLU)."""
     from block_quantized_gemv_amd import workloads as wl
     H, I, Q = model.hidden, model.inter, model.qkv_rows
-    norm = "mq::k_gemv_q4k<1,false,2>"
+    wb = model.layer_matrix_bytes
+    f = 1 if model.weight_format == "q4_0" else 0      # the kernels' format template argument
+    norm = f"mq::k_gemv_q4k<{f},1,false,2>"
     kinds = []
     for _ in range(model.n_layers):
-        kinds += [("qkv", norm, wl.q4k_bytes(Q, H) + 4 * H + 4 * Q),
-                  ("o", norm, wl.q4k_bytes(H, H) + 4 * H + 4 * H),
-                  ("gate/up", "mq::k_gemv_q4k_swiglu<true>", wl.q4k_bytes(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
-                  ("down", "mq::k_gemv_q4k<1,false,1>", wl.q4k_bytes(H, I) + wl.q8_bytes(1, I) + 4 * H)]
+        kinds += [("qkv", norm, wb(Q, H) + 4 * H + 4 * Q),
+                  ("o", norm, wb(H, H) + 4 * H + 4 * H),
+                  ("gate/up", f"mq::k_gemv_q4k_swiglu<{f},true>", wb(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
+                  ("down", f"mq::k_gemv_q4k<{f},1,false,1>", wb(H, I) + wl.q8_bytes(1, I) + 4 * H)]
     kinds.append(("lm_head", "mq::k_gemv_q8_0<false,true>", wl.q8_bytes(model.vocab, H) + 4 * H + 4 * model.vocab))
     return kinds
 
@@ -204,7 +207,8 @@ def time_kernels(mq, model, eager_chain, reps):
     layer = [by_kind[k] for k in ("qkv", "o", "gate/up", "down") if k in by_kind]
     agg_b = sum(d["bytes"] * len(d["us"]) for d in layer)
     agg_us = sum(sum(d["us"]) for d in layer)
-    aggregate = {"what": "byte-weighted aggregate of the per-layer q4_K GEMVs (QKV, O, gate/up, down)",
+    aggregate = {"what": f"byte-weighted aggregate of the per-layer {model.weight_format} GEMVs "
+                         "(QKV, O, gate/up, down)",
                  "GB_s": round(agg_b / agg_us / 1e3, 1), "frac": round(agg_b / agg_us / 1e3 / HBM_PEAK_GBS, 4)}
     return {"bound": "hbm", "kernel": dominant, "launches": dk["n"], "bytes_per_launch": round(avg_b),
             "us_per_launch": round(avg_us, 3), "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -256,19 +260,21 @@ def cpu_baseline_decode(model, host_w, n_layers_sample):
         os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     except (AttributeError, OSError):
         pass
+    gemv = o.gemv_q4_0 if model.weight_format == "q4_0" else o.gemv_q4k
     t0 = time.perf_counter()
     nbytes = 0
     for l in range(n_layers_sample):
         qkv, ow, gu, dn = (host_w[k][l] for k in ("qkv", "o", "gu", "down"))
         a = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel()
-        t, _ = o.gemv_q4k(qkv, model.qkv_rows, H, a)
+        t, _ = gemv(qkv, model.qkv_rows, H, a)
         b = o.quantize_q8_0(o.rmsnorm(t[:H], eps)).ravel()
-        ov, _ = o.gemv_q4k(ow, H, H, b)
+        ov, _ = gemv(ow, H, H, b)
         c = o.quantize_q8_0(o.rmsnorm(ov, eps)).ravel()
-        g_u, _ = o.gemv_q4k(gu, 2 * I, H, c)
+        g_u, _ = gemv(gu, 2 * I, H, c)
         g = o.quantize_q8_0(o.swiglu(g_u)).ravel()
-        h, _ = o.gemv_q4k(dn, H, I, g)
-        nbytes += sum(workloads.q4k_bytes(m, k) + workloads.q8_bytes(1, k) + 4 * m for m, k in model.layer_shapes())
+        h, _ = gemv(dn, H, I, g)
+        nbytes += sum(model.layer_matrix_bytes(m, k) + workloads.q8_bytes(1, k) + 4 * m
+                      for m, k in model.layer_shapes())
     z = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel()
     o.gemv_q8_0(lm, lm_rows, H, z)
     nbytes += workloads.q8_bytes(lm_rows, H) + workloads.q8_bytes(1, H) + 4 * lm_rows
@@ -423,7 +429,7 @@ def run_decode(args, model, cpu_layers):
            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
            "config": {"workload": model.name, "hidden": model.hidden, "layers": model.n_layers,
                       "qkv_rows": model.qkv_rows, "inter": model.inter, "vocab": model.vocab, "n": 1,
-                      "seed": model.seed, "weights": "q4_K (lm_head q8_0)", "graph": bool(info["captured"]),
+                      "seed": model.seed, "weights": f"{model.weight_format} (lm_head q8_0)", "graph": bool(info["captured"]),
                       "graph_nodes": info["n_nodes"], "bytes_per_step": nbytes},
            "tok_per_s": round(1e3 / ms, 2), "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
            "pct_of_stream_probe": round(100 * value / probe["GB_s"], 2), "stream_probe": probe,
@@ -617,6 +623,8 @@ def main():
         out = run_decode(args, workloads.DECODE_7B, cpu_layers=workloads.DECODE_7B.n_layers)
     elif args.workload == "05b":
         out = run_decode(args, workloads.DECODE_05B, cpu_layers=workloads.DECODE_05B.n_layers)
+    elif args.workload == "05b_q4_0":
+        out = run_decode(args, workloads.DECODE_05B_Q4_0, cpu_layers=workloads.DECODE_05B_Q4_0.n_layers)
     elif args.workload == "single":
         out = run_single(args)
     elif args.workload == "batched":

@@ -21,9 +21,10 @@ MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_HIP, MQ_ERR_CAPTURE, MQ_ERR_NOMEM = 0, -
 MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE, MQ_UNFUSED_GLUE, MQ_LAZY_CAPTURE, MQ_HOST_LOGITS = 1, 2, 4, 8, 16, 32
 MQ_GRAPH, MQ_EAGER = 0, 1
 MQ_READ_PINNED, MQ_READ_PAGEABLE = 0, 1
+MQ_FMT_Q4_K, MQ_FMT_Q4_0 = 0, 1
 MQ_FAULT_NONE, MQ_FAULT_CAPTURE, MQ_FAULT_PINNED_ALLOC = 0, 1, 2
 
-Q4K_BLOCK_BYTES, Q8_BLOCK_BYTES = 144, 34
+Q4K_BLOCK_BYTES, Q8_BLOCK_BYTES, Q4_0_BLOCK_BYTES = 144, 34, 18
 
 
 class MQError(RuntimeError):
@@ -40,7 +41,7 @@ class ChainDesc(C.Structure):
                 ("inter", C.c_int64), ("vocab", C.c_int64),
                 ("w_qkv", C.POINTER(_vp)), ("w_o", C.POINTER(_vp)), ("w_gu", C.POINTER(_vp)),
                 ("w_down", C.POINTER(_vp)), ("w_lm", _vp), ("x_table", _vp), ("n_inputs", C.c_int),
-                ("logits", _vp), ("eps", C.c_float), ("flags", C.c_uint)]
+                ("logits", _vp), ("eps", C.c_float), ("flags", C.c_uint), ("weight_format", C.c_int)]
 
 
 class MoEDesc(C.Structure):
@@ -59,6 +60,9 @@ SIGNATURES = {
     "mq_gemv_q4k_q8_batched": ([_vp, _vp, _vp, _i64, _i64, _int, _vp], _int),
     "mq_gemv_q4k_grouped": ([_vp, _i64, _int, _vp, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp], _int),
     "mq_gemv_q8_0_q8": ([_vp, _vp, _vp, _i64, _i64, _vp], _int),
+    "mq_gemv_q4_0_q8": ([_vp, _vp, _vp, _i64, _i64, _vp], _int),
+    "mq_gemv_q4_0_q8_batched": ([_vp, _vp, _vp, _i64, _i64, _int, _vp], _int),
+    "mq_debug_gemv_q4_0_q8_isums": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp], _int),
     "mq_rmsnorm_quantize_q8_0": ([_vp, _vp, _i64, _f32, _vp], _int),
     "mq_swiglu_quantize_q8_0": ([_vp, _vp, _i64, _int, _i64, _vp], _int),
     "mq_debug_gemv_q4k_q8_isums": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp], _int),
@@ -131,6 +135,10 @@ def q4k_bytes(m, k):
 
 def q8_bytes(n, k):
     return n * (k // 32) * Q8_BLOCK_BYTES
+
+
+def q4_0_bytes(m, k):
+    return m * (k // 32) * Q4_0_BLOCK_BYTES
 
 
 def version() -> str:
@@ -222,6 +230,24 @@ def mq_gemv_q4k_q8_batched(w, xq, m, k, n, y=None, stream=None):
     return y
 
 
+def mq_gemv_q4_0_q8(w, xq, m, k, y=None, stream=None):
+    if y is None:
+        y = torch.empty(m, dtype=torch.float32, device=w.device)
+    _check(lib().mq_gemv_q4_0_q8(_ptr(w, torch.uint8, q4_0_bytes(m, k), "w"),
+                                 _ptr(xq, torch.uint8, q8_bytes(1, k), "xq"),
+                                 _ptr(y, torch.float32, 4 * m, "y"), m, k, _stream(stream)))
+    return y
+
+
+def mq_gemv_q4_0_q8_batched(w, xq, m, k, n, y=None, stream=None):
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check(lib().mq_gemv_q4_0_q8_batched(_ptr(w, torch.uint8, q4_0_bytes(m, k), "w"),
+                                         _ptr(xq, torch.uint8, q8_bytes(n, k), "xq"),
+                                         _ptr(y, torch.float32, 4 * m * n, "y"), m, k, n, _stream(stream)))
+    return y
+
+
 def mq_gemv_q4k_grouped(w_all, expert_bytes, n_experts, ids, xq, xq_stride_bytes, m, k, y=None,
                         combine=None, y_out=None, want_y=True, stream=None):
     n_sel = ids.numel()
@@ -277,6 +303,17 @@ def mq_debug_gemv_q4k_q8_isums(w, xq, m, k, stream=None):
     return y, isum, ysum
 
 
+def mq_debug_gemv_q4_0_q8_isums(w, xq, m, k, stream=None):
+    dev = w.device
+    y = torch.empty(m, dtype=torch.float32, device=dev)
+    isum = torch.empty((m, k // 32), dtype=torch.int32, device=dev)
+    ysum = torch.empty(k // 32, dtype=torch.int32, device=dev)
+    _check(lib().mq_debug_gemv_q4_0_q8_isums(_ptr(w, torch.uint8, q4_0_bytes(m, k), "w"),
+                                             _ptr(xq, torch.uint8, q8_bytes(1, k), "xq"), _ptr(y), _ptr(isum),
+                                             _ptr(ysum), m, k, _stream(stream)))
+    return y, isum, ysum
+
+
 def mq_debug_gemv_q8_0_q8_isums(w, xq, m, k, stream=None):
     dev = w.device
     y = torch.empty(m, dtype=torch.float32, device=dev)
@@ -300,10 +337,14 @@ class DecodeChain:
         self.logits = logits if logits is not None else torch.empty(model.vocab, dtype=torch.float32,
                                                                      device=x_table.device)
         n_inputs = x_table.shape[0]
+        fmt = getattr(model, "weight_format", "q4_K")
+        if fmt not in ("q4_K", "q4_0"):
+            raise ValueError(f"unknown weight format {fmt!r}")
         d = ChainDesc(L, model.hidden, model.qkv_rows, model.inter, model.vocab, *self._arrays,
                       _ptr(weights["lm"], torch.uint8, q8_bytes(model.vocab, model.hidden), "lm"),
                       _ptr(x_table, torch.float32, 4 * n_inputs * model.hidden, "x_table"), n_inputs,
-                      _ptr(self.logits, torch.float32, 4 * model.vocab, "logits"), model.eps, flags)
+                      _ptr(self.logits, torch.float32, 4 * model.vocab, "logits"), model.eps, flags,
+                      MQ_FMT_Q4_0 if fmt == "q4_0" else MQ_FMT_Q4_K)
         h = _vp()
         _check(lib().mq_chain_create(C.byref(d), _stream(stream), C.byref(h)))
         self.handle = h

@@ -103,20 +103,27 @@ int workspace(size_t need, hipStream_t stream, void** out) {
     return MQ_OK;
 }
 
-// Chooses full staging or split-k for a q4_K GEMV with ncols columns.
-int run_q4k(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t m, int64_t k, int ncols,
-            hipStream_t stream) {
+// Chooses full staging or split-k for a 4-bit GEMV with ncols columns
+// (the debug dump runs with full staging only).
+int run_q4(int fmt, const void* w, const void* xq, int64_t col_bytes, float* y, int32_t* isum, int32_t* ysum,
+           int64_t m, int64_t k, int ncols, hipStream_t stream) {
     const int lds = ncols * stage_bytes((int)(k / 32));
     if (lds <= kMaxStageLds)
-        return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, nullptr, nullptr, m, k, ncols, stream),
-                          "q4_K GEMV launch");
+        return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, isum, ysum, m, k, ncols, stream, fmt),
+                          "4-bit GEMV launch");
+    if (isum) return fail(MQ_ERR_SHAPE, "k too large for the dump kernel");
     if (ncols * kStageGroupBytes > kMaxStageLds) return fail(MQ_ERR_SHAPE, "too many columns");
     void* ws = nullptr;
     const size_t need = (size_t)gemv_q4k_splitk_nsplit(k) * (size_t)m * ncols * sizeof(double);
     int rc = workspace(need, stream, &ws);
     if (rc != MQ_OK) return rc;
-    return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)ws, m, k, ncols, stream),
-                      "q4_K split-k GEMV launch");
+    return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)ws, m, k, ncols, stream, fmt),
+                      "4-bit split-k GEMV launch");
+}
+
+int run_q4k(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t m, int64_t k, int ncols,
+            hipStream_t stream) {
+    return run_q4(kFmtQ4K, w, xq, col_bytes, y, nullptr, nullptr, m, k, ncols, stream);
 }
 
 }  // namespace
@@ -393,6 +400,28 @@ int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, i
     return run_q4k(w, xq, (k / 32) * kQ8Bytes, y, m, k, n, stream);
 }
 
+int mq_gemv_q4_0_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k, hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    return run_q4(kFmtQ4_0, w, xq, 0, y, nullptr, nullptr, m, k, 1, stream);
+}
+
+int mq_gemv_q4_0_q8_batched(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n,
+                            hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
+    return run_q4(kFmtQ4_0, w, xq, (k / 32) * kQ8Bytes, y, nullptr, nullptr, m, k, n, stream);
+}
+
+int mq_debug_gemv_q4_0_q8_isums(const void* w, const void* xq, float* y, int32_t* isum, int32_t* ysum,
+                                int64_t m, int64_t k, hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    CHECK_ARG(isum && aligned(isum, 4), "isum must be a non-null int32 buffer");
+    return run_q4(kFmtQ4_0, w, xq, 0, y, isum, ysum, m, k, 1, stream);
+}
+
 int mq_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts, const int32_t* ids,
                         int n_sel, const void* xq, int64_t xq_stride_bytes, float* y,
                         const float* combine, float* y_out, int64_t m, int64_t k, hipStream_t stream) {
@@ -472,6 +501,8 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
               "null pointer in the descriptor");
     CHECK_ARG(d->n_inputs >= 1, "n_inputs must be >= 1");
     CHECK_ARG(d->eps >= 0.0f, "eps must be >= 0");
+    CHECK_ARG(d->weight_format == MQ_FMT_Q4_K || d->weight_format == MQ_FMT_Q4_0, "unknown weight_format %d",
+              d->weight_format);
     CHECK_ARG(aligned(d->w_lm, 4) && aligned(d->x_table, 16) && aligned(d->logits, 4),
               "misaligned pointer (x_table must be 16-byte aligned)");
     for (int l = 0; l < d->n_layers; ++l)
@@ -489,6 +520,7 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const int64_t qH = H / 32 * kQ8Bytes, qI = I / 32 * kQ8Bytes;
     const bool keep = (d->flags & MQ_KEEP_INTERMEDIATES) != 0;
     const int exact = (d->flags & MQ_EXACT_GLUE) != 0;
+    const int fmt = d->weight_format == MQ_FMT_Q4_0 ? kFmtQ4_0 : kFmtQ4K;
     int rc = MQ_OK;
     c->step = (int64_t*)chain_alloc(c, sizeof(int64_t), &rc);
     // Q8 inputs of every GEMV and f32 outputs; with MQ_KEEP_INTERMEDIATES every
@@ -525,13 +557,13 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
             const int64_t* sel = l == 0 ? step : nullptr;
             const int nin = l == 0 ? n_inputs : 1;
             c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(xin, qa, H, eps, sel, nin, nullptr, s); });
-            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s, fmt); });
             c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, nullptr, s); });
-            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s, fmt); });
             c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, nullptr, s); });
-            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wg, qc, 0, gu, nullptr, nullptr, 2 * I, H, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wg, qc, 0, gu, nullptr, nullptr, 2 * I, H, 1, s, fmt); });
             c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, qg, I, 1, I, s); });
-            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s, fmt); });
             h_prev = h;
         }
         uint8_t* qz = c->q8_trace + (keep ? L * q8_layer : q8_layer);
@@ -559,10 +591,10 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
                                  : NormIn{h_prev, nullptr, 1, eps, keep ? qa : nullptr, nullptr, exact};
         const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr, exact};
         const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr, exact};
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s, fmt); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s, fmt); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s, fmt); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s, fmt); });
         h_prev = h;
     }
     uint8_t* qz = c->q8_trace + (keep ? L * q8_layer : q8_layer);

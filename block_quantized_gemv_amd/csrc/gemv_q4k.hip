@@ -139,6 +139,78 @@ __device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P,
 }
 
 // --------------------------------------------------------------------------
+// q4_0 weights in the same geometry.  Eight 18-byte q4_0 blocks (f16 d, then
+// 16 quant bytes: byte i holds weight i in its low nibble and weight 16+i in
+// its high nibble; weight = d*(q - 8)) fill the same 144 bytes and 256
+// weights as one q4_K super-block, so rows of k/256 such groups use the q4_K
+// lane layout unchanged.  Lane j takes blocks 2j and 2j+1 (bytes 36j..36j+35,
+// dword aligned), whose activation is staged pair 4*group + j as for q4_K.
+// The first block's quants start 2 bytes into a dword and are realigned
+// with v_alignbyte; the second block's are aligned.
+struct Q40Load {
+    u32x4 a, b;
+    uint32_t c;
+};
+
+__device__ __forceinline__ void load_group(const uint8_t* __restrict__ grp, int j, Q40Load& L) {
+    const uint8_t* p = grp + 36 * j;
+    L.a = *(const u32x4_a4*)p;
+    L.b = *(const u32x4_a4*)(p + 16);
+    L.c = *(const uint32_t*)(p + 32);
+}
+__device__ __forceinline__ void load_group(const uint8_t* __restrict__ grp, int j, SBLoad& L) {
+    load_sb(grp, 32 * j, L);
+}
+
+template <int FMT> struct GroupLoad { using type = SBLoad; };
+template <> struct GroupLoad<kFmtQ4_0> { using type = Q40Load; };
+
+template <int NC, bool DUMP>
+__device__ __forceinline__ void group_item(const SBLoad& L, const Lanes& ln, int P, bool valid,
+                                           const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
+                                           int32_t* __restrict__ dump, int64_t dump_row_off) {
+    sb_item<NC, DUMP>(L, ln, P, valid, lds, col_bytes, acc, dump, dump_row_off);
+}
+
+// d_a*(d8_0*isum_0 - 8*d8_0*ysum_0) + d_b*(d8_1*isum_1 - 8*d8_1*ysum_1) in
+// f64: d8*isum has < 28 significant bits and 8*d8*ysum shares its scale, so
+// each bracket is exact, and so is its product with the block's f16 d; only
+// the final addition rounds.
+template <int NC, bool DUMP>
+__device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, int P, bool valid,
+                                           const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
+                                           int32_t* __restrict__ dump, int64_t dump_row_off) {
+    const uint32_t dw[9] = {L.a.x, L.a.y, L.a.z, L.a.w, L.b.x, L.b.y, L.b.z, L.b.w, L.c};
+    uint32_t q0[4], q1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        q0[k] = __builtin_amdgcn_alignbyte(dw[k + 1], dw[k], 2);
+        q1[k] = dw[5 + k];
+    }
+    const double da = (double)f16_to_f32(dw[0]);
+    const double db = (double)f16_to_f32(dw[4] >> 16);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        StagedPair x;
+        read_pair(lds + c * col_bytes, P, x, true);
+        int i0 = 0, i1 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            i0 = dot4(q0[k] & 0x0F0F0F0Fu, x.c[k], i0);
+            i0 = dot4((q0[k] >> 4) & 0x0F0F0F0Fu, x.c[4 + k], i0);
+            i1 = dot4(q1[k] & 0x0F0F0F0Fu, x.c[8 + k], i1);
+            i1 = dot4((q1[k] >> 4) & 0x0F0F0F0Fu, x.c[12 + k], i1);
+        }
+        const double v = fma(da, fma(x.d0, (double)i0, -8.0 * x.ds0), db * fma(x.d1, (double)i1, -8.0 * x.ds1));
+        acc[c] += valid ? v : 0.0;
+        if (DUMP && valid) {
+            dump[dump_row_off + 2 * P] = i0;
+            dump[dump_row_off + 2 * P + 1] = i1;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
 // Full staging: all NC activation columns live in LDS.  Wave w owns tiles
 // w, w+W, w+2W, ... (W = waves in the grid); its items are (tile, pass) in
 // that order.  Where the activation comes from (SRC):
@@ -152,7 +224,7 @@ __device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P,
 // tiles to different workgroups, so that every CU gets the same share.
 constexpr int kSrcQ8 = 0, kSrcQ8Early = 1, kSrcNorm = 2;
 
-template <int NC, bool DUMP, int SRC>
+template <int FMT, int NC, bool DUMP, int SRC>
 __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
@@ -175,7 +247,7 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
     // whereas one fixed address for all waves would queue thousands of
     // requests on a single channel.
     struct Item {
-        SBLoad L;
+        typename GroupLoad<FMT>::type L;
         bool valid;
         int row, pass;
     };
@@ -189,7 +261,7 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
         const bool inb = n_items > 0 && it.row < M && sb < nsb;
         it.valid = inb && !past;
         if (past) it.row = M;
-        load_sb(inb ? w + (int64_t)(t * ln.R + ln.row_local) * row_bytes + sb * kQ4KBytes : w, 32 * ln.j, it.L);
+        load_group(inb ? w + (int64_t)(t * ln.R + ln.row_local) * row_bytes + sb * kQ4KBytes : w, ln.j, it.L);
     };
 
     // Early sources: the activation is requested first, then items 0 and
@@ -222,8 +294,8 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.0;
     stream_items<kEarly>(n_items, A, B, fetch, [&](const Item& it) {
-        sb_item<NC, DUMP>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
-                          (int64_t)it.row * nb);
+        group_item<NC, DUMP>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
+                             (int64_t)it.row * nb);
         if (it.pass != passes - 1) return;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -239,7 +311,7 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
 // (one staging group per activation column), rows in slots of 64 lanes; the
 // f64 partial of each (split, row, column) goes to `part` and a second kernel
 // sums the splits in order.
-template <int NC>
+template <int FMT, int NC>
 __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     double* __restrict__ part, int M, int nsb) {
@@ -259,12 +331,12 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
         row = wave + i * W;
         p = w + row * row_bytes + (lane_ok ? (sb0 + ln.g) * kQ4KBytes : 0);
     };
-    SBLoad A, B;
+    typename GroupLoad<FMT>::type A, B;
     const uint8_t* pa;
     int ra = 0;
     if (n_items > 0) {
         where(0, pa, ra);
-        load_sb(pa, 32 * ln.j, A);
+        load_group(pa, ln.j, A);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -272,11 +344,11 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
                  blockDim.x, nullptr);
     __syncthreads();
 
-    auto item = [&](const SBLoad& L, int row) {
+    auto item = [&](const typename GroupLoad<FMT>::type& L, int row) {
         double acc[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[c] = 0.0;
-        sb_item<NC, false>(L, ln, pair_of(ln, 0), lane_ok, lds, kStageGroupBytes, acc, nullptr, 0);
+        group_item<NC, false>(L, ln, pair_of(ln, 0), lane_ok, lds, kStageGroupBytes, acc, nullptr, 0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const double v = wave_sum_f64(acc[c]);
@@ -287,10 +359,10 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
         const uint8_t* pb;
         int rb;
         where(i + 1, pb, rb);
-        load_sb(pb, 32 * ln.j, B);
+        load_group(pb, ln.j, B);
         item(A, ra);
         where(i + 2, pa, ra);
-        load_sb(pa, 32 * ln.j, A);
+        load_group(pa, ln.j, A);
         if (i + 1 < n_items) item(B, rb);
     }
 }
@@ -409,7 +481,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
 // values are the ones the plain GEMV would write.  With NORM the input is
 // Q8(RMSNorm(x)) formed in the prologue (8 waves, so that fewer
 // workgroups repeat it); otherwise xq (4 waves).
-template <bool NORM>
+template <int FMT, bool NORM>
 __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* __restrict__ gu_out,
     uint8_t* __restrict__ g_q8, int inter, int nsb, NormIn nin) {
@@ -431,7 +503,7 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     // Items past the last re-read the last item's lines (see k_gemv_q4k)
     // and are not computed.
     struct Item {
-        SBLoad L;
+        typename GroupLoad<FMT>::type L;
         bool valid;
         int st, pass;
     };
@@ -443,7 +515,7 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
         const int sb = it.pass * ln.gpp + ln.g;
         const bool inb = sb < nsb;
         it.valid = inb && !past;
-        load_sb(inb ? w + row_of(it.st) * row_bytes + sb * kQ4KBytes : w, 32 * ln.j, it.L);
+        load_group(inb ? w + row_of(it.st) * row_bytes + sb * kQ4KBytes : w, ln.j, it.L);
     };
 
     float4 xr[kNormRegChunks];
@@ -465,7 +537,7 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
 
     double acc[1] = {0.0};
     stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
-        sb_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
+        group_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
         if (it.pass != passes - 1) return;
         const float v = (float)group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
@@ -631,7 +703,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
 
     double acc[1] = {0.0};
     stream_items<true>(n_items, A, B, fetch, [&](const Item& it) {
-        sb_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
+        group_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
         if (it.pass != passes - 1) return;
         const float v = (float)group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
@@ -753,15 +825,15 @@ static int balanced_grid(int64_t units, const void* fn, int lds) {
     return (int)(grid > 0 ? grid : 1);
 }
 
-template <int NC, bool DUMP>
+template <int FMT, int NC, bool DUMP>
 static hipError_t launch_nc(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                             int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int nsb,
                             hipStream_t stream) {
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = NC * stage_bytes(nsb * 8);
-    const void* fn = (const void*)k_gemv_q4k<NC, DUMP, kSrcQ8>;
-    MQ_LAUNCH((k_gemv_q4k<NC, DUMP, kSrcQ8>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds, stream,
-              (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, y, dump_isum, dump_ysum, (int)m, nsb,
+    const void* fn = (const void*)k_gemv_q4k<FMT, NC, DUMP, kSrcQ8>;
+    MQ_LAUNCH((k_gemv_q4k<FMT, NC, DUMP, kSrcQ8>), dim3(balanced_grid(p.n_tiles, fn, lds)), dim3(256), lds,
+              stream, (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, y, dump_isum, dump_ysum, (int)m, nsb,
               p.log2s, p.passes, p.n_tiles, NormIn{});
     return hipGetLastError();
 }
@@ -785,6 +857,7 @@ void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads, int
 }
 
 // One q8_0 column with early staging (see k_gemv_q4k).
+template <int FMT>
 static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64_t m, int nsb,
                                   hipStream_t stream) {
     const Q4KPlan p = plan_q4k(m, nsb);
@@ -795,56 +868,71 @@ static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64
     const int cap = (int)(want < kWavesQ8EarlyMin ? kWavesQ8EarlyMin : want > kWavesQ8EarlyMax ? kWavesQ8EarlyMax : want);
     int grid = 1, threads = 64;
     prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads, cap);
-    MQ_LAUNCH((k_gemv_q4k<1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
-              (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb, p.log2s,
-              p.passes, p.n_tiles, NormIn{});
+    MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream,
+              (const uint8_t*)w, (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m,
+              nsb, p.log2s, p.passes, p.n_tiles, NormIn{});
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
-                                hipStream_t stream) {
+template <int FMT>
+static hipError_t launch_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
+                              hipStream_t stream) {
     const int nsb = (int)(k / 256);
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
     int grid = 1, threads = 64;
     prologue_grid(p.n_tiles, k / 4, &grid, &threads, kWavesNorm);
-    MQ_LAUNCH((k_gemv_q4k<1, false, kSrcNorm>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
+    MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcNorm>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
               (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb,
               p.log2s, p.passes, p.n_tiles, nin);
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
-                           int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
-                           hipStream_t stream) {
-    const int nsb = (int)(k / 256);
-    if (dump_isum) return launch_nc<1, true>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, stream);
+hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
+                                hipStream_t stream, int fmt) {
+    return fmt == kFmtQ4_0 ? launch_norm<kFmtQ4_0>(w, nin, y, m, k, stream)
+                           : launch_norm<kFmtQ4K>(w, nin, y, m, k, stream);
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const void* w, const void* xq, int64_t xq_col_bytes, float* y, int32_t* dump_isum,
+                             int32_t* dump_ysum, int64_t m, int nsb, int ncols, hipStream_t stream) {
+    if (dump_isum) return launch_nc<FMT, 1, true>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, stream);
     switch (ncols) {
-        case 1: return launch_q8_early(w, xq, y, m, nsb, stream);
-        case 2: return launch_nc<2, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 3: return launch_nc<3, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 4: return launch_nc<4, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 5: return launch_nc<5, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 6: return launch_nc<6, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 7: return launch_nc<7, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 8: return launch_nc<8, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 1: return launch_q8_early<FMT>(w, xq, y, m, nsb, stream);
+        case 2: return launch_nc<FMT, 2, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 3: return launch_nc<FMT, 3, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 4: return launch_nc<FMT, 4, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 5: return launch_nc<FMT, 5, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 6: return launch_nc<FMT, 6, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 7: return launch_nc<FMT, 7, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 8: return launch_nc<FMT, 8, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
+                           int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
+                           hipStream_t stream, int fmt) {
+    const int nsb = (int)(k / 256);
+    return fmt == kFmtQ4_0
+               ? launch_fmt<kFmtQ4_0>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, ncols, stream)
+               : launch_fmt<kFmtQ4K>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, ncols, stream);
+}
+
 int gemv_q4k_splitk_nsplit(int64_t k) { return (int)((k / 256 + 15) / 16); }
 
-template <int NC>
+template <int FMT, int NC>
 static hipError_t launch_split_nc(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                                   double* part, int64_t m, int nsb, hipStream_t stream) {
     const int n_split = (nsb + 15) / 16;
     const int lds = NC * kStageGroupBytes;
-    const void* fn = (const void*)k_gemv_q4k_splitk<NC>;
+    const void* fn = (const void*)k_gemv_q4k_splitk<FMT, NC>;
     const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, lds) * 4 / n_split;
     const int64_t k = (m + (wmax > 0 ? wmax : 1) - 1) / (wmax > 0 ? wmax : 1);
     const int64_t waves = (m + k - 1) / k;
     const int gx = (int)((waves + 3) / 4);
-    MQ_LAUNCH((k_gemv_q4k_splitk<NC>), dim3(gx, n_split), dim3(256), lds, stream,
+    MQ_LAUNCH((k_gemv_q4k_splitk<FMT, NC>), dim3(gx, n_split), dim3(256), lds, stream,
                        (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, part, (int)m, nsb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -854,33 +942,47 @@ static hipError_t launch_split_nc(const void* w, const void* xq, int64_t xq_col_
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
-                                  double* part, int64_t m, int64_t k, int ncols, hipStream_t stream) {
-    const int nsb = (int)(k / 256);
+template <int FMT>
+static hipError_t launch_split_fmt(const void* w, const void* xq, int64_t xq_col_bytes, float* y, double* part,
+                                   int64_t m, int nsb, int ncols, hipStream_t stream) {
     switch (ncols) {
-        case 1: return launch_split_nc<1>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 2: return launch_split_nc<2>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 3: return launch_split_nc<3>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 4: return launch_split_nc<4>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 5: return launch_split_nc<5>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 6: return launch_split_nc<6>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 7: return launch_split_nc<7>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
-        case 8: return launch_split_nc<8>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 1: return launch_split_nc<FMT, 1>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 2: return launch_split_nc<FMT, 2>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 3: return launch_split_nc<FMT, 3>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 4: return launch_split_nc<FMT, 4>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 5: return launch_split_nc<FMT, 5>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 6: return launch_split_nc<FMT, 6>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 7: return launch_split_nc<FMT, 7>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 8: return launch_split_nc<FMT, 8>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                  int64_t inter, int64_t k, hipStream_t stream) {
+hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
+                                  double* part, int64_t m, int64_t k, int ncols, hipStream_t stream, int fmt) {
+    const int nsb = (int)(k / 256);
+    return fmt == kFmtQ4_0 ? launch_split_fmt<kFmtQ4_0>(w, xq, xq_col_bytes, y, part, m, nsb, ncols, stream)
+                           : launch_split_fmt<kFmtQ4K>(w, xq, xq_col_bytes, y, part, m, nsb, ncols, stream);
+}
+
+template <int FMT>
+static hipError_t launch_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
+                                int64_t inter, int64_t k, hipStream_t stream) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
     if (nin)
-        MQ_LAUNCH(k_gemv_q4k_swiglu<true>, dim3((unsigned)(inter / 32)), dim3(512), lds, stream,
+        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true>), dim3((unsigned)(inter / 32)), dim3(512), lds, stream,
                   (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin);
     else
-        MQ_LAUNCH(k_gemv_q4k_swiglu<false>, dim3((unsigned)(inter / 32)), dim3(256), lds, stream,
+        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, false>), dim3((unsigned)(inter / 32)), dim3(256), lds, stream,
                   (const uint8_t*)w, (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb, NormIn{});
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
+                                  int64_t inter, int64_t k, hipStream_t stream, int fmt) {
+    return fmt == kFmtQ4_0 ? launch_swiglu<kFmtQ4_0>(w, xq, nin, gu_out, g_q8, inter, k, stream)
+                           : launch_swiglu<kFmtQ4K>(w, xq, nin, gu_out, g_q8, inter, k, stream);
 }
 
 hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,

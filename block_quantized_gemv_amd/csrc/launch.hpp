@@ -33,19 +33,25 @@ bool take_next_launch_events(hipEvent_t* start, hipEvent_t* stop);
 // Largest LDS a workgroup of the full-staging kernels may take.
 constexpr int kMaxStageLds = 64 * 1024;
 
+// Layer weight formats of the 4-bit GEMVs: q4_K super-blocks, or q4_0
+// blocks, eight of which fill the same 144 bytes (the plain, RMSNorm,
+// batched, split-k and gate/up launchers take either; the grouped and
+// expert kernels take q4_K only).
+constexpr int kFmtQ4K = 0, kFmtQ4_0 = 1;
+
 hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                            int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
-                           hipStream_t stream);
-// The q4_K GEMV of one activation Q8(RMSNorm(x)) formed in the kernel's
+                           hipStream_t stream, int fmt = kFmtQ4K);
+// The 4-bit GEMV of one activation Q8(RMSNorm(x)) formed in the kernel's
 // prologue from the f32 input nin describes (the decode-step chain).
 hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,
-                                hipStream_t stream);
+                                hipStream_t stream, int fmt = kFmtQ4K);
 // Gate/up GEMV with the SwiGLU stand-in fused: rows [0, inter) are gate rows,
 // [inter, 2*inter) up rows; writes Q8(silu(gate)*up) (inter/32 blocks) and,
 // if gu_out is set, the f32 GEMV outputs.  inter % 32 == 0.  The activation
 // is xq, or Q8(RMSNorm(x)) formed in the prologue when nin is set.
 hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                  int64_t inter, int64_t k, hipStream_t stream);
+                                  int64_t inter, int64_t k, hipStream_t stream, int fmt = kFmtQ4K);
 // Workgroups and threads per workgroup for `units` equal work units of a
 // kernel whose workgroups each run a prologue of `prologue` per-thread
 // steps: about one workgroup per CU, of at most max_waves waves.
@@ -66,7 +72,8 @@ constexpr int kWavesQ8EarlyMin = 7, kWavesQ8EarlyMax = 12, kItemsPerWave = 10;
 // holds n_split*m*ncols doubles.
 int gemv_q4k_splitk_nsplit(int64_t k);
 hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
-                                  double* part, int64_t m, int64_t k, int ncols, hipStream_t stream);
+                                  double* part, int64_t m, int64_t k, int ncols, hipStream_t stream,
+                                  int fmt = kFmtQ4K);
 hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,
                                    const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
                                    float* y, const float* combine, float* y_out,

@@ -22,6 +22,10 @@ def q8_bytes(m: int, k: int) -> int:
     return m * (k // 32) * 34
 
 
+def q4_0_bytes(m: int, k: int) -> int:
+    return m * (k // 32) * 18
+
+
 @dataclass(frozen=True)
 class SingleGemv:
     name: str = "q4_K x q8_0 GEMV 1024x1024"
@@ -43,14 +47,18 @@ class DecodeModel:
     vocab: int
     seed: int
     eps: float = 1e-6
+    weight_format: str = "q4_K"      # layer matrices: "q4_K" or "q4_0"
 
     def layer_shapes(self):
-        """(rows, k) of the four q4_K GEMVs of one layer, in step order."""
+        """(rows, k) of the four 4-bit GEMVs of one layer, in step order."""
         return [(self.qkv_rows, self.hidden), (self.hidden, self.hidden),
                 (2 * self.inter, self.hidden), (self.hidden, self.inter)]
 
+    def layer_matrix_bytes(self, m: int, k: int) -> int:
+        return q4_0_bytes(m, k) if self.weight_format == "q4_0" else q4k_bytes(m, k)
+
     def weight_bytes(self) -> int:
-        per_layer = sum(q4k_bytes(m, k) for m, k in self.layer_shapes())
+        per_layer = sum(self.layer_matrix_bytes(m, k) for m, k in self.layer_shapes())
         return self.n_layers * per_layer + q8_bytes(self.vocab, self.hidden)
 
     def algorithmic_bytes(self) -> int:
@@ -65,6 +73,11 @@ class DecodeModel:
 
 DECODE_05B = DecodeModel("0.5B-class decode step (hidden 1024, 24 layers, q8_0 lm_head 151552x1024)",
                          hidden=1024, n_layers=24, qkv_rows=1280, inter=4864, vocab=151552, seed=1)
+# The format of the 0.5B model the pages measure ('07 · R3', §5: 0.5B q4_0).
+DECODE_05B_Q4_0 = DecodeModel("0.5B-class decode step, q4_0 layer weights (hidden 1024, 24 layers, "
+                              "q8_0 lm_head 151552x1024)",
+                              hidden=1024, n_layers=24, qkv_rows=1280, inter=4864, vocab=151552, seed=5,
+                              weight_format="q4_0")
 DECODE_7B = DecodeModel("7B-class decode step (hidden 3584, 28 layers, q8_0 lm_head 152064x3584)",
                         hidden=3584, n_layers=28, qkv_rows=4608, inter=18944, vocab=152064, seed=2)
 

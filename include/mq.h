@@ -117,6 +117,27 @@ int mq_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,
                         int64_t m, int64_t k, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * q4_0 x q8_0 GEMV: the 0.5B model the pages measure is stored in q4_0
+ * ('07 · R3 — Small-model per-token overhead', §5), which the pages name but
+ * do not lay out.  Read plainly: per 32 weights an 18-byte block, f16 d then
+ * 16 quant bytes, byte i holding weight i in its low nibble and weight 16+i
+ * in its high nibble, weight = d*(q - 8); rows hold k/32 blocks back to back.
+ * w: [m][k/32 blocks] (16-byte aligned); xq: k/32 q8_0 blocks; y: f32 [m].
+ * k % 256 == 0 (eight blocks fill one 144-byte group of the 4-bit kernels'
+ * lane layout), m >= 1.  Per block the kernel forms the exact int32 sum
+ * isum = sum q*q8 of the stored nibbles (v_dot4) and adds
+ * d*(d8*isum - 8*d8*ysum) in f64, where d8*ysum is the activation block's
+ * scale times its code sum; rows are reduced in a fixed order and rounded
+ * to f32 once.  Errors as mq_gemv_q4k_q8.
+ */
+int mq_gemv_q4_0_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                    hipStream_t stream);
+/* 1 <= n <= 8 activation columns; layouts, split-k workspace and errors as
+ * mq_gemv_q4k_q8_batched. */
+int mq_gemv_q4_0_q8_batched(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                            int n, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * q8_0 x q8_0 GEMV (the lm_head): w: q8_0 matrix [m][k/32 blocks], 4-byte
  * aligned; xq: k/32 blocks; y: f32 [m].  k % 64 == 0.
  * Per block isum = sum w8*x8 (int32), then y += d_w*d_x*isum in f64.
@@ -154,6 +175,11 @@ int mq_debug_gemv_q4k_q8_isums(const void* w, const void* xq, float* y, int32_t*
                                int32_t* ysum, int64_t m, int64_t k, hipStream_t stream);
 int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t* isum,
                                 int64_t m, int64_t k, hipStream_t stream);
+/* The q4_0 kernel's sums: isum as above (q = stored nibble 0..15), ysum as
+ * for q4_K (may be NULL).  MQ_ERR_SHAPE when the activation does not fit in
+ * LDS (k above about 55,000). */
+int mq_debug_gemv_q4_0_q8_isums(const void* w, const void* xq, float* y, int32_t* isum,
+                                int32_t* ysum, int64_t m, int64_t k, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Decode-step chain: one decode step of a stand-in model, recorded once as a
@@ -202,11 +228,13 @@ typedef struct mq_chain mq_chain;
 enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u, MQ_UNFUSED_GLUE = 8u,
        MQ_LAZY_CAPTURE = 16u, MQ_HOST_LOGITS = 32u };
 enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
+/* Weight format of the four layer GEMVs (the lm_head is q8_0 either way). */
+enum { MQ_FMT_Q4_K = 0, MQ_FMT_Q4_0 = 1 };
 
 typedef struct {
     int n_layers;                      /* >= 1 */
     int64_t hidden, qkv_rows, inter, vocab;   /* hidden, inter % 256 == 0; qkv_rows >= hidden, % 4 == 0 */
-    const void* const* w_qkv;          /* HOST arrays of n_layers device pointers (q4_K) */
+    const void* const* w_qkv;          /* HOST arrays of n_layers device pointers (weight_format) */
     const void* const* w_o;
     const void* const* w_gu;
     const void* const* w_down;
@@ -217,6 +245,7 @@ typedef struct {
     float eps;
     unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE | MQ_UNFUSED_GLUE
                                           | MQ_LAZY_CAPTURE | MQ_HOST_LOGITS */
+    int weight_format;                 /* MQ_FMT_Q4_K or MQ_FMT_Q4_0 (layer matrices) */
 } mq_chain_desc;
 
 /* Validates, allocates every device buffer the step needs (nothing is

@@ -70,20 +70,22 @@ def oracle_gemv_parallel(fn, w, m, k, xq, rows=None, pool=None):
 
 def oracle_chain_parallel(o, model, W, h0, n_layers, pool):
     """The decode step composed from the oracle's stages (the composition is
-    the one oracle.chain implements, pinned by pin_chain_structure), with the
-    GEMV rows spread over threads.  Returns logits, s_abs, q8 trace, f32 trace."""
+    the one oracle.chain implements, pinned by pin_chain_structure and
+    pin_chain_structure_q4_0), with the GEMV rows spread over threads.
+    Returns logits, s_abs, q8 trace, f32 trace."""
     H, I, eps = model.hidden, model.inter, model.eps
+    gemv = o.gemv_q4_0 if getattr(model, "weight_format", "q4_K") == "q4_0" else o.gemv_q4k
     h = np.asarray(h0, np.float32)
     q8s, f32s = [], []
     for l in range(n_layers):
         a = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel(); q8s.append(a)
-        t, _ = oracle_gemv_parallel(o.gemv_q4k, W["qkv"][l], model.qkv_rows, H, a, pool=pool)
+        t, _ = oracle_gemv_parallel(gemv, W["qkv"][l], model.qkv_rows, H, a, pool=pool)
         b = o.quantize_q8_0(o.rmsnorm(t[:H], eps)).ravel(); q8s.append(b)
-        ov, _ = oracle_gemv_parallel(o.gemv_q4k, W["o"][l], H, H, b, pool=pool)
+        ov, _ = oracle_gemv_parallel(gemv, W["o"][l], H, H, b, pool=pool)
         c = o.quantize_q8_0(o.rmsnorm(ov, eps)).ravel(); q8s.append(c)
-        gu, _ = oracle_gemv_parallel(o.gemv_q4k, W["gu"][l], 2 * I, H, c, pool=pool)
+        gu, _ = oracle_gemv_parallel(gemv, W["gu"][l], 2 * I, H, c, pool=pool)
         g = o.quantize_q8_0(o.swiglu(gu)).ravel(); q8s.append(g)
-        h, _ = oracle_gemv_parallel(o.gemv_q4k, W["down"][l], H, I, g, pool=pool)
+        h, _ = oracle_gemv_parallel(gemv, W["down"][l], H, I, g, pool=pool)
         f32s += [t, ov, gu, h]
     z = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel(); q8s.append(z)
     logits, s_abs = oracle_gemv_parallel(o.gemv_q8_0, W["lm"], model.vocab, H, z, pool=pool)
@@ -94,12 +96,13 @@ def model_weights(model, n_layers):
     """Seeded synthetic weights of a decode-step model (host numpy)."""
     from block_quantized_gemv_amd import synth
     s = model.seed
+    mat = synth.q4_0_matrix if getattr(model, "weight_format", "q4_K") == "q4_0" else synth.q4k_matrix
     W = {"qkv": [], "o": [], "gu": [], "down": []}
     for l in range(n_layers):
-        W["qkv"].append(synth.q4k_matrix(s, (synth.KEY_LAYER, l, 0), model.qkv_rows, model.hidden))
-        W["o"].append(synth.q4k_matrix(s, (synth.KEY_LAYER, l, 1), model.hidden, model.hidden))
-        W["gu"].append(synth.q4k_matrix(s, (synth.KEY_LAYER, l, 2), 2 * model.inter, model.hidden))
-        W["down"].append(synth.q4k_matrix(s, (synth.KEY_LAYER, l, 3), model.hidden, model.inter))
+        W["qkv"].append(mat(s, (synth.KEY_LAYER, l, 0), model.qkv_rows, model.hidden))
+        W["o"].append(mat(s, (synth.KEY_LAYER, l, 1), model.hidden, model.hidden))
+        W["gu"].append(mat(s, (synth.KEY_LAYER, l, 2), 2 * model.inter, model.hidden))
+        W["down"].append(mat(s, (synth.KEY_LAYER, l, 3), model.hidden, model.inter))
     W["lm"] = synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, model.hidden)
     return W
 

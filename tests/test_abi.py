@@ -57,6 +57,11 @@ def test_gemv_argument_errors(mq):
     assert L.mq_quantize_q8_0(FAKE, C.c_void_p(0x10001), 32, 1, None) == mq.MQ_ERR_ARG
     assert L.mq_swiglu_quantize_q8_0(FAKE, FAKE, 64, 1, 32, None) == mq.MQ_ERR_SHAPE
     assert L.mq_rmsnorm_quantize_q8_0(FAKE, FAKE, 64, -1.0, None) == mq.MQ_ERR_ARG
+    assert L.mq_gemv_q4_0_q8(FAKE, FAKE, FAKE, 16, 288, None) == mq.MQ_ERR_SHAPE             # k % 256
+    assert L.mq_gemv_q4_0_q8(C.c_void_p(0x10004), FAKE, FAKE, 16, 256, None) == mq.MQ_ERR_ARG
+    assert L.mq_gemv_q4_0_q8_batched(FAKE, FAKE, FAKE, 16, 256, 9, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_debug_gemv_q4_0_q8_isums(FAKE, FAKE, FAKE, None, None, 16, 256, None) == mq.MQ_ERR_ARG
+    assert L.mq_debug_gemv_q4_0_q8_isums(FAKE, FAKE, FAKE, FAKE, None, 16, 256 * 300, None) == mq.MQ_ERR_SHAPE
 
 
 def test_stream_probe_argument_errors(mq):
@@ -103,6 +108,10 @@ def test_chain_argument_errors(mq):
     assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_ARG          # n_inputs
     d.n_inputs, d.qkv_rows = 1, 512
     assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # qkv_rows < hidden
+    d.qkv_rows, d.weight_format = 1280, 7
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_ARG          # weight_format
+    assert "weight_format" in L.mq_last_error().decode()
+    d.weight_format = mq.MQ_FMT_Q4_K
     assert L.mq_decode_chain(None, 0, None) == mq.MQ_ERR_ARG
     assert L.mq_chain_destroy(None) == mq.MQ_OK
     m = mq.MoEDesc(64, 8, 2048, 1408, FAKE, 16, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 10, 0)

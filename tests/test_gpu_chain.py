@@ -277,6 +277,26 @@ def test_chain_7b_full_depth_vs_oracle(mq, o, pool):
     _chain_vs_oracle(mq, o, pool, workloads.DECODE_7B, workloads.DECODE_7B.n_layers, n_inputs=1)
 
 
+def test_chain_05b_q4_0_full_depth_vs_oracle(mq, o, pool):
+    """The pages' measured 0.5B model format: q4_0 layer weights, all 24 layers."""
+    from block_quantized_gemv_amd import workloads
+    _chain_vs_oracle(mq, o, pool, workloads.DECODE_05B_Q4_0, 24)
+
+
+def test_q4_0_chain_graph_equals_eager(mq):
+    from block_quantized_gemv_amd import synth, workloads
+    model = dataclasses.replace(workloads.DECODE_05B_Q4_0, n_layers=3)
+    W = model_weights(model, 3)
+    Wd = _dev_weights(W)
+    xd = to_dev(synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (8, model.hidden)))
+    g = mq.DecodeChain(model, Wd, xd)
+    e = mq.DecodeChain(model, Wd, xd, flags=mq.MQ_EAGER_ONLY)
+    assert g.info()["captured"] and g.info()["n_nodes"] == 4 * 3 + 1
+    for i in range(8):
+        u, v = to_host(g.step()).copy(), to_host(e.step(mq.MQ_EAGER)).copy()
+        assert _same(u, v), f"q4_0 graph != eager at step {i}"
+
+
 def test_unfused_glue_chain_vs_oracle(mq, o, pool):
     """The unfused measurement arm (glue kernels between q8_0-input GEMVs)
     computes the same step: 0.5B, all layers, against the oracle."""

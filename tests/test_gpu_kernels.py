@@ -170,6 +170,85 @@ def test_batched_full_size(mq, o, pool, name, m, k, n):
         log(f"    col {c}: bit-identical to the n=1 kernel on {same:.4f} of rows")
 
 
+# ------------------------------------------------------------- q4_0 GEMV ----
+
+Q4_0_SMALL = [(1, 256), (3, 512), (17, 768), (1023, 1024), (1025, 3584), (333, 4864), (64, 18944), (130, 4096)]
+
+
+def _codes_sum(xq):
+    return np.asarray(xq, np.uint8).reshape(-1, 34)[:, 2:].view(np.int8).astype(np.int32).sum(axis=1)
+
+
+@pytest.mark.parametrize("m,k", Q4_0_SMALL)
+def test_gemv_q4_0_small(mq, o, m, k):
+    synth = _synth()
+    log(f"q4_0 GEMV {m}x{k}")
+    w = synth.q4_0_matrix(200 + k, (synth.KEY_MATRIX, m), m, k)
+    x = synth.normal_f32(200 + k, (synth.KEY_COLUMNS, m), (k,))
+    xq = o.quantize_q8_0(x).ravel()
+    wd, xd = to_dev(w), to_dev(xq)
+    y = to_host(mq.mq_gemv_q4_0_q8(wd, xd, m, k))
+    yd, isum, ysum = (to_host(t) for t in mq.mq_debug_gemv_q4_0_q8_isums(wd, xd, m, k))
+    ri = o.isums_q4_0(w, m, k, xq)
+    assert np.array_equal(isum, ri), f"int32 block sums differ at {np.argwhere(isum != ri)[:4]}"
+    assert np.array_equal(ysum, _codes_sum(xq)), "activation sums differ"
+    assert np.array_equal(yd.view(np.uint32), y.view(np.uint32)), "dump build changed the float result"
+    y_ref, s_abs = o.gemv_q4_0(w, m, k, xq)
+    check_tolerance(y, y_ref, s_abs, f"q4_0 {m}x{k}")
+
+
+def test_gemv_q4_0_worked_example(mq, o):
+    """The hand-worked q4_0 block (y = 32.0, isum = 1600), first of eight in
+    one 256-weight group; the other seven blocks have d = 0 and meet zero
+    activation blocks."""
+    from oracle_pins import _golden_lines
+    lines = dict(ln.split(":", 1) for ln in _golden_lines("q4_0_gemv_worked.txt"))
+    blk = bytes(int(t, 16) for t in lines["block"].split())
+    w = np.frombuffer(blk + bytes([0, 0] + [0x5A] * 16) * 7, np.uint8)
+    q = np.array([int(t) for t in lines["act_q"].split()], np.int8)
+    xq = np.frombuffer(np.uint16(int(lines["act_d_bits"], 16)).tobytes() + q.tobytes() + bytes(34 * 7), np.uint8)
+    y, isum, _ = mq.mq_debug_gemv_q4_0_q8_isums(to_dev(w), to_dev(xq), 1, 256)
+    assert float(to_host(y)[0]) == float(lines["y"])
+    assert int(to_host(isum)[0, 0]) == int(lines["isum"])
+
+
+Q4_0_FULL = [("0.5B qkv", 1280, 1024), ("0.5B o", 1024, 1024), ("0.5B gate/up", 9728, 1024),
+             ("0.5B down", 1024, 4864), ("7B gate/up", 37888, 3584), ("7B down", 3584, 18944)]
+
+
+@pytest.mark.parametrize("name,m,k", Q4_0_FULL, ids=[s[0] for s in Q4_0_FULL])
+def test_gemv_q4_0_full_size(mq, o, pool, name, m, k):
+    synth = _synth()
+    log(f"q4_0 GEMV full size {name} {m}x{k}")
+    w = synth.q4_0_matrix(5, (synth.KEY_MATRIX, m, k), m, k)
+    x = synth.normal_f32(5, (synth.KEY_COLUMNS, m, k), (k,))
+    xq_dev = mq.mq_quantize_q8_0(to_dev(x))
+    xq = o.quantize_q8_0(x).ravel()
+    assert np.array_equal(to_host(xq_dev), xq)
+    y = to_host(mq.mq_gemv_q4_0_q8(to_dev(w), xq_dev, m, k))
+    rows = sample_rows(m, 2048, seed=m)
+    y_ref, s_abs = oracle_gemv_parallel(o.gemv_q4_0, w, m, k, xq, rows=rows, pool=pool)
+    check_tolerance(y[rows], y_ref, s_abs, name)
+
+
+@pytest.mark.parametrize("n,m,k", [(2, 301, 2560), (5, 130, 1024), (8, 301, 2560), (8, 515, 18944)])
+def test_batched_q4_0(mq, o, n, m, k):
+    """Every column against the oracle (k = 18944 at n = 8 takes split-k),
+    and against the n = 1 kernel."""
+    synth = _synth()
+    log(f"q4_0 batched {m}x{k} n={n}")
+    w = synth.q4_0_matrix(6, (synth.KEY_MATRIX, n, k), m, k)
+    x = synth.normal_f32(6, (synth.KEY_COLUMNS, n, k), (n, k))
+    xq = o.quantize_q8_0(x).reshape(n, -1)
+    wd, xd = to_dev(w), to_dev(xq.ravel())
+    y = to_host(mq.mq_gemv_q4_0_q8_batched(wd, xd, m, k, n))
+    for c in range(n):
+        y_ref, s_abs = o.gemv_q4_0(w, m, k, xq[c])
+        check_tolerance(y[:, c], y_ref, s_abs, f"q4_0 batched n={n} col {c}")
+        y1 = to_host(mq.mq_gemv_q4_0_q8(wd, to_dev(xq[c]), m, k))
+        check_tolerance(y1, y_ref, s_abs, f"q4_0 n=1 col {c}")
+
+
 # ------------------------------------------------------------ q8_0 lm_head ----
 
 @pytest.mark.parametrize("m,k", [(1, 64), (5, 128), (130, 1024), (67, 3584), (1000, 2048)])
