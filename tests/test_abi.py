@@ -50,6 +50,9 @@ def test_gemv_argument_errors(mq):
     assert L.mq_gemv_q4k_q8(C.c_void_p(0x10008), FAKE, FAKE, 16, 256, None) == mq.MQ_ERR_ARG   # not 16-aligned
     assert L.mq_gemv_q4k_q8(FAKE, FAKE, FAKE, 16, 300, None) == mq.MQ_ERR_SHAPE
     assert L.mq_gemv_q4k_q8(FAKE, FAKE, FAKE, 0, 256, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_q4k_q8(FAKE, FAKE, FAKE, (1 << 30) + 1, 256, None) == mq.MQ_ERR_SHAPE   # rows above 2^30
+    assert L.mq_gemv_q4k_q8(FAKE, FAKE, FAKE, 16, (1 << 24) + 256, None) == mq.MQ_ERR_SHAPE  # k above 2^24
+    assert L.mq_gemv_q4_0_q8(FAKE, FAKE, FAKE, (1 << 30) + 1, 256, None) == mq.MQ_ERR_SHAPE
     assert L.mq_gemv_q4k_q8_batched(FAKE, FAKE, FAKE, 16, 256, 9, None) == mq.MQ_ERR_SHAPE
     assert L.mq_gemv_q4k_q8_batched(FAKE, FAKE, FAKE, 16, 256, 0, None) == mq.MQ_ERR_SHAPE
     assert L.mq_gemv_q8_0_q8(FAKE, FAKE, FAKE, 16, 96, None) == mq.MQ_ERR_SHAPE

@@ -249,6 +249,48 @@ def test_batched_q4_0(mq, o, n, m, k):
         check_tolerance(y1, y_ref, s_abs, f"q4_0 n=1 col {c}")
 
 
+# ------------------------------------------------------------ edge cases ----
+
+@pytest.mark.parametrize("fmt", ["q4_K", "q4_0"])
+@pytest.mark.parametrize("n", [1, 2])
+def test_gemv_split_k_large_k(mq, o, fmt, n):
+    """k = 65536: one column no longer fits in LDS, so even n = 1 takes the
+    split-k kernel and the ordered second pass."""
+    synth = _synth()
+    m, k = 37, 65536
+    log(f"{fmt} split-k {m}x{k} n={n}")
+    mat = synth.q4_0_matrix if fmt == "q4_0" else synth.q4k_matrix
+    gemv = o.gemv_q4_0 if fmt == "q4_0" else o.gemv_q4k
+    w = mat(7, (synth.KEY_MATRIX, n, k), m, k)
+    x = synth.normal_f32(7, (synth.KEY_COLUMNS, n, k), (n, k))
+    xq = o.quantize_q8_0(x).reshape(n, -1)
+    wd, xd = to_dev(w), to_dev(xq.ravel())
+    if n == 1:
+        f = mq.mq_gemv_q4_0_q8 if fmt == "q4_0" else mq.mq_gemv_q4k_q8
+        y = to_host(f(wd, xd, m, k))[:, None]
+    else:
+        f = mq.mq_gemv_q4_0_q8_batched if fmt == "q4_0" else mq.mq_gemv_q4k_q8_batched
+        y = to_host(f(wd, xd, m, k, n))
+    for c in range(n):
+        y_ref, s_abs = gemv(w, m, k, xq[c])
+        check_tolerance(y[:, c], y_ref, s_abs, f"{fmt} split-k col {c}")
+
+
+def test_gemv_zero_activation(mq, o):
+    """An all-zero activation quantizes to zero blocks (d = 0, q = 0); every
+    product is then exactly zero, so every output is +0 or -0."""
+    synth = _synth()
+    m, k = 515, 3584
+    xq = o.quantize_q8_0(np.zeros(k, np.float32)).ravel()
+    assert not xq.any()
+    xd = to_dev(xq)
+    for name, w, f in (("q4_K", synth.q4k_matrix(8, (synth.KEY_MATRIX, 1), m, k), mq.mq_gemv_q4k_q8),
+                       ("q4_0", synth.q4_0_matrix(8, (synth.KEY_MATRIX, 2), m, k), mq.mq_gemv_q4_0_q8),
+                       ("q8_0", synth.q8_0_matrix(8, (synth.KEY_MATRIX, 3), m, k), mq.mq_gemv_q8_0_q8)):
+        y = to_host(f(to_dev(w), xd, m, k))
+        assert np.all(y == 0.0), f"{name}: nonzero output for a zero activation"
+
+
 # ------------------------------------------------------------ q8_0 lm_head ----
 
 @pytest.mark.parametrize("m,k", [(1, 64), (5, 128), (130, 1024), (67, 3584), (1000, 2048)])
