@@ -22,6 +22,11 @@
  *  - mq_last_error() returns this thread's message for the last failing
  *    call (host memory owned by the library, valid until the next call).
  *  - No exceptions cross this boundary; the library never exits or aborts.
+ *  - Threads: the stateless entry points may be called from several host
+ *    threads at once.  A chain object is not synchronized: calls on one
+ *    chain (step, reset, info, reads) must not overlap.  mq_read_to_host
+ *    serializes on its mutex.  mq_test_set_fault is a process-wide switch
+ *    for single-threaded tests.
  *
  * Formats (little-endian, packed):
  *  - q4_K super-block, 256 weights in 144 bytes: f16 d at 0, f16 dmin at 2,
@@ -35,8 +40,9 @@
  *  - q8_0 block, 32 values in 34 bytes: f16 d, then 32 int8 q; value = d*q.
  *    A q8_0 vector of k values is k/32 consecutive blocks.  Base pointers
  *    must be 2-byte aligned; q8_0 weight matrices 4-byte aligned.
+ *  - q4_0 block, 32 weights in 18 bytes (see mq_gemv_q4_0_q8).
  *  The pages name these formats but do not lay them out; the layout above
- *  is the synthetic workload's definition.
+ *  is the synthetic workload's definition (q4_0: the plain reading).
  */
 #ifndef MQ_H
 #define MQ_H
