@@ -599,21 +599,42 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
                 32 * ln.j, it.L);
     };
 
+    // Contiguous slot columns (the expert chain's) are staged as one vector,
+    // slot s's pairs starting at s*nb/2: their loads go out together with the
+    // ids, before the weights, and both weight items are requested before
+    // the staging stores.  Otherwise each column is staged on its own after
+    // the first item is requested.
+    const bool contig = xq_stride == (int64_t)nb * kQ8Bytes;
     Item A, B;
-    fetch(0, A);
-    for (int c = 0; c < n_sel; ++c)
-        stage_q8(xq + c * xq_stride, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x, nullptr);
+    if (contig) {
+        Q8Regs qr;
+        stage_q8_load(xq, n_sel * nb, qr);
+        fetch(0, A);
+        fetch(1, B);
+        stage_q8_store(xq, n_sel * nb, qr, lds);
+    } else {
+        fetch(0, A);
+        for (int c = 0; c < n_sel; ++c)
+            stage_q8(xq + c * xq_stride, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x, nullptr);
+    }
     __syncthreads();
 
     double acc[1] = {0.0};
-    const uint8_t* xs = lds + slot * col_bytes;
-    stream_items<false>(n_items, A, B, fetch, [&](const Item& it) {
-        sb_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, xs, col_bytes, acc, nullptr, 0);
+    const uint8_t* xs = contig ? lds : lds + slot * col_bytes;
+    const int pbase = contig ? slot * (nb / 2) : 0;
+    auto use = [&](const Item& it) {
+        // lanes past the row's last super-block read pair 0 (their result is dropped)
+        const int P = it.valid ? pbase + pair_of(ln, it.pass) : 0;
+        sb_item<1, false>(it.L, ln, P, it.valid, xs, col_bytes, acc, nullptr, 0);
         if (it.pass != passes - 1) return;
         const double v = group_sum_f64(acc[0], ln.log2s);
         acc[0] = 0.0;
         if ((ln.lane & (ln.S - 1)) == 0) res[(slot * tpw + it.k) * ln.R + ln.row_local] = slot_ok ? (float)v : __builtin_nanf("");
-    });
+    };
+    if (contig)
+        stream_items<true>(n_items, A, B, fetch, use);
+    else
+        stream_items<false>(n_items, A, B, fetch, use);
     __syncthreads();
     float* yo = y_out + (out_row ? (int64_t)(*out_row % out_rows) * M : 0);
     for (int i = threadIdx.x; i < tpw * ln.R; i += blockDim.x) {
@@ -995,13 +1016,15 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
     const int lds = (xq_stride ? n_sel : 1) * stage_bytes(nsb * 8);
     const int64_t units = combine ? p.n_tiles : (int64_t)p.n_tiles * n_sel;
     if (combine && !y && xq_stride) {
+        // contiguous slot columns are staged as one vector (see the kernel)
+        const int lds_c = xq_stride == (int64_t)nsb * 8 * kQ8Bytes ? stage_bytes(n_sel * nsb * 8) : lds;
         // slots in parallel: about two workgroups per CU, tiles split evenly
         const int64_t want = 2 * (int64_t)device_cu_count();
         int tpw = (int)((p.n_tiles + want - 1) / want);
         if (tpw * p.rows_per_tile > 64) tpw = 64 / p.rows_per_tile;
         if (tpw < 1) tpw = 1;
         const int grid = (p.n_tiles + tpw - 1) / tpw;
-        MQ_LAUNCH(k_gemv_q4k_grouped_combine, dim3(grid), dim3(64 * n_sel), lds, stream, (const uint8_t*)w_all,
+        MQ_LAUNCH(k_gemv_q4k_grouped_combine, dim3(grid), dim3(64 * n_sel), lds_c, stream, (const uint8_t*)w_all,
                   expert_bytes, n_experts, ids, n_sel, (const uint8_t*)xq, xq_stride, combine, y_out, out_row,
                   out_rows, (int)m, nsb, p.log2s, p.passes, p.n_tiles, tpw, inc_step);
     } else if (combine) {

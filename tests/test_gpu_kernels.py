@@ -408,6 +408,38 @@ def test_grouped_gate_up_and_down(mq, o, experts):
     del torch
 
 
+def test_grouped_down_combine_kernel(mq, o, experts):
+    """y = NULL with a combine runs the slot-parallel combine kernel.  Slot
+    columns packed back to back are staged as one vector; a wider stride
+    stages them column by column: both give the same bytes, within the
+    tolerance of the oracle's per-slot products combined in slot order."""
+    wl, gu, dn = experts
+    synth = _synth()
+    H, I, KP = wl.hidden, wl.inter, wl.k_pad
+    dn_d = to_dev(dn.ravel())
+    ids_all, logits_all = synth.routing(wl.seed, 2, wl.n_experts, wl.n_sel)
+    for t in range(2):
+        ids = ids_all[t]
+        x = synth.normal_f32(wl.seed, (synth.KEY_TOKEN_X, 100 + t), (wl.n_sel, I))
+        g = np.stack([o.quantize_q8_0(x[s]).ravel() for s in range(wl.n_sel)])
+        comb = o.softmax(logits_all[t])
+        outs = []
+        for pad in (0, 34):
+            stride = KP // 32 * 34 + pad
+            gp = np.zeros((wl.n_sel, stride), np.uint8)
+            gp[:, :g.shape[1]] = g
+            _, y_out = mq.mq_gemv_q4k_grouped(dn_d, dn[0].nbytes, wl.n_experts, to_dev(ids), to_dev(gp.ravel()),
+                                              stride, H, KP, combine=to_dev(comb), want_y=False)
+            outs.append(to_host(y_out).copy())
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "staging layouts disagree"
+        acc, sab = np.zeros(H), np.zeros(H)
+        for s, e in enumerate(ids):
+            y_ref, s_abs = o.gemv_q4k(dn[e], H, I, g[s])
+            acc += float(comb[s]) * y_ref.astype(np.float64)
+            sab += abs(float(comb[s])) * s_abs
+        check_tolerance(outs[0], acc, sab, f"token {t} combine kernel")
+
+
 # ------------------------------------------------------ measurement probe ----
 
 def test_stream_probe_reads_every_word(mq):
