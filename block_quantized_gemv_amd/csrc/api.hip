@@ -147,6 +147,9 @@ struct mq_chain {
     int64_t vocab = 0;
     float* host_logits = nullptr;     // MQ_HOST_LOGITS: pinned f32 [vocab], written by the step's last node
     bool lazy = false;                // MQ_LAZY_CAPTURE: capture on the third MQ_GRAPH step
+    int32_t* ids_next = nullptr;      // expert chain: routing ids of token (*step mod n_tokens)
+    const int32_t* ids_table = nullptr;
+    int n_tokens = 0, n_sel = 0;
     bool capture_tried = false;
     int64_t graph_steps = 0;
     double capture_ms = 0.0;
@@ -205,8 +208,16 @@ int enqueue(mq_chain* c, hipStream_t s) {
 }
 
 // Warm run, counter reset, then capture; failure to capture leaves an eager chain.
+// Sets the step counter; the expert chain's next-token ids follow it.
+hipError_t set_step(mq_chain* c, int64_t step, hipStream_t stream) {
+    hipError_t e = launch_set_i64(c->step, step, stream);
+    if (e == hipSuccess && c->ids_next)
+        e = launch_moe_prime(c->step, c->n_tokens, c->ids_table, c->n_sel, c->ids_next, stream);
+    return e;
+}
+
 int zero_counters(mq_chain* c, hipStream_t stream) {
-    hipError_t e = launch_set_i64(c->step, 0, stream);
+    hipError_t e = set_step(c, 0, stream);
     if (e == hipSuccess && c->cur) e = launch_set_i64(c->cur, 0, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     return hip_status(e, "counter reset");
@@ -643,12 +654,18 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     float* comb = rc == MQ_OK ? (float*)chain_alloc(c, 64 * sizeof(float), &rc) : nullptr;
     const int64_t gstride = KP / 32 * kQ8Bytes;
     uint8_t* gq = rc == MQ_OK ? (uint8_t*)chain_alloc(c, (size_t)S * gstride, &rc) : nullptr;
+    int32_t* ids_next = rc == MQ_OK ? (int32_t*)chain_alloc(c, 64 * sizeof(int32_t), &rc) : nullptr;
     if (rc != MQ_OK) { chain_free(c); return rc; }
+    c->ids_next = ids_next;
+    c->ids_table = d->ids_table;
+    c->n_tokens = d->n_tokens;
+    c->n_sel = S;
 
     // Two kernels per token: gate/up (reads the counter, quantizes x_t in
     // its prologue, writes the routing, the combine weights and
     // Q8(SwiGLU)), then down with the weighted combine, which advances the
-    // counter.
+    // counter and leaves the next token's routing ids in ids_next, where the
+    // next gate/up reads them without waiting for the counter.
     int64_t *step = c->step, *cur = c->cur;
     const mq_moe_desc dd = *d;
     const int per_launch = d->tokens_per_launch > 0 ? d->tokens_per_launch : 1;
@@ -656,11 +673,12 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
         c->ops.push_back([=](hipStream_t s) {
             return launch_moe_gate_up(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, I, H, step, dd.n_tokens,
                                       dd.ids_table, dd.logits_table, dd.x_table, S, KP, cur, ids, comb, gq, nullptr,
-                                      s);
+                                      s, ids_next);
         });
         c->ops.push_back([=](hipStream_t s) {
             return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,
-                                           nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, step, s);
+                                           nullptr, comb, dd.y_table, cur, dd.n_tokens, H, KP, step, s, dd.ids_table,
+                                           ids_next);
         });
     }
     rc = chain_finish(c, stream, d->flags);
@@ -726,7 +744,7 @@ int mq_chain_host_logits(const mq_chain* c, const float** host_logits) {
 int mq_chain_reset(mq_chain* c, int64_t step, hipStream_t stream) {
     CHECK_ARG(c, "null chain");
     CHECK_ARG(step >= 0, "step must be >= 0");
-    return hip_status(launch_set_i64(c->step, step, stream), "counter reset");
+    return hip_status(set_step(c, step, stream), "counter reset");
 }
 
 int mq_chain_trace_sizes(const mq_chain* c, int64_t* q8_bytes, int64_t* f32_count) {

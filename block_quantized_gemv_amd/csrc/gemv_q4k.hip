@@ -566,10 +566,18 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
     const int32_t* __restrict__ ids, int n_sel, const uint8_t* __restrict__ xq, int64_t xq_stride,
     const float* __restrict__ combine, float* __restrict__ y_out, const int64_t* __restrict__ out_row,
     int64_t out_rows, int M, int nsb, int log2s, int passes, int n_tiles, int tpw,
-    int64_t* __restrict__ inc_step) {
+    int64_t* __restrict__ inc_step, const int32_t* __restrict__ ids_table, int32_t* __restrict__ ids_next) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float res[16 * 64];          // [slot][tile in the workgroup][row in the tile]
-    if (inc_step && blockIdx.x == 0 && threadIdx.x == 0) *inc_step += 1;
+    // The first wave of workgroup 0 advances the token counter (out_rows
+    // tokens) and, with ids_next, hands the next token's routing ids to the
+    // next gate/up kernel, which then need not wait for the counter to read
+    // them.  The counter is read first, the ids once it has arrived, and
+    // both are stored at the end, so no wait lands before the weights.
+    const bool counter = inc_step && blockIdx.x == 0 && threadIdx.x < 64;
+    const bool hand = counter && ids_next && (int)threadIdx.x < n_sel;
+    int64_t next = 0;
+    if (counter && (threadIdx.x == 0 || hand)) next = *inc_step + 1;
     const Lanes ln(log2s);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
@@ -617,6 +625,8 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
         for (int c = 0; c < n_sel; ++c)
             stage_q8(xq + c * xq_stride, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x, nullptr);
     }
+    int32_t next_id = 0;
+    if (hand) next_id = ids_table[(int64_t)((uint64_t)next % (uint64_t)out_rows) * n_sel + threadIdx.x];
     __syncthreads();
 
     double acc[1] = {0.0};
@@ -644,6 +654,8 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
         for (int s2 = 0; s2 < n_sel; ++s2) comb += (double)combine[s2] * (double)res[s2 * tpw * ln.R + i];
         yo[row] = (float)comb;
     }
+    if (counter && threadIdx.x == 0) *inc_step = next;
+    if (hand) ids_next[threadIdx.x] = next_id;
 }
 
 // --------------------------------------------------------------------------
@@ -662,7 +674,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     const int64_t* __restrict__ step, int n_tokens, const int32_t* __restrict__ ids_table,
     const float* __restrict__ logits_table, const float* __restrict__ x_table, int n_sel, int64_t k_pad,
     int64_t* __restrict__ cur, int32_t* __restrict__ ids_out, float* __restrict__ combine_out,
-    uint8_t* __restrict__ g_q8, float* __restrict__ gu_out) {
+    uint8_t* __restrict__ g_q8, float* __restrict__ gu_out, const int32_t* __restrict__ ids_next) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
     const Lanes ln(4);
@@ -670,7 +682,8 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     const int q = threadIdx.x >> 6;
     const int b = blockIdx.x, slot = blockIdx.y;
     const int64_t t = (int64_t)((uint64_t)*step % (uint64_t)n_tokens);
-    const int e = ids_table[t * n_sel + slot];
+    // ids_next, when given, already holds token t's ids (see the down kernel)
+    const int e = ids_next ? ids_next[slot] : ids_table[t * n_sel + slot];
     const bool e_ok = e >= 0 && e < n_experts;
     const bool work = e_ok && b < inter / 32;
     const int n_items = work ? 2 * passes : 0;
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
         for (int j = 0; j < n_sel; ++j) sum += __shfl(ex, j);
         if (i < n_sel) {
             combine_out[i] = (float)(ex / sum);
-            ids_out[i] = ids_table[t * n_sel + i];
+            ids_out[i] = ids_next ? ids_next[i] : ids_table[t * n_sel + i];
         }
         if (i == 0) *cur = t;
     }
@@ -1010,7 +1023,8 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
                                    const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
                                    float* y, const float* combine, float* y_out,
                                    const int64_t* out_row, int64_t out_rows, int64_t m, int64_t k,
-                                   int64_t* inc_step, hipStream_t stream) {
+                                   int64_t* inc_step, hipStream_t stream, const int32_t* ids_table,
+                                   int32_t* ids_next) {
     const int nsb = (int)(k / 256);
     const Q4KPlan p = plan_q4k_mult(m, nsb, combine ? 1 : n_sel);
     const int lds = (xq_stride ? n_sel : 1) * stage_bytes(nsb * 8);
@@ -1026,7 +1040,7 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
         const int grid = (p.n_tiles + tpw - 1) / tpw;
         MQ_LAUNCH(k_gemv_q4k_grouped_combine, dim3(grid), dim3(64 * n_sel), lds_c, stream, (const uint8_t*)w_all,
                   expert_bytes, n_experts, ids, n_sel, (const uint8_t*)xq, xq_stride, combine, y_out, out_row,
-                  out_rows, (int)m, nsb, p.log2s, p.passes, p.n_tiles, tpw, inc_step);
+                  out_rows, (int)m, nsb, p.log2s, p.passes, p.n_tiles, tpw, inc_step, ids_table, ids_next);
     } else if (combine) {
         const void* fn = (const void*)k_gemv_q4k_grouped<true>;
         MQ_LAUNCH((k_gemv_q4k_grouped<true>), dim3(balanced_grid(units, fn, lds)), dim3(256), lds, stream,
@@ -1047,12 +1061,24 @@ hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_exp
                               const int64_t* step, int n_tokens, const int32_t* ids_table,
                               const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
                               int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* ids_next) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
     MQ_LAUNCH(k_moe_gate_up, dim3((unsigned)(k_pad / 32), (unsigned)n_sel), dim3(512), lds, stream,
               (const uint8_t*)w_all, expert_bytes, n_experts, (int)inter, nsb, step, n_tokens, ids_table,
-              logits_table, x_table, n_sel, k_pad, cur, ids_out, combine_out, (uint8_t*)g_q8, gu_out);
+              logits_table, x_table, n_sel, k_pad, cur, ids_out, combine_out, (uint8_t*)g_q8, gu_out, ids_next);
+    return hipGetLastError();
+}
+
+__global__ void k_moe_prime(const int64_t* __restrict__ step, int n_tokens, const int32_t* __restrict__ ids_table,
+                            int n_sel, int32_t* __restrict__ ids_next) {
+    const int i = threadIdx.x;
+    if (i < n_sel) ids_next[i] = ids_table[(int64_t)((uint64_t)*step % (uint64_t)n_tokens) * n_sel + i];
+}
+
+hipError_t launch_moe_prime(const int64_t* step, int n_tokens, const int32_t* ids_table, int n_sel,
+                            int32_t* ids_next, hipStream_t stream) {
+    hipLaunchKernelGGL(k_moe_prime, dim3(1), dim3(64), 0, stream, step, n_tokens, ids_table, n_sel, ids_next);
     return hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int 
                                    const int32_t* ids, int n_sel, const void* xq, int64_t xq_stride,
                                    float* y, const float* combine, float* y_out,
                                    const int64_t* out_row, int64_t out_rows, int64_t m, int64_t k,
-                                   int64_t* inc_step, hipStream_t stream);
+                                   int64_t* inc_step, hipStream_t stream, const int32_t* ids_table = nullptr,
+                                   int32_t* ids_next = nullptr);
 // One routed-expert token's gate/up GEMVs with the SwiGLU -> q8_0 epilogue
 // (k_moe_gate_up): token t = *step mod n_tokens; writes cur = t, ids_out,
 // combine_out (softmax of the router logits) and g_q8 (n_sel columns of
@@ -87,7 +88,13 @@ hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_exp
                               const int64_t* step, int n_tokens, const int32_t* ids_table,
                               const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
                               int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
-                              hipStream_t stream);
+                              hipStream_t stream, const int32_t* ids_next = nullptr);
+// ids_next[0..n_sel) = the routing ids of token (*step mod n_tokens): set
+// wherever the expert chain's counter is set, kept current by the down
+// kernel that advances it (ids_next of launch_gemv_q4k_grouped), and read
+// by the next gate/up kernel (ids_next of launch_moe_gate_up).
+hipError_t launch_moe_prime(const int64_t* step, int n_tokens, const int32_t* ids_table, int n_sel,
+                            int32_t* ids_next, hipStream_t stream);
 hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* dump_isum, int64_t m,
                             int64_t k, hipStream_t stream);
 hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,

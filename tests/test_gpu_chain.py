@@ -352,6 +352,14 @@ def test_moe_chain(mq, o):
             s_abs += abs(float(c_ref[s])) * sa
         check_tolerance(yg[t], y_ref, s_abs, f"token {t}")
     assert g.info()["step"] == T
+    # a reset points the counter (and the routing the chain keeps for it) at
+    # token 5: the row is recomputed with the same bytes
+    import torch
+    g.y_table[5].zero_()
+    g.reset(5)
+    g.step(mq.MQ_GRAPH)
+    assert np.array_equal(to_host(g.y_table)[5].view(np.uint32), yg[5].view(np.uint32)), "reset to token 5"
+    assert g.info()["step"] == 6
     # several tokens per launch: the same bytes, tokens_per_launch tokens per call
     m4 = mq.MoEChain(*args, tokens_per_launch=4)
     assert m4.info()["captured"] and m4.info()["n_nodes"] == 8
