@@ -361,7 +361,7 @@ int mq_time_next_launches(const hipEvent_t* starts, const hipEvent_t* stops, int
 
 /* ---------------------------------------------------------------------------
  * Measurement: streaming-read probe.  Reads `bytes` at device pointer p once
- * (plain 16-byte loads, grid-stride, four in flight per lane) and writes the
+ * (plain 16-byte loads, one contiguous range per workgroup, four in flight per lane) and writes the
  * XOR of all its 32-bit words to the device uint32 *xor_out (overwritten; the
  * value lets a test check that every word was read).  It gives the read rate
  * this GPU reaches on a large buffer, against which the GEMVs' rates are
