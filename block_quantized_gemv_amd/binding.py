@@ -377,7 +377,9 @@ class DecodeChain:
     def host_logits(self):
         """numpy f32 [vocab] view of the chain's pinned host logits (MQ_HOST_LOGITS),
         or None.  It is overwritten by every step: synchronize before reading and
-        copy what must outlive the next step."""
+        copy what must outlive the next step.  The memory belongs to the chain:
+        the view is invalid once the chain is closed (or collected), so keep the
+        chain object alive while the view is used."""
         p = _vp()
         _check(lib().mq_chain_host_logits(self.handle, C.byref(p)))
         if not p.value:
