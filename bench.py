@@ -289,6 +289,20 @@ def cpu_baseline_decode(model, host_w, n_layers_sample):
             "cpu": _cpu_model()}
 
 
+def _pin_one_core():
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+
+
+def _cpu_line(nbytes, seconds, sample, **extra):
+    out = {"value": round(nbytes / seconds / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "seconds": round(seconds, 3), "sample": sample + ", single thread pinned to one core", "cpu": _cpu_model()}
+    out.update(extra)
+    return out
+
+
 def _cpu_model():
     try:
         for ln in open("/proc/cpuinfo"):
@@ -480,10 +494,24 @@ def run_single(args):
         us = [a.elapsed_time(b) * 1e3 for a, b in evs]
         res[mode] = {"us": round(float(np.median(us)), 3), "sem_us": round(sem(us), 4),
                      "GB_s": round(wl.algorithmic_bytes() / float(np.median(us)) / 1e3, 1)}
-    return {"metric": METRIC, "value": res["cold"]["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": res["cold"]["us"] / 1e3, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl.name, "m": wl.m, "k": wl.k, "seed": wl.seed}, "modes": res}
+    out = {"metric": METRIC, "value": res["cold"]["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": res["cold"]["us"] / 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+           "config": {"workload": wl.name, "m": wl.m, "k": wl.k, "seed": wl.seed}, "modes": res}
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.Oracle()
+        xqh = o.quantize_q8_0(synth.normal_f32(wl.seed, (synth.KEY_COLUMNS,), (wl.k,))).ravel()
+        _pin_one_core()
+        ts = []
+        for _ in range(20):
+            t0 = time.perf_counter()
+            o.gemv_q4k(base, wl.m, wl.k, xqh)
+            ts.append(time.perf_counter() - t0)
+        med = float(np.median(ts))
+        out["cpu_baseline"] = _cpu_line(wl.algorithmic_bytes(), med, "median of 20 runs of the whole GEMV",
+                                        us_per_gemv=round(med * 1e6, 1))
+    return out
 
 
 def run_batched(args):
@@ -493,9 +521,13 @@ def run_batched(args):
     wl = workloads.BATCHED
     dev = torch.device("cuda:0")
     rows = {}
+    host_gu = None
     for (m, k) in wl.shapes:
         reps = max(2, int(math.ceil(1.2e9 / workloads.q4k_bytes(m, k))))
-        W = torch.from_numpy(synth.q4k_matrix(wl.seed, (synth.KEY_MATRIX, m, k), m, k)).to(dev)
+        Wh = synth.q4k_matrix(wl.seed, (synth.KEY_MATRIX, m, k), m, k)
+        if (m, k) == (37888, 3584):
+            host_gu = Wh
+        W = torch.from_numpy(Wh).to(dev)
         Ws = [W] + [W.clone() for _ in range(reps - 1)]
         for n in (1,) + tuple(wl.ns):
             xq = mq.mq_quantize_q8_0(torch.from_numpy(synth.normal_f32(wl.seed, (synth.KEY_COLUMNS, n, k), (n, k))).to(dev))
@@ -517,10 +549,24 @@ def run_batched(args):
         del Ws, W
         torch.cuda.empty_cache()
     best = rows[f"37888x3584 n=8"]["GB_s"]
-    return {"metric": METRIC, "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": rows["37888x3584 n=8"]["us"] / 1e3, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl.name, "seed": wl.seed, "value_is": "7B gate/up n=8, cold"}, "shapes": rows}
+    out = {"metric": METRIC, "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": rows["37888x3584 n=8"]["us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+           "config": {"workload": wl.name, "seed": wl.seed, "value_is": "7B gate/up n=8, cold"}, "shapes": rows}
+    if not args.no_cpu_baseline and host_gu is not None:
+        import oracle
+        o = oracle.Oracle()
+        m, k, n = 37888, 3584, 8
+        xq = o.quantize_q8_0(synth.normal_f32(wl.seed, (synth.KEY_COLUMNS, n, k), (n, k))).reshape(n, -1)
+        _pin_one_core()
+        t0 = time.perf_counter()
+        for c in range(n):
+            o.gemv_q4k(host_gu, m, k, xq[c])
+        dt = time.perf_counter() - t0
+        nbytes = workloads.q4k_bytes(m, k) + workloads.q8_bytes(n, k) + 4 * m * n
+        out["cpu_baseline"] = _cpu_line(nbytes, dt, "the 37888x3584 gate/up shape with n = 8 columns, one oracle "
+                                        "GEMV per column", ms_per_call=round(dt * 1e3, 1))
+    return out
 
 
 def run_moe(args):
@@ -530,10 +576,9 @@ def run_moe(args):
     wl = workloads.MOE
     dev = torch.device("cuda:0")
     H, I = wl.hidden, wl.inter
-    gu = torch.from_numpy(np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 0), 2 * I, H)
-                                    for e in range(wl.n_experts)])).to(dev)
-    dn = torch.from_numpy(np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 1), H, I)
-                                    for e in range(wl.n_experts)])).to(dev)
+    gu_h = np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 0), 2 * I, H) for e in range(wl.n_experts)])
+    dn_h = np.stack([synth.q4k_matrix(wl.seed, (synth.KEY_EXPERT, e, 1), H, I) for e in range(wl.n_experts)])
+    gu, dn = torch.from_numpy(gu_h).to(dev), torch.from_numpy(dn_h).to(dev)
     T = wl.n_tokens
     ids, logits = synth.routing(wl.seed, T, wl.n_experts, wl.n_sel)
     X = synth.normal_f32(wl.seed, (synth.KEY_TOKEN_X,), (T, H))
@@ -586,13 +631,26 @@ def run_moe(args):
             arm.close()
     log(f"interleaved A/B: {ab}")
     nbytes = wl.token_weight_bytes()
-    return {"metric": METRIC, "value": round(nbytes / us / 1e3, 1), "unit": "GB/s", "n_gpus": 1, "steps": T,
-            "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-            "config": {"workload": wl.name, "seed": wl.seed, "tokens": T, "tokens_per_graph_launch": per,
-                       "bytes_per_token_padded": nbytes},
-            "us_per_token": round(us, 3), "event_us_per_token": round(a.elapsed_time(b) * 1e3 / (T // per * per), 3),
-            "tokens_per_s": round(1e6 / us, 1), "ab_interleaved": ab}
+    out = {"metric": METRIC, "value": round(nbytes / us / 1e3, 1), "unit": "GB/s", "n_gpus": 1, "steps": T,
+           "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+           "config": {"workload": wl.name, "seed": wl.seed, "tokens": T, "tokens_per_graph_launch": per,
+                      "bytes_per_token_padded": nbytes},
+           "us_per_token": round(us, 3), "event_us_per_token": round(a.elapsed_time(b) * 1e3 / (T // per * per), 3),
+           "tokens_per_s": round(1e6 / us, 1), "ab_interleaved": ab}
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.Oracle()
+        gu_all, dn_all = gu_h.reshape(-1), dn_h.reshape(-1)
+        n_cpu = 16
+        _pin_one_core()
+        t0 = time.perf_counter()
+        for t in range(n_cpu):
+            o.moe_token(gu_all, gu_h[0].nbytes, dn_all, dn_h[0].nbytes, ids[t], logits[t], X[t], H, I)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = _cpu_line(nbytes * n_cpu, dt, f"the first {n_cpu} of the {T} tokens",
+                                        ms_per_token=round(dt * 1e3 / n_cpu, 2))
+    return out
 
 
 def calibrate_copy(mib):
