@@ -55,7 +55,7 @@ __device__ __forceinline__ void load_sb(const uint8_t* __restrict__ blk, int jo,
 // of each dword, so both are decoded at once.
 struct SBScales {
     double d, dmin, m0, m1;
-    int sc0, sc1;
+    uint32_t scp;      // the two six-bit scales: sc0 | sc1 << 8
 };
 __device__ __forceinline__ void decode_scales(const u32x4& hdr, int sh, bool low, SBScales& s) {
     const uint32_t a2 = (hdr.y >> sh) & 0xFFFFu;
@@ -63,8 +63,11 @@ __device__ __forceinline__ void decode_scales(const u32x4& hdr, int sh, bool low
     const uint32_t c2 = (hdr.w >> sh) & 0xFFFFu;
     const uint32_t scp = low ? (a2 & 0x3F3Fu) : ((c2 & 0x0F0Fu) | ((a2 & 0xC0C0u) >> 2));
     const uint32_t mp = low ? (b2 & 0x3F3Fu) : (((c2 >> 4) & 0x0F0Fu) | ((b2 & 0xC0C0u) >> 2));
-    s.sc0 = (int)(scp & 0xFFu);
-    s.sc1 = (int)(scp >> 8);
+    // An empty asm hides scp's range, so that the byte masks where the
+    // scales are used survive and both products select 24-bit multiplies.
+    uint32_t opaque = scp;
+    asm("" : "+v"(opaque));
+    s.scp = opaque;
     s.m0 = (double)(int)(mp & 0xFFu);
     s.m1 = (double)(int)(mp >> 8);
     s.d = (double)f16_to_f32(hdr.x);
@@ -84,13 +87,19 @@ __device__ __forceinline__ void sb_isums(const SBLoad& L, const StagedPair& x, i
     i1 = b;
 }
 
-// d8_0*(d*sc0*i0 - dmin*m0*ysum_0) + d8_1*(d*sc1*i1 - dmin*m1*ysum_1) in f64.
-// Every product is exact (sc*isum < 2^22 and d8*ysum < 2^24 significant
-// bits against 53), so only the additions round.
-__device__ __forceinline__ double sb_value(const SBScales& s, const StagedPair& x, int i0, int i1) {
-    const double t = fma((double)__mul24(s.sc1, i1), x.d1, (double)__mul24(s.sc0, i0) * x.d0);
+// acc + d8_0*(d*sc0*i0 - dmin*m0*ysum_0) + d8_1*(d*sc1*i1 - dmin*m1*ysum_1)
+// in f64, as acc + d*t - dmin*u.  Every product is exact (sc*isum < 2^22 and
+// d8*ysum < 2^24 significant bits against 53), so only the additions round.
+// The caller passes d = dmin = 0 for an invalid item and points it at a
+// staged activation pair: t and u are then finite (six-bit scales and mins,
+// exact integer sums, finite activation scales), so it adds exactly zero.  The scales are masked where they are
+// used, so that both products select 24-bit multiplies.
+__device__ __forceinline__ double sb_accumulate(double acc, double d, double neg_dmin, const SBScales& s,
+                                                const StagedPair& x, int i0, int i1) {
+    const int sc0 = (int)(s.scp & 0xFFu), sc1 = (int)((s.scp >> 8) & 0xFFu);
+    const double t = fma((double)__mul24(sc1, i1), x.d1, (double)__mul24(sc0, i0) * x.d0);
     const double u = fma(s.m1, x.ds1, s.m0 * x.ds0);
-    return fma(s.d, t, -s.dmin * u);
+    return fma(neg_dmin, u, fma(d, t, acc));
 }
 
 // Per-lane constants of the lane layout.
@@ -123,14 +132,17 @@ __device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P,
                                         int32_t* __restrict__ dump, int64_t dump_row_off) {
     SBScales s;
     decode_scales(L.hdr, ln.sh, ln.low, s);
+    const double d = valid ? s.d : 0.0, neg_dmin = valid ? -s.dmin : 0.0;
+    // A lane past the row's last super-block would read an unstaged pair;
+    // an invalid lane reads pair j of super-block 0, so its terms are finite.
+    P = valid ? P : ln.j;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         StagedPair x;
         read_pair(lds + c * col_bytes, P, x, true);
         int i0, i1;
         sb_isums(L, x, i0, i1);
-        const double v = sb_value(s, x, i0, i1);
-        acc[c] += valid ? v : 0.0;
+        acc[c] = sb_accumulate(acc[c], d, neg_dmin, s, x, i0, i1);
         if (DUMP && valid) {
             dump[dump_row_off + 2 * P] = i0;
             dump[dump_row_off + 2 * P + 1] = i1;
@@ -172,10 +184,10 @@ __device__ __forceinline__ void group_item(const SBLoad& L, const Lanes& ln, int
     sb_item<NC, DUMP>(L, ln, P, valid, lds, col_bytes, acc, dump, dump_row_off);
 }
 
-// d_a*(d8_0*isum_0 - 8*d8_0*ysum_0) + d_b*(d8_1*isum_1 - 8*d8_1*ysum_1) in
-// f64: d8*isum has < 28 significant bits and 8*d8*ysum shares its scale, so
-// each bracket is exact, and so is its product with the block's f16 d; only
-// the final addition rounds.
+// acc + d_a*(d8_0*isum_0 - 8*d8_0*ysum_0) + d_b*(d8_1*isum_1 - 8*d8_1*ysum_1)
+// in f64: d8*isum has < 28 significant bits and 8*d8*ysum shares its scale,
+// so each bracket is exact, and so is its product with the block's f16 d;
+// only the two additions round.
 template <int NC, bool DUMP>
 __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, int P, bool valid,
                                            const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
@@ -187,8 +199,11 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
         q0[k] = __builtin_amdgcn_alignbyte(dw[k + 1], dw[k], 2);
         q1[k] = dw[5 + k];
     }
-    const double da = (double)f16_to_f32(dw[0]);
-    const double db = (double)f16_to_f32(dw[4] >> 16);
+    // zero scales for an invalid item, which reads a staged pair (finite
+    // brackets), so that it adds zero
+    const double da = valid ? (double)f16_to_f32(dw[0]) : 0.0;
+    const double db = valid ? (double)f16_to_f32(dw[4] >> 16) : 0.0;
+    P = valid ? P : ln.j;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         StagedPair x;
@@ -201,8 +216,7 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
             i1 = dot4(q1[k] & 0x0F0F0F0Fu, x.c[8 + k], i1);
             i1 = dot4((q1[k] >> 4) & 0x0F0F0F0Fu, x.c[12 + k], i1);
         }
-        const double v = fma(da, fma(x.d0, (double)i0, -8.0 * x.ds0), db * fma(x.d1, (double)i1, -8.0 * x.ds1));
-        acc[c] += valid ? v : 0.0;
+        acc[c] = fma(da, fma(x.d0, (double)i0, -8.0 * x.ds0), fma(db, fma(x.d1, (double)i1, -8.0 * x.ds1), acc[c]));
         if (DUMP && valid) {
             dump[dump_row_off + 2 * P] = i0;
             dump[dump_row_off + 2 * P + 1] = i1;
