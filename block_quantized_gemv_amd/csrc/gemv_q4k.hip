@@ -103,10 +103,17 @@ __device__ __forceinline__ double sb_accumulate(double acc, double d, double neg
 }
 
 // Per-lane constants of the lane layout.
+// A staged pair's LDS banks depend only on its index mod 16.  An invalid
+// lane reads pair (P & pmask) instead of P, which is staged (pairs 0..15 are
+// when the row has at least four super-blocks) and lies in the same banks
+// whenever pmask = 15, so that the redirection adds no bank conflicts.
+__device__ __forceinline__ int staged_pair_mask(int nsb) { return nsb >= 4 ? 15 : nsb >= 2 ? 7 : 3; }
+
 struct Lanes {
-    int lane, log2s, S, R, gpp, row_local, g, j, sh;
+    int lane, log2s, S, R, gpp, row_local, g, j, sh, pmask;
     bool low;
-    __device__ Lanes(int log2s_) {
+    __device__ Lanes(int log2s_, int nsb) {
+        pmask = staged_pair_mask(nsb);
         lane = threadIdx.x & 63;
         log2s = log2s_;
         S = 1 << log2s;
@@ -134,8 +141,8 @@ __device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P,
     decode_scales(L.hdr, ln.sh, ln.low, s);
     const double d = valid ? s.d : 0.0, neg_dmin = valid ? -s.dmin : 0.0;
     // A lane past the row's last super-block would read an unstaged pair;
-    // an invalid lane reads pair j of super-block 0, so its terms are finite.
-    P = valid ? P : ln.j;
+    // an invalid lane reads a staged one, so its terms are finite.
+    P = valid ? P : (P & ln.pmask);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         StagedPair x;
@@ -203,7 +210,7 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
     // brackets), so that it adds zero
     const double da = valid ? (double)f16_to_f32(dw[0]) : 0.0;
     const double db = valid ? (double)f16_to_f32(dw[4] >> 16) : 0.0;
-    P = valid ? P : ln.j;
+    P = valid ? P : (P & ln.pmask);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         StagedPair x;
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
     int M, int nsb, int log2s, int passes, int n_tiles, NormIn nin) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const Lanes ln(log2s);
+    const Lanes ln(log2s, nsb);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
     const int W = gridDim.x * (blockDim.x >> 6);
@@ -330,10 +337,10 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     double* __restrict__ part, int M, int nsb) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const Lanes ln(6);
     const int split = blockIdx.y;
     const int sb0 = 16 * split;
     const int nsb_s = min(16, nsb - sb0);
+    const Lanes ln(6, nsb_s);
     const int W = gridDim.x * (blockDim.x >> 6);
     const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int n_items = wave < M ? (M - 1 - wave) / W + 1 : 0;
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
     int n_tiles, int64_t* __restrict__ inc_step) {
     extern __shared__ __align__(16) uint8_t lds[];
     if (inc_step && blockIdx.x == 0 && threadIdx.x == 0) *inc_step += 1;
-    const Lanes ln(log2s);
+    const Lanes ln(log2s, nsb);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
     const int n_cols = xq_stride ? n_sel : 1;
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     __shared__ float gu_s[64];
     constexpr int WV = NORM ? 8 : 4;        // waves per workgroup
     constexpr int TPH = 8 / WV;             // tiles per half (gate or up) per wave
-    const Lanes ln(4);
+    const Lanes ln(4, nsb);
     const int nb = nsb * 8;
     const int passes = (nsb + 3) / 4;
     const int n_items = 2 * TPH * passes;
@@ -592,7 +599,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
     const bool hand = counter && ids_next && (int)threadIdx.x < n_sel;
     int64_t next = 0;
     if (counter && (threadIdx.x == 0 || hand)) next = *inc_step + 1;
-    const Lanes ln(log2s);
+    const Lanes ln(log2s, nsb);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
     const int slot = threadIdx.x >> 6;
@@ -691,7 +698,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     uint8_t* __restrict__ g_q8, float* __restrict__ gu_out, const int32_t* __restrict__ ids_next) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
-    const Lanes ln(4);
+    const Lanes ln(4, nsb);
     const int passes = (nsb + 3) / 4;
     const int q = threadIdx.x >> 6;
     const int b = blockIdx.x, slot = blockIdx.y;
