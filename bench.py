@@ -668,8 +668,8 @@ def calibrate_copy(mib):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              f"(the row-sharded multi-GPU design is described, not built)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the row-sharded multi-GPU design is described, not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
