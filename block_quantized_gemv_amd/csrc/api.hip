@@ -148,6 +148,9 @@ struct mq_chain {
     float* host_logits = nullptr;     // MQ_HOST_LOGITS: pinned f32 [vocab], written by the step's last node
     bool lazy = false;                // MQ_LAZY_CAPTURE: capture on the third MQ_GRAPH step
     int32_t* ids_next = nullptr;      // expert chain: routing ids of token (*step mod n_tokens)
+    double* gu_part = nullptr;        // decode step: row sums of the split gate/up blocks' halves
+    unsigned* gu_cnt = nullptr;       // decode step: one hand-over counter per split gate/up block
+    int gu_split = 0;                 // number of split gate/up blocks
     const int32_t* ids_table = nullptr;
     int n_tokens = 0, n_sel = 0;
     bool capture_tried = false;
@@ -211,6 +214,7 @@ int enqueue(mq_chain* c, hipStream_t s) {
 // Sets the step counter; the expert chain's next-token ids follow it.
 hipError_t set_step(mq_chain* c, int64_t step, hipStream_t stream) {
     hipError_t e = launch_set_i64(c->step, step, stream);
+    if (e == hipSuccess && c->gu_cnt) e = hipMemsetAsync(c->gu_cnt, 0, c->gu_split * sizeof(unsigned), stream);
     if (e == hipSuccess && c->ids_next)
         e = launch_moe_prime(c->step, c->n_tokens, c->ids_table, c->n_sel, c->ids_next, stream);
     return e;
@@ -543,6 +547,14 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const int64_t f32_alloc = keep ? c->f32_count : f32_layer;
     if (rc == MQ_OK) c->q8_trace = (uint8_t*)chain_alloc(c, q8_alloc, &rc);
     if (rc == MQ_OK) c->f32_trace = (float*)chain_alloc(c, f32_alloc * sizeof(float), &rc);
+    // gate/up blocks beyond a multiple of the CU count are split in two halves
+    // along K (launch_gemv_q4k_swiglu), with this hand-over space
+    const int gu_split = (d->flags & MQ_UNFUSED_GLUE) ? 0 : swiglu_split_blocks(I, H);
+    if (rc == MQ_OK && gu_split > 0) {
+        c->gu_part = (double*)chain_alloc(c, (size_t)gu_split * 128 * sizeof(double), &rc);
+        if (rc == MQ_OK) c->gu_cnt = (unsigned*)chain_alloc(c, (size_t)gu_split * sizeof(unsigned), &rc);
+        if (rc == MQ_OK) c->gu_split = gu_split;
+    }
     if (rc != MQ_OK) { chain_free(c); return rc; }
 
     const float eps = d->eps;
@@ -604,7 +616,9 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr, exact};
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s, fmt); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s, fmt); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s, fmt); });
+        double* gp = c->gu_part;
+        unsigned* gc = c->gu_cnt;
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s, fmt, gp, gc); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s, fmt); });
         h_prev = h;
     }

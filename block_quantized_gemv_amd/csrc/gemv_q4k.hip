@@ -505,16 +505,30 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
 template <int FMT, bool NORM>
 __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* __restrict__ gu_out,
-    uint8_t* __restrict__ g_q8, int inter, int nsb, NormIn nin) {
+    uint8_t* __restrict__ g_q8, int inter, int nsb, NormIn nin, double* __restrict__ part,
+    unsigned* __restrict__ cnt) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
+    __shared__ double gu_d[64];
     constexpr int WV = NORM ? 8 : 4;        // waves per workgroup
     constexpr int TPH = 8 / WV;             // tiles per half (gate or up) per wave
     const Lanes ln(4, nsb);
     const int nb = nsb * 8;
-    const int passes = (nsb + 3) / 4;
+    // The last NS output blocks are split along K into two halves (their
+    // first and last passes), run by workgroups 0 .. 2*NS-1 so that they
+    // start first; the other blocks follow, one workgroup each.  A half
+    // leaves its f64 row sums in `part`; the second half to finish adds the
+    // two (addition commutes, so the order of arrival does not matter) and
+    // writes the block.  NS = gridDim.x - inter/32.
+    const int nblk = inter / 32, NS = (int)gridDim.x - nblk;
+    const bool half = (int)blockIdx.x < 2 * NS;
+    const int hs = (int)blockIdx.x & 1;                     // which half
+    const int u = half ? nblk - NS + (int)blockIdx.x / 2 : (int)blockIdx.x - 2 * NS;
+    const int passes_all = (nsb + 3) / 4;
+    const int p0 = half && hs ? passes_all / 2 : 0;
+    const int passes = half ? (hs ? passes_all - passes_all / 2 : passes_all / 2) : passes_all;
     const int n_items = 2 * TPH * passes;
-    const int u = blockIdx.x, q = threadIdx.x >> 6;
+    const int q = threadIdx.x >> 6;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
 
     // item i: tile st = i / passes (st / TPH: 0 gate, 1 up; st % TPH: which
@@ -532,7 +546,7 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
         const bool past = i >= n_items;
         const int ii = past ? n_items - 1 : i;
         it.st = ii / passes;
-        it.pass = ii % passes;
+        it.pass = p0 + ii % passes;
         const int sb = it.pass * ln.gpp + ln.g;
         const bool inb = sb < nsb;
         it.valid = inb && !past;
@@ -559,20 +573,49 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     double acc[1] = {0.0};
     stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
         group_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
-        if (it.pass != passes - 1) return;
-        const float v = (float)group_sum_f64(acc[0], 4);
+        if (it.pass != p0 + passes - 1) return;
+        const double v = group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
         if ((ln.lane & 15) == 0) {
-            gu_s[(it.st / TPH) * 32 + local_of(it.st)] = v;
-            if (gu_out) gu_out[row_of(it.st)] = v;
+            const int r = (it.st / TPH) * 32 + local_of(it.st);
+            if (half) {
+                gu_d[r] = v;
+            } else {
+                gu_s[r] = (float)v;
+                if (gu_out) gu_out[row_of(it.st)] = (float)v;
+            }
         }
     });
     __syncthreads();
-    if (q == 0) {
-        const int i = ln.lane;
-        const float a = i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
-        quantize_lane(a, g_q8 + (int64_t)u * kQ8Bytes, i & 31, i < 32);
+    if (q != 0) return;
+    const int i = ln.lane;
+    if (half) {
+        // Row sums of this half to `part`, then the block's counter; the
+        // second arrival reads the other half's sums.  The sums are stored
+        // and read with agent-scope accesses, which go through the L2 to the
+        // device's coherence point, so ordering needs only the wait for the
+        // stores' completion before the counter moves, and the reads are
+        // issued after the counter's value has returned.  Agent-scope fences
+        // would instead write back and invalidate the whole L2 of the XCD,
+        // once per half: that cost more than the split saves.
+        const int sblk = u - (nblk - NS);
+        double* mine = part + (int64_t)(2 * sblk + hs) * 64;
+        const double* other = part + (int64_t)(2 * sblk + (hs ^ 1)) * 64;
+        const double own = gu_d[i];
+        __hip_atomic_store(mine + i, own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        unsigned prev = 0;
+        if (i == 0) prev = __hip_atomic_fetch_add(cnt + sblk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        if (prev == 0) return;                  // the other half finishes the block
+        asm volatile("" ::: "memory");
+        const float v = (float)(own + __hip_atomic_load(other + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        gu_s[i] = v;
+        if (gu_out) gu_out[(i / 32) * inter + 32 * u + (i & 31)] = v;
+        if (i == 0) __hip_atomic_store(cnt + sblk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    const float a = i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
+    quantize_lane(a, g_q8 + (int64_t)u * kQ8Bytes, i & 31, i < 32);
 }
 
 // --------------------------------------------------------------------------
@@ -1022,22 +1065,33 @@ hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_
 
 template <int FMT>
 static hipError_t launch_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                int64_t inter, int64_t k, hipStream_t stream) {
+                                int64_t inter, int64_t k, hipStream_t stream, double* part, unsigned* cnt) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
-    if (nin)
-        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true>), dim3((unsigned)(inter / 32)), dim3(512), lds, stream,
-                  (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin);
-    else
-        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, false>), dim3((unsigned)(inter / 32)), dim3(256), lds, stream,
-                  (const uint8_t*)w, (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb, NormIn{});
+    const unsigned nblk = (unsigned)(inter / 32);
+    if (nin) {
+        const int ns = part && cnt ? swiglu_split_blocks(inter, k) : 0;
+        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true>), dim3(nblk + (unsigned)ns), dim3(512), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin, part, cnt);
+    } else {
+        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, false>), dim3(nblk), dim3(256), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb, NormIn{},
+                  (double*)nullptr, (unsigned*)nullptr);
+    }
     return hipGetLastError();
 }
 
+int swiglu_split_blocks(int64_t inter, int64_t k) {
+    const int64_t nblk = inter / 32, cus = device_cu_count();
+    const int64_t passes = (k / 256 + 3) / 4;
+    if (passes < 2 || nblk <= cus) return 0;
+    return (int)(nblk % cus);
+}
+
 hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                  int64_t inter, int64_t k, hipStream_t stream, int fmt) {
-    return fmt == kFmtQ4_0 ? launch_swiglu<kFmtQ4_0>(w, xq, nin, gu_out, g_q8, inter, k, stream)
-                           : launch_swiglu<kFmtQ4K>(w, xq, nin, gu_out, g_q8, inter, k, stream);
+                                  int64_t inter, int64_t k, hipStream_t stream, int fmt, double* part, unsigned* cnt) {
+    return fmt == kFmtQ4_0 ? launch_swiglu<kFmtQ4_0>(w, xq, nin, gu_out, g_q8, inter, k, stream, part, cnt)
+                           : launch_swiglu<kFmtQ4K>(w, xq, nin, gu_out, g_q8, inter, k, stream, part, cnt);
 }
 
 hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,

@@ -50,8 +50,15 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
 // [inter, 2*inter) up rows; writes Q8(silu(gate)*up) (inter/32 blocks) and,
 // if gu_out is set, the f32 GEMV outputs.  inter % 32 == 0.  The activation
 // is xq, or Q8(RMSNorm(x)) formed in the prologue when nin is set.
+// When the output blocks outnumber the CUs and part/cnt are given, the
+// surplus blocks (swiglu_split_blocks of them) are each computed as two
+// halves along K by two workgroups that hand over through part (128 doubles
+// per block) and cnt (one counter per block, zero before the launch and
+// left zero after it); see k_gemv_q4k_swiglu.
 hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                  int64_t inter, int64_t k, hipStream_t stream, int fmt = kFmtQ4K);
+                                  int64_t inter, int64_t k, hipStream_t stream, int fmt = kFmtQ4K,
+                                  double* part = nullptr, unsigned* cnt = nullptr);
+int swiglu_split_blocks(int64_t inter, int64_t k);
 // Workgroups and threads per workgroup for `units` equal work units of a
 // kernel whose workgroups each run a prologue of `prologue` per-thread
 // steps: about one workgroup per CU, of at most max_waves waves.

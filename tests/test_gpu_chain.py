@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (check_tolerance, log, model_weights, oracle_chain_parallel, q8_code_diff, to_dev,
+from gpu_helpers import (check_tolerance, log, model_weights, oracle_chain_parallel, oracle_gemv_parallel, q8_code_diff, to_dev,
                          to_host)
 
 pytestmark = pytest.mark.gpu
@@ -374,3 +374,51 @@ def test_moe_chain(mq, o):
         lz.step(mq.MQ_GRAPH)
     assert lz.info()["captured"] and lz.info()["step"] == T
     assert np.array_equal(to_host(lz.y_table).view(np.uint32), yg.view(np.uint32)), "lazy capture changed the bytes"
+
+
+def test_gate_up_split_blocks_7b_width(mq, o, pool):
+    """At 7B widths the gate/up kernel has 592 output blocks; the blocks beyond
+    a multiple of the CU count are each computed by two workgroups, one per
+    half of K, that hand over through a counter (k_gemv_q4k_swiglu).  One
+    layer: graph == eager, byte for byte, over six steps (the counters must be
+    back at zero after every launch); every gate/up row, split or not, within
+    the GEMV tolerance of the oracle on the q8_0 input the chain formed; and
+    the SwiGLU q8_0 vector equal to the oracle's quantization of the chain's
+    own gate/up values."""
+    import torch
+    from block_quantized_gemv_amd import synth, workloads
+    m = dataclasses.replace(workloads.DECODE_7B, n_layers=1)
+    H, I, QKV = m.hidden, m.inter, m.qkv_rows
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblk = I // 32
+    ns = nblk % cus if nblk > cus else 0
+    assert ns > 0, f"{nblk} gate/up blocks on {cus} CUs: no split blocks to test"
+    W = model_weights(m, 1)
+    Wd = _dev_weights(W)
+    X = synth.normal_f32(m.seed, (synth.KEY_STEP_INPUTS,), (3, H))
+    xd = to_dev(X)
+    g = mq.DecodeChain(m, Wd, xd, flags=mq.MQ_KEEP_INTERMEDIATES)
+    e = mq.DecodeChain(m, Wd, xd, flags=mq.MQ_KEEP_INTERMEDIATES | mq.MQ_EAGER_ONLY)
+    assert g.info()["captured"]
+    for i in range(6):
+        lg = to_host(g.step()).copy()
+        qg, fg = (to_host(t).copy() for t in g.trace())
+        le = to_host(e.step(mq.MQ_EAGER)).copy()
+        qe, fe = (to_host(t).copy() for t in e.trace())
+        assert _same(lg, le) and _same(qg, qe) and _same(fg, fe), f"graph != eager at step {i}"
+    qH = H // 32 * 34
+    qc = qg[2 * qH:3 * qH]
+    gu = fg[QKV + H:QKV + H + 2 * I]
+    y_ref, s_abs = oracle_gemv_parallel(o.gemv_q4k, W["gu"][0], 2 * I, H, qc, pool=pool)
+    rel, exact = check_tolerance(gu, y_ref, s_abs, "7B gate/up with split blocks")
+    first = 32 * (nblk - ns)
+    split_rows = np.concatenate([np.arange(first, I), I + np.arange(first, I)])
+    same_split = float(np.mean(gu[split_rows].view(np.uint32) ==
+                               np.asarray(y_ref, np.float32)[split_rows].view(np.uint32)))
+    log(f"  {ns} split blocks; gate/up max |dy|/S_abs {rel:.2e}; bit-identical to the oracle: "
+        f"all rows {exact:.5f}, split rows {same_split:.5f}")
+    gq = qg[3 * qH:3 * qH + I // 32 * 34]
+    want = np.asarray(o.quantize_q8_0(o.swiglu(gu)), np.uint8).ravel()
+    assert np.array_equal(gq, want), "SwiGLU q8_0 differs from the oracle's quantization of the same gate/up values"
+    g.close()
+    e.close()
