@@ -214,7 +214,7 @@ int enqueue(mq_chain* c, hipStream_t s) {
 // Sets the step counter; the expert chain's next-token ids follow it.
 hipError_t set_step(mq_chain* c, int64_t step, hipStream_t stream) {
     hipError_t e = launch_set_i64(c->step, step, stream);
-    if (e == hipSuccess && c->gu_cnt) e = hipMemsetAsync(c->gu_cnt, 0, c->gu_split * sizeof(unsigned), stream);
+    if (e == hipSuccess && c->gu_cnt) e = launch_zero_u32(c->gu_cnt, c->gu_split, stream);
     if (e == hipSuccess && c->ids_next)
         e = launch_moe_prime(c->step, c->n_tokens, c->ids_table, c->n_sel, c->ids_next, stream);
     return e;

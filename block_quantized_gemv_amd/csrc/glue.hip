@@ -49,6 +49,10 @@ __global__ __launch_bounds__(256) void k_swiglu_quantize(const float* __restrict
 
 __global__ void k_set_i64(int64_t* p, int64_t v) { *p = v; }
 
+__global__ void k_zero_u32(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 // ------------------------------------------------------------------ host ----
 
 hipError_t launch_quantize_q8_0(const float* x, void* xq, int64_t k, int n_cols, hipStream_t stream) {
@@ -75,6 +79,12 @@ hipError_t launch_swiglu_quantize(const float* gu, void* xq, int64_t inter, int 
 
 hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t stream) {
     hipLaunchKernelGGL(k_set_i64, dim3(1), dim3(1), 0, stream, p, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

@@ -116,6 +116,8 @@ hipError_t launch_rmsnorm_quantize(const float* x, void* xq, int64_t k, float ep
 hipError_t launch_swiglu_quantize(const float* gu, void* xq, int64_t inter, int n_cols, int64_t k_pad,
                                   hipStream_t stream);
 hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t stream);
+// p[0..n) = 0 with a kernel (no memset node when the stream is captured).
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 // XOR of the 32-bit words of bytes (multiple of 16) at p (16-byte aligned)
 // into *xor_out; workgroups <= 0 means one per CU.
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int workgroups,

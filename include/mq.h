@@ -292,8 +292,9 @@ int mq_chain_read_logits(const mq_chain* c, float* host_out, int64_t n, unsigned
  * (that step's copy overwrites it). */
 int mq_chain_host_logits(const mq_chain* c, const float** host_logits);
 /* Set the device step counter (enqueued on `stream` as kernels, capture-safe;
- * an expert chain also refreshes the routing ids it keeps for the token the
- * counter points at). */
+ * a decode-step chain also zeroes the hand-over counters of its split gate/up
+ * blocks, and an expert chain refreshes the routing ids it keeps for the
+ * token the counter points at). */
 int mq_chain_reset(mq_chain* c, int64_t step, hipStream_t stream);
 /* With MQ_KEEP_INTERMEDIATES: copy the last step's intermediates into the
  * caller's device buffers (either may be NULL): q8_out gets, per layer, the

@@ -406,6 +406,10 @@ def test_gate_up_split_blocks_7b_width(mq, o, pool):
         le = to_host(e.step(mq.MQ_EAGER)).copy()
         qe, fe = (to_host(t).copy() for t in e.trace())
         assert _same(lg, le) and _same(qg, qe) and _same(fg, fe), f"graph != eager at step {i}"
+    g.reset(0)
+    e.reset(0)
+    assert _same(to_host(g.step()).copy(), to_host(e.step(mq.MQ_EAGER)).copy()), "graph != eager after reset"
+    qg, fg = (to_host(t).copy() for t in g.trace())
     qH = H // 32 * 34
     qc = qg[2 * qH:3 * qH]
     gu = fg[QKV + H:QKV + H + 2 * I]
