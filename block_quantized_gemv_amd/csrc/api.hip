@@ -669,8 +669,18 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     const int64_t gstride = KP / 32 * kQ8Bytes;
     uint8_t* gq = rc == MQ_OK ? (uint8_t*)chain_alloc(c, (size_t)S * gstride, &rc) : nullptr;
     int32_t* ids_next = rc == MQ_OK ? (int32_t*)chain_alloc(c, 64 * sizeof(int32_t), &rc) : nullptr;
+    // gate/up's working blocks beyond a multiple of the CU count run as two
+    // halves along K (launch_moe_gate_up), with this hand-over space
+    const int gu_split = moe_split_blocks(d->n_sel, I, H);
+    if (rc == MQ_OK && gu_split > 0) {
+        c->gu_part = (double*)chain_alloc(c, (size_t)gu_split * 128 * sizeof(double), &rc);
+        if (rc == MQ_OK) c->gu_cnt = (unsigned*)chain_alloc(c, (size_t)gu_split * sizeof(unsigned), &rc);
+        if (rc == MQ_OK) c->gu_split = gu_split;
+    }
     if (rc != MQ_OK) { chain_free(c); return rc; }
     c->ids_next = ids_next;
+    double* gpart = c->gu_part;
+    unsigned* gcnt = c->gu_cnt;
     c->ids_table = d->ids_table;
     c->n_tokens = d->n_tokens;
     c->n_sel = S;
@@ -687,7 +697,7 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
         c->ops.push_back([=](hipStream_t s) {
             return launch_moe_gate_up(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, I, H, step, dd.n_tokens,
                                       dd.ids_table, dd.logits_table, dd.x_table, S, KP, cur, ids, comb, gq, nullptr,
-                                      s, ids_next);
+                                      s, ids_next, gpart, gcnt);
         });
         c->ops.push_back([=](hipStream_t s) {
             return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,

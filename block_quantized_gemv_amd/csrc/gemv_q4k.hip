@@ -738,13 +738,40 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     const int64_t* __restrict__ step, int n_tokens, const int32_t* __restrict__ ids_table,
     const float* __restrict__ logits_table, const float* __restrict__ x_table, int n_sel, int64_t k_pad,
     int64_t* __restrict__ cur, int32_t* __restrict__ ids_out, float* __restrict__ combine_out,
-    uint8_t* __restrict__ g_q8, float* __restrict__ gu_out, const int32_t* __restrict__ ids_next) {
+    uint8_t* __restrict__ g_q8, float* __restrict__ gu_out, const int32_t* __restrict__ ids_next,
+    int n_split, double* __restrict__ part, unsigned* __restrict__ cnt) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
+    __shared__ double gu_d[64];
     const Lanes ln(4, nsb);
-    const int passes = (nsb + 3) / 4;
     const int q = threadIdx.x >> 6;
-    const int b = blockIdx.x, slot = blockIdx.y;
+    // One workgroup per (slot, output block), in a 1-D grid.  As in
+    // k_gemv_q4k_swiglu, the last n_split working blocks (slot-major) run as
+    // two halves along K, workgroups 0 .. 2*n_split-1, which hand over
+    // through part/cnt; the other blocks, padding included, follow.
+    const int nbw = inter / 32, nbp = (int)(k_pad / 32), working = n_sel * nbw;
+    const int idx = blockIdx.x;
+    const bool half = idx < 2 * n_split;
+    const int hs = idx & 1;
+    int slot, b;
+    if (half) {
+        const int lin = working - n_split + idx / 2;
+        slot = lin / nbw;
+        b = lin - slot * nbw;
+    } else {
+        const int f = idx - 2 * n_split;
+        if (f < working - n_split) {
+            slot = f / nbw;
+            b = f - slot * nbw;
+        } else {
+            const int pz = f - (working - n_split), npad = nbp - nbw;
+            slot = pz / npad;
+            b = nbw + (pz - slot * npad);
+        }
+    }
+    const int passes_all = (nsb + 3) / 4;
+    const int p0 = half && hs ? passes_all / 2 : 0;
+    const int passes = half ? (hs ? passes_all - passes_all / 2 : passes_all / 2) : passes_all;
     const int64_t t = (int64_t)((uint64_t)*step % (uint64_t)n_tokens);
     // ids_next, when given, already holds token t's ids (see the down kernel)
     const int e = ids_next ? ids_next[slot] : ids_table[t * n_sel + slot];
@@ -766,7 +793,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
         const bool past = i >= n_items;
         const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
         it.st = ii / passes;
-        it.pass = ii % passes;
+        it.pass = p0 + ii % passes;
         const int sb = it.pass * ln.gpp + ln.g;
         const bool inb = n_items > 0 && sb < nsb;
         it.valid = inb && !past;
@@ -802,20 +829,42 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     double acc[1] = {0.0};
     stream_items<true>(n_items, A, B, fetch, [&](const Item& it) {
         group_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
-        if (it.pass != passes - 1) return;
-        const float v = (float)group_sum_f64(acc[0], 4);
+        if (it.pass != p0 + passes - 1) return;
+        const double v = group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
         if ((ln.lane & 15) == 0) {
-            gu_s[it.st * 32 + local] = v;
-            if (gu_out) gu_out[(int64_t)slot * 2 * inter + row_of(it.st)] = v;
+            if (half) {
+                gu_d[it.st * 32 + local] = v;
+            } else {
+                gu_s[it.st * 32 + local] = (float)v;
+                if (gu_out) gu_out[(int64_t)slot * 2 * inter + row_of(it.st)] = (float)v;
+            }
         }
     });
     __syncthreads();
-    if (q == 0) {
-        const int i = ln.lane;
-        const float a = work && i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
-        quantize_lane(a, g_q8 + ((int64_t)slot * (k_pad / 32) + b) * kQ8Bytes, i & 31, i < 32);
+    if (q != 0) return;
+    const int i = ln.lane;
+    if (half) {
+        // The hand-over of k_gemv_q4k_swiglu.  A half whose expert id is out
+        // of range has no items; its sums are zero, and so is the block.
+        const int sblk = idx / 2;
+        double* mine = part + (int64_t)(2 * sblk + hs) * 64;
+        const double* other = part + (int64_t)(2 * sblk + (hs ^ 1)) * 64;
+        const double own = work ? gu_d[i] : 0.0;
+        __hip_atomic_store(mine + i, own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        unsigned prev = 0;
+        if (i == 0) prev = __hip_atomic_fetch_add(cnt + sblk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        if (prev == 0) return;
+        asm volatile("" ::: "memory");
+        const float v = (float)(own + __hip_atomic_load(other + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        gu_s[i] = v;
+        if (gu_out && work) gu_out[(int64_t)slot * 2 * inter + (i / 32) * inter + 32 * b + (i & 31)] = v;
+        if (i == 0) __hip_atomic_store(cnt + sblk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    const float a = work && i < 32 ? swiglu_value(gu_s[i], gu_s[32 + i]) : 0.0f;
+    quantize_lane(a, g_q8 + ((int64_t)slot * (k_pad / 32) + b) * kQ8Bytes, i & 31, i < 32);
 }
 
 // --------------------------------------------------------------------------
@@ -1136,13 +1185,22 @@ hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_exp
                               const int64_t* step, int n_tokens, const int32_t* ids_table,
                               const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
                               int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
-                              hipStream_t stream, const int32_t* ids_next) {
+                              hipStream_t stream, const int32_t* ids_next, double* part, unsigned* cnt) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
-    MQ_LAUNCH(k_moe_gate_up, dim3((unsigned)(k_pad / 32), (unsigned)n_sel), dim3(512), lds, stream,
+    const int ns = part && cnt ? moe_split_blocks(n_sel, inter, k) : 0;
+    MQ_LAUNCH(k_moe_gate_up, dim3((unsigned)((k_pad / 32) * n_sel + ns)), dim3(512), lds, stream,
               (const uint8_t*)w_all, expert_bytes, n_experts, (int)inter, nsb, step, n_tokens, ids_table,
-              logits_table, x_table, n_sel, k_pad, cur, ids_out, combine_out, (uint8_t*)g_q8, gu_out, ids_next);
+              logits_table, x_table, n_sel, k_pad, cur, ids_out, combine_out, (uint8_t*)g_q8, gu_out, ids_next,
+              ns, part, cnt);
     return hipGetLastError();
+}
+
+int moe_split_blocks(int n_sel, int64_t inter, int64_t k) {
+    const int64_t working = (int64_t)n_sel * (inter / 32), cus = device_cu_count();
+    const int64_t passes = (k / 256 + 3) / 4;
+    if (passes < 2 || working <= cus) return 0;
+    return (int)(working % cus);
 }
 
 __global__ void k_moe_prime(const int64_t* __restrict__ step, int n_tokens, const int32_t* __restrict__ ids_table,

@@ -95,7 +95,13 @@ hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_exp
                               const int64_t* step, int n_tokens, const int32_t* ids_table,
                               const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
                               int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
-                              hipStream_t stream, const int32_t* ids_next = nullptr);
+                              hipStream_t stream, const int32_t* ids_next = nullptr, double* part = nullptr,
+                              unsigned* cnt = nullptr);
+// Working blocks (n_sel * inter/32) beyond a multiple of the CU count, which
+// launch_moe_gate_up splits in two halves along K when part/cnt are given
+// (the hand-over of launch_gemv_q4k_swiglu: 128 doubles and one counter,
+// zero before and after a launch, per split block).
+int moe_split_blocks(int n_sel, int64_t inter, int64_t k);
 // ids_next[0..n_sel) = the routing ids of token (*step mod n_tokens): set
 // wherever the expert chain's counter is set, kept current by the down
 // kernel that advances it (ids_next of launch_gemv_q4k_grouped), and read
