@@ -376,7 +376,8 @@ def test_moe_chain(mq, o):
     assert np.array_equal(to_host(lz.y_table).view(np.uint32), yg.view(np.uint32)), "lazy capture changed the bytes"
 
 
-def test_gate_up_split_blocks_7b_width(mq, o, pool):
+@pytest.mark.parametrize("fmt", ["q4_K", "q4_0"])
+def test_gate_up_split_blocks_7b_width(mq, o, pool, fmt):
     """At 7B widths the gate/up kernel has 592 output blocks; the blocks beyond
     a multiple of the CU count are each computed by two workgroups, one per
     half of K, that hand over through a counter (k_gemv_q4k_swiglu).  One
@@ -388,6 +389,8 @@ def test_gate_up_split_blocks_7b_width(mq, o, pool):
     import torch
     from block_quantized_gemv_amd import synth, workloads
     m = dataclasses.replace(workloads.DECODE_7B, n_layers=1)
+    if fmt == "q4_0":
+        m = dataclasses.replace(m, weight_format="q4_0")
     H, I, QKV = m.hidden, m.inter, m.qkv_rows
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nblk = I // 32
@@ -413,8 +416,9 @@ def test_gate_up_split_blocks_7b_width(mq, o, pool):
     qH = H // 32 * 34
     qc = qg[2 * qH:3 * qH]
     gu = fg[QKV + H:QKV + H + 2 * I]
-    y_ref, s_abs = oracle_gemv_parallel(o.gemv_q4k, W["gu"][0], 2 * I, H, qc, pool=pool)
-    rel, exact = check_tolerance(gu, y_ref, s_abs, "7B gate/up with split blocks")
+    gemv = o.gemv_q4_0 if fmt == "q4_0" else o.gemv_q4k
+    y_ref, s_abs = oracle_gemv_parallel(gemv, W["gu"][0], 2 * I, H, qc, pool=pool)
+    rel, exact = check_tolerance(gu, y_ref, s_abs, f"7B gate/up ({fmt}) with split blocks")
     first = 32 * (nblk - ns)
     split_rows = np.concatenate([np.arange(first, I), I + np.arange(first, I)])
     same_split = float(np.mean(gu[split_rows].view(np.uint32) ==
