@@ -618,7 +618,8 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s, fmt); });
         double* gp = c->gu_part;
         unsigned* gc = c->gu_cnt;
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s, fmt, gp, gc); });
+        const int gn = c->gu_split;
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s, fmt, gp, gc, gn); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s, fmt); });
         h_prev = h;
     }
@@ -681,6 +682,7 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
     c->ids_next = ids_next;
     double* gpart = c->gu_part;
     unsigned* gcnt = c->gu_cnt;
+    const int gsplit = c->gu_split;
     c->ids_table = d->ids_table;
     c->n_tokens = d->n_tokens;
     c->n_sel = S;
@@ -697,7 +699,7 @@ int mq_moe_create(const mq_moe_desc* d, hipStream_t stream, mq_chain** out) {
         c->ops.push_back([=](hipStream_t s) {
             return launch_moe_gate_up(dd.w_gu_all, dd.gu_expert_bytes, dd.n_experts, I, H, step, dd.n_tokens,
                                       dd.ids_table, dd.logits_table, dd.x_table, S, KP, cur, ids, comb, gq, nullptr,
-                                      s, ids_next, gpart, gcnt);
+                                      s, ids_next, gpart, gcnt, gsplit);
         });
         c->ops.push_back([=](hipStream_t s) {
             return launch_gemv_q4k_grouped(dd.w_dn_all, dd.dn_expert_bytes, dd.n_experts, ids, S, gq, gstride,

@@ -1114,12 +1114,15 @@ hipError_t launch_gemv_q4k_splitk(const void* w, const void* xq, int64_t xq_col_
 
 template <int FMT>
 static hipError_t launch_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                int64_t inter, int64_t k, hipStream_t stream, double* part, unsigned* cnt) {
+                                int64_t inter, int64_t k, hipStream_t stream, double* part, unsigned* cnt,
+                                int n_split) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
     const unsigned nblk = (unsigned)(inter / 32);
     if (nin) {
-        const int ns = part && cnt ? swiglu_split_blocks(inter, k) : 0;
+        // halves need two passes or more; the hand-over space is the caller's
+        const bool ok = part && cnt && n_split > 0 && n_split <= (int)nblk && (nsb + 3) / 4 >= 2;
+        const int ns = ok ? n_split : 0;
         MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true>), dim3(nblk + (unsigned)ns), dim3(512), lds, stream,
                   (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin, part, cnt);
     } else {
@@ -1138,9 +1141,10 @@ int swiglu_split_blocks(int64_t inter, int64_t k) {
 }
 
 hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
-                                  int64_t inter, int64_t k, hipStream_t stream, int fmt, double* part, unsigned* cnt) {
-    return fmt == kFmtQ4_0 ? launch_swiglu<kFmtQ4_0>(w, xq, nin, gu_out, g_q8, inter, k, stream, part, cnt)
-                           : launch_swiglu<kFmtQ4K>(w, xq, nin, gu_out, g_q8, inter, k, stream, part, cnt);
+                                  int64_t inter, int64_t k, hipStream_t stream, int fmt, double* part, unsigned* cnt,
+                                  int n_split) {
+    return fmt == kFmtQ4_0 ? launch_swiglu<kFmtQ4_0>(w, xq, nin, gu_out, g_q8, inter, k, stream, part, cnt, n_split)
+                           : launch_swiglu<kFmtQ4K>(w, xq, nin, gu_out, g_q8, inter, k, stream, part, cnt, n_split);
 }
 
 hipError_t launch_gemv_q4k_grouped(const void* w_all, int64_t expert_bytes, int n_experts,
@@ -1185,10 +1189,12 @@ hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_exp
                               const int64_t* step, int n_tokens, const int32_t* ids_table,
                               const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
                               int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
-                              hipStream_t stream, const int32_t* ids_next, double* part, unsigned* cnt) {
+                              hipStream_t stream, const int32_t* ids_next, double* part, unsigned* cnt,
+                              int n_split) {
     const int nsb = (int)(k / 256);
     const int lds = stage_bytes(nsb * 8);
-    const int ns = part && cnt ? moe_split_blocks(n_sel, inter, k) : 0;
+    const bool ok = part && cnt && n_split > 0 && n_split <= n_sel * (int)(inter / 32) && (nsb + 3) / 4 >= 2;
+    const int ns = ok ? n_split : 0;
     MQ_LAUNCH(k_moe_gate_up, dim3((unsigned)((k_pad / 32) * n_sel + ns)), dim3(512), lds, stream,
               (const uint8_t*)w_all, expert_bytes, n_experts, (int)inter, nsb, step, n_tokens, ids_table,
               logits_table, x_table, n_sel, k_pad, cur, ids_out, combine_out, (uint8_t*)g_q8, gu_out, ids_next,

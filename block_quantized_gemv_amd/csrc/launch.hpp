@@ -50,14 +50,14 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
 // [inter, 2*inter) up rows; writes Q8(silu(gate)*up) (inter/32 blocks) and,
 // if gu_out is set, the f32 GEMV outputs.  inter % 32 == 0.  The activation
 // is xq, or Q8(RMSNorm(x)) formed in the prologue when nin is set.
-// When the output blocks outnumber the CUs and part/cnt are given, the
-// surplus blocks (swiglu_split_blocks of them) are each computed as two
-// halves along K by two workgroups that hand over through part (128 doubles
-// per block) and cnt (one counter per block, zero before the launch and
-// left zero after it); see k_gemv_q4k_swiglu.
+// With part/cnt and n_split > 0 (normally swiglu_split_blocks, taken when
+// the caller sized part/cnt), the last n_split output blocks are each
+// computed as two halves along K by two workgroups that hand over through
+// part (128 doubles per block) and cnt (one counter per block, zero before
+// the launch and left zero after it); see k_gemv_q4k_swiglu.
 hipError_t launch_gemv_q4k_swiglu(const void* w, const void* xq, const NormIn* nin, float* gu_out, void* g_q8,
                                   int64_t inter, int64_t k, hipStream_t stream, int fmt = kFmtQ4K,
-                                  double* part = nullptr, unsigned* cnt = nullptr);
+                                  double* part = nullptr, unsigned* cnt = nullptr, int n_split = 0);
 int swiglu_split_blocks(int64_t inter, int64_t k);
 // Workgroups and threads per workgroup for `units` equal work units of a
 // kernel whose workgroups each run a prologue of `prologue` per-thread
@@ -96,11 +96,11 @@ hipError_t launch_moe_gate_up(const void* w_all, int64_t expert_bytes, int n_exp
                               const float* logits_table, const float* x_table, int n_sel, int64_t k_pad,
                               int64_t* cur, int32_t* ids_out, float* combine_out, void* g_q8, float* gu_out,
                               hipStream_t stream, const int32_t* ids_next = nullptr, double* part = nullptr,
-                              unsigned* cnt = nullptr);
+                              unsigned* cnt = nullptr, int n_split = 0);
 // Working blocks (n_sel * inter/32) beyond a multiple of the CU count, which
-// launch_moe_gate_up splits in two halves along K when part/cnt are given
-// (the hand-over of launch_gemv_q4k_swiglu: 128 doubles and one counter,
-// zero before and after a launch, per split block).
+// launch_moe_gate_up splits in two halves along K when given part/cnt sized
+// for them and n_split (the hand-over of launch_gemv_q4k_swiglu: 128 doubles
+// and one counter, zero before and after a launch, per split block).
 int moe_split_blocks(int n_sel, int64_t inter, int64_t k);
 // ids_next[0..n_sel) = the routing ids of token (*step mod n_tokens): set
 // wherever the expert chain's counter is set, kept current by the down
