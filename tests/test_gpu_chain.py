@@ -376,25 +376,17 @@ def test_moe_chain(mq, o):
     assert np.array_equal(to_host(lz.y_table).view(np.uint32), yg.view(np.uint32)), "lazy capture changed the bytes"
 
 
-@pytest.mark.parametrize("fmt", ["q4_K", "q4_0"])
-def test_gate_up_split_blocks_7b_width(mq, o, pool, fmt):
-    """At 7B widths the gate/up kernel has 592 output blocks; the blocks beyond
-    a multiple of the CU count are each computed by two workgroups, one per
-    half of K, that hand over through a counter (k_gemv_q4k_swiglu).  One
-    layer: graph == eager, byte for byte, over six steps (the counters must be
-    back at zero after every launch); every gate/up row, split or not, within
-    the GEMV tolerance of the oracle on the q8_0 input the chain formed; and
-    the SwiGLU q8_0 vector equal to the oracle's quantization of the chain's
-    own gate/up values."""
+def _split_case(mq, o, pool, m, what):
+    """Graph == eager over six steps and a reset, every gate/up row within the
+    GEMV tolerance of the oracle (logged: how many are bit-identical), and the
+    SwiGLU q8_0 vector equal to the oracle's quantization of the chain's own
+    gate/up values, for a one-layer chain whose gate/up has split blocks."""
     import torch
-    from block_quantized_gemv_amd import synth, workloads
-    m = dataclasses.replace(workloads.DECODE_7B, n_layers=1)
-    if fmt == "q4_0":
-        m = dataclasses.replace(m, weight_format="q4_0")
+    from block_quantized_gemv_amd import synth
     H, I, QKV = m.hidden, m.inter, m.qkv_rows
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nblk = I // 32
-    ns = nblk % cus if nblk > cus else 0
+    ns = nblk % cus if nblk > cus and (H // 256 + 3) // 4 >= 2 else 0
     assert ns > 0, f"{nblk} gate/up blocks on {cus} CUs: no split blocks to test"
     W = model_weights(m, 1)
     Wd = _dev_weights(W)
@@ -416,9 +408,9 @@ def test_gate_up_split_blocks_7b_width(mq, o, pool, fmt):
     qH = H // 32 * 34
     qc = qg[2 * qH:3 * qH]
     gu = fg[QKV + H:QKV + H + 2 * I]
-    gemv = o.gemv_q4_0 if fmt == "q4_0" else o.gemv_q4k
+    gemv = o.gemv_q4_0 if getattr(m, "weight_format", "q4_K") == "q4_0" else o.gemv_q4k
     y_ref, s_abs = oracle_gemv_parallel(gemv, W["gu"][0], 2 * I, H, qc, pool=pool)
-    rel, exact = check_tolerance(gu, y_ref, s_abs, f"7B gate/up ({fmt}) with split blocks")
+    rel, exact = check_tolerance(gu, y_ref, s_abs, f"{what} gate/up with split blocks")
     first = 32 * (nblk - ns)
     split_rows = np.concatenate([np.arange(first, I), I + np.arange(first, I)])
     same_split = float(np.mean(gu[split_rows].view(np.uint32) ==
@@ -430,3 +422,25 @@ def test_gate_up_split_blocks_7b_width(mq, o, pool, fmt):
     assert np.array_equal(gq, want), "SwiGLU q8_0 differs from the oracle's quantization of the same gate/up values"
     g.close()
     e.close()
+
+
+@pytest.mark.parametrize("fmt", ["q4_K", "q4_0"])
+def test_gate_up_split_blocks_7b_width(mq, o, pool, fmt):
+    """At 7B widths the gate/up kernel has 592 output blocks; the blocks beyond
+    a multiple of the CU count are each computed by two workgroups, one per
+    half of K, that hand over through a counter (k_gemv_q4k_swiglu)."""
+    from block_quantized_gemv_amd import workloads
+    m = dataclasses.replace(workloads.DECODE_7B, n_layers=1)
+    if fmt == "q4_0":
+        m = dataclasses.replace(m, weight_format="q4_0")
+    _split_case(mq, o, pool, m, f"7B {fmt}")
+
+
+@pytest.mark.parametrize("inter", [8448, 16128])
+def test_gate_up_split_block_counts(mq, o, pool, inter):
+    """Few and many split blocks: hidden 1280 (two passes over K), 264 and 504
+    gate/up blocks, so 8 and 248 of them split on a 256-CU GPU."""
+    from block_quantized_gemv_amd import workloads
+    m = dataclasses.replace(workloads.DECODE_7B, n_layers=1, hidden=1280, qkv_rows=1280 + 256, inter=inter,
+                            vocab=4096)
+    _split_case(mq, o, pool, m, f"hidden 1280, inter {inter}")
