@@ -67,6 +67,7 @@ SIGNATURES = {
     "mq_swiglu_quantize_q8_0": ([_vp, _vp, _i64, _int, _i64, _vp], _int),
     "mq_debug_gemv_q4k_q8_isums": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp], _int),
     "mq_debug_gemv_q8_0_q8_isums": ([_vp, _vp, _vp, _vp, _i64, _i64, _vp], _int),
+    "mq_debug_gate_up_swiglu": ([_vp, _vp, _f32, _vp, _vp, _i64, _i64, _int, _vp, _vp, _int, _vp], _int),
     "mq_chain_create": ([C.POINTER(ChainDesc), _vp, C.POINTER(_vp)], _int),
     "mq_decode_chain": ([_vp, _int, _vp], _int),
     "mq_chain_info": ([_vp, C.POINTER(_int), C.POINTER(_int), C.POINTER(_i64)], _int),
@@ -77,6 +78,8 @@ SIGNATURES = {
     "mq_read_to_host": ([_vp, _vp, _i64, _u32, _vp], _int),
     "mq_readback_stats": ([C.POINTER(_i64), C.POINTER(_i64), C.POINTER(_i64), C.POINTER(_int)], _int),
     "mq_readback_release": ([], _int),
+    "mq_workspace_stats": ([C.POINTER(_i64), C.POINTER(_int), C.POINTER(_int)], _int),
+    "mq_workspace_release": ([], _int),
     "mq_chain_trace_sizes": ([_vp, C.POINTER(_i64), C.POINTER(_i64)], _int),
     "mq_chain_read_trace": ([_vp, _vp, _vp, _vp], _int),
     "mq_chain_destroy": ([_vp], _int),
@@ -202,6 +205,16 @@ def mq_readback_release():
     _check(lib().mq_readback_release())
 
 
+def mq_workspace_stats():
+    b, n, r = _i64(), _int(), _int()
+    _check(lib().mq_workspace_stats(C.byref(b), C.byref(n), C.byref(r)))
+    return {"bytes": b.value, "streams": n.value, "retired": r.value}
+
+
+def mq_workspace_release():
+    _check(lib().mq_workspace_release())
+
+
 def mq_quantize_q8_0(x, xq=None, stream=None):
     """x: f32 [k] or [n, k] -> uint8 [n*(k/32)*34] q8_0 blocks (written into xq if given)."""
     k = x.shape[-1]
@@ -322,6 +335,21 @@ def mq_debug_gemv_q8_0_q8_isums(w, xq, m, k, stream=None):
                                              _ptr(xq, torch.uint8, q8_bytes(1, k), "xq"), _ptr(y), _ptr(isum),
                                              m, k, _stream(stream)))
     return y, isum
+
+
+def mq_debug_gate_up_swiglu(w, x, inter, k, n_split=0, part=None, cnt=None, weight_format="q4_K", eps=1e-6,
+                            stream=None):
+    """The fused gate/up kernel alone: returns (gu f32 [2*inter], g q8_0 bytes)."""
+    dev = w.device
+    fmt = MQ_FMT_Q4_0 if weight_format == "q4_0" else MQ_FMT_Q4_K
+    wb = q4_0_bytes(2 * inter, k) if fmt == MQ_FMT_Q4_0 else q4k_bytes(2 * inter, k)
+    gu = torch.empty(2 * inter, dtype=torch.float32, device=dev)
+    g = torch.empty(q8_bytes(1, inter), dtype=torch.uint8, device=dev)
+    _check(lib().mq_debug_gate_up_swiglu(_ptr(w, torch.uint8, wb, "w"), _ptr(x, torch.float32, 4 * k, "x"), eps,
+                                         _ptr(gu), _ptr(g), inter, k, n_split,
+                                         _ptr(part, torch.float64, 128 * 8 * n_split, "part"),
+                                         _ptr(cnt, torch.int32, 4 * n_split, "cnt"), fmt, _stream(stream)))
+    return gu, g
 
 
 class DecodeChain:

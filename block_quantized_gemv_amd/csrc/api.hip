@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <functional>
 #include <mutex>
@@ -20,7 +21,7 @@ using namespace mq;
 namespace {
 
 thread_local std::string g_err;
-unsigned g_fault = MQ_FAULT_NONE;
+std::atomic<unsigned> g_fault{MQ_FAULT_NONE};
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -68,38 +69,50 @@ bool capturing(hipStream_t s) {
     return st != hipStreamCaptureStatusNone;
 }
 
-// Device workspace for the split-k partials, one per device, grown on demand.
+// Device workspaces for the split-k partials of the 4-bit GEMVs: one per
+// (device, stream), so that calls on different streams never share partials
+// (calls on one stream are ordered by it).  A workspace only grows, and the
+// buffer it outgrows is kept until mq_workspace_release: a call already
+// enqueued, or a graph captured earlier, may still be using it.
 struct Workspace {
-    void* ptr = nullptr;
-    size_t bytes = 0;
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
 };
 std::mutex g_ws_mu;
-Workspace g_ws[64];
+std::vector<Workspace> g_ws;
+std::vector<Workspace> g_ws_retired;
 
 int workspace(size_t need, hipStream_t stream, void** out) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MQ_ERR_HIP, "hipGetDevice failed");
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MQ_ERR_HIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_ws_mu);
-    Workspace& ws = g_ws[dev];
-    if (ws.bytes < need) {
-        if (capturing(stream))
-            return fail(MQ_ERR_CAPTURE, "workspace must grow to %zu bytes while the stream is captured; "
-                        "call once outside capture first", need);
-        if (ws.ptr) {
-            hipError_t e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_status(e, "hipDeviceSynchronize");
-            (void)hipFree(ws.ptr);
-            ws.ptr = nullptr;
-            ws.bytes = 0;
-        }
-        size_t b = need < (1u << 20) ? (1u << 20) : need;
-        if (hipMalloc(&ws.ptr, b) != hipSuccess) {
-            ws.ptr = nullptr;
-            return fail(MQ_ERR_NOMEM, "hipMalloc(%zu) for the workspace failed", b);
-        }
-        ws.bytes = b;
+    Workspace* ws = nullptr;
+    for (Workspace& w : g_ws)
+        if (w.dev == dev && w.stream == stream) ws = &w;
+    if (ws && ws->bytes >= need) {
+        *out = ws->ptr;
+        return MQ_OK;
     }
-    *out = ws.ptr;
+    if (capturing(stream))
+        return fail(MQ_ERR_CAPTURE, "the split-k workspace of this stream must grow to %zu bytes while the stream "
+                    "is captured; call once outside capture first", need);
+    size_t b = (size_t)1 << 20;
+    while (b < need) b <<= 1;
+    void* p = nullptr;
+    if (hipMalloc(&p, b) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MQ_ERR_NOMEM, "hipMalloc(%zu) for the split-k workspace failed", b);
+    }
+    if (ws) {
+        g_ws_retired.push_back(*ws);
+        ws->ptr = p;
+        ws->bytes = b;
+    } else {
+        g_ws.push_back(Workspace{dev, stream, p, b});
+    }
+    *out = p;
     return MQ_OK;
 }
 
@@ -182,15 +195,14 @@ void chain_free(mq_chain* c) {
 // copy to the step.  Failure to pin leaves the chain without it (one
 // warning per process).
 void add_host_logits(mq_chain* c) {
-    static bool warned = false;
+    static std::atomic<bool> warned{false};
     void* p = nullptr;
     const size_t bytes = (size_t)c->vocab * sizeof(float);
     const hipError_t e = (g_fault & MQ_FAULT_PINNED_ALLOC) ? hipErrorOutOfMemory
                                                           : hipHostMalloc(&p, bytes, hipHostMallocDefault);
     if (e != hipSuccess) {
         (void)hipGetLastError();
-        if (!warned) {
-            warned = true;
+        if (!warned.exchange(true)) {
             fprintf(stderr, "mq: pinning the %zu-byte host logits of a chain failed (%s); the chain has no host copy\n",
                     bytes, hipGetErrorString(e));
         }
@@ -388,6 +400,38 @@ int mq_readback_release(void) {
     return hip_status(e, "freeing the pinned readback buffer");
 }
 
+int mq_workspace_release(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if (g_ws.empty() && g_ws_retired.empty()) return ok();
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(MQ_ERR_HIP, "hipGetDevice failed");
+    hipError_t first = hipSuccess;
+    auto free_all = [&](std::vector<Workspace>& v) {
+        for (const Workspace& w : v) {
+            hipError_t e = hipSetDevice(w.dev);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+            if (e == hipSuccess) e = hipFree(w.ptr);
+            if (first == hipSuccess) first = e;
+        }
+        v.clear();
+    };
+    free_all(g_ws);
+    free_all(g_ws_retired);
+    (void)hipSetDevice(cur);
+    return hip_status(first, "freeing the split-k workspaces");
+}
+
+int mq_workspace_stats(int64_t* bytes, int* n_streams, int* n_retired) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int64_t total = 0;
+    for (const Workspace& w : g_ws) total += (int64_t)w.bytes;
+    for (const Workspace& w : g_ws_retired) total += (int64_t)w.bytes;
+    if (bytes) *bytes = total;
+    if (n_streams) *n_streams = (int)g_ws.size();
+    if (n_retired) *n_retired = (int)g_ws_retired.size();
+    return ok();
+}
+
 int mq_test_set_fault(unsigned fault_mask) {
     g_fault = fault_mask;
     return ok();
@@ -500,6 +544,25 @@ int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t
     CHECK_SHAPE(m >= 1 && m <= kMaxRows, "m out of range");
     CHECK_SHAPE(k >= 64 && k % 64 == 0 && stage_bytes((int)(k / 32)) <= kMaxStageLds, "bad k");
     return hip_status(launch_gemv_q8_0(w, xq, y, isum, m, k, stream), "dump GEMV launch");
+}
+
+int mq_debug_gate_up_swiglu(const void* w, const float* x, float eps, float* gu_out, void* g_q8, int64_t inter,
+                            int64_t k, int n_split, double* part, unsigned* cnt, int weight_format,
+                            hipStream_t stream) {
+    CHECK_ARG(w && x && g_q8, "null pointer");
+    CHECK_ARG(aligned(w, 16) && aligned(x, 16) && aligned(g_q8, 2) && aligned(gu_out, 4), "misaligned pointer");
+    CHECK_ARG(weight_format == MQ_FMT_Q4_K || weight_format == MQ_FMT_Q4_0, "unknown weight_format %d",
+              weight_format);
+    CHECK_ARG(n_split >= 0, "n_split must be >= 0");
+    CHECK_SHAPE(inter >= 32 && inter % 32 == 0 && 2 * inter <= kMaxRows, "inter must be a positive multiple of 32");
+    CHECK_SHAPE(k >= 256 && k % 256 == 0 && stage_bytes((int)(k / 32)) <= kMaxStageLds,
+                "k must be a positive multiple of 256 that fits in LDS");
+    CHECK_ARG(eps >= 0.0f, "eps must be >= 0");
+    const NormIn nin{x, nullptr, 1, eps, nullptr, nullptr, 0};
+    const int fmt = weight_format == MQ_FMT_Q4_0 ? kFmtQ4_0 : kFmtQ4K;
+    return hip_status(launch_gemv_q4k_swiglu(w, nullptr, &nin, gu_out, g_q8, inter, k, stream, fmt, part, cnt,
+                                             n_split),
+                      "gate/up launch");
 }
 
 int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) {

@@ -24,6 +24,8 @@
 // which lets the compiler wait only for the item it is about to use.
 #include <hip/hip_ext.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "common.hpp"
@@ -904,30 +906,39 @@ bool take_next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
         }                                                                                       \
     } while (0)
 
+// Both caches below are filled on first use and may be read and filled by
+// several host threads at once: the CU count per device is an atomic, the
+// occupancy table sits behind a mutex.
 int device_cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
-// Resident 256-thread workgroups per CU for a kernel with `lds` bytes of
-// dynamic LDS (occupancy query, cached).
-static int blocks_per_cu(const void* fn, int lds) {
-    struct Entry { const void* fn; int lds, n; };
-    static Entry cache[256];
-    static int used = 0;
-    for (int i = 0; i < used; ++i)
-        if (cache[i].fn == fn && cache[i].lds == lds) return cache[i].n;
+// Resident workgroups of `threads` threads per CU for kernel fn with `lds`
+// bytes of dynamic LDS on the current device (occupancy query, cached).
+int blocks_per_cu(const void* fn, int threads, int lds) {
+    struct Entry { int dev; const void* fn; int threads, lds, n; };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry& e : cache)
+            if (e.dev == dev && e.fn == fn && e.threads == threads && e.lds == lds) return e.n;
+    }
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, lds) != hipSuccess || n <= 0) n = 2;
-    if (used < 256) cache[used++] = Entry{fn, lds, n};
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess || n <= 0) n = 2;
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back(Entry{dev, fn, threads, lds, n});
     return n;
 }
 
@@ -965,7 +976,7 @@ Q4KPlan plan_q4k(int64_t m, int nsb) { return plan_q4k_mult(m, nsb, 1); }
 // Waves to launch for `units` equal work units: all resident at once and
 // every wave with the same number of units (or one fewer).
 static int balanced_grid(int64_t units, const void* fn, int lds) {
-    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, lds) * 4;
+    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, 256, lds) * 4;
     const int64_t k = (units + wmax - 1) / wmax;
     const int64_t waves = (units + k - 1) / k;
     const int64_t grid = (waves + 3) / 4;
@@ -1075,7 +1086,7 @@ static hipError_t launch_split_nc(const void* w, const void* xq, int64_t xq_col_
     const int n_split = (nsb + 15) / 16;
     const int lds = NC * kStageGroupBytes;
     const void* fn = (const void*)k_gemv_q4k_splitk<FMT, NC>;
-    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, lds) * 4 / n_split;
+    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, 256, lds) * 4 / n_split;
     const int64_t k = (m + (wmax > 0 ? wmax : 1) - 1) / (wmax > 0 ? wmax : 1);
     const int64_t waves = (m + k - 1) / k;
     const int gx = (int)((waves + 3) / 4);

@@ -141,24 +141,13 @@ Q8Plan plan_q8_0(int64_t m, int npairs) {
     return p;
 }
 
-static int q8_blocks_per_cu(const void* fn, int lds) {
-    static const void* cfn[8];
-    static int clds[8], cn[8], used = 0;
-    for (int i = 0; i < used; ++i)
-        if (cfn[i] == fn && clds[i] == lds) return cn[i];
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, lds) != hipSuccess || n <= 0) n = 2;
-    if (used < 8) { cfn[used] = fn; clds[used] = lds; cn[used] = n; ++used; }
-    return n;
-}
-
 hipError_t launch_gemv_q8_0(const void* w, const void* xq, float* y, int32_t* dump_isum, int64_t m,
                             int64_t k, hipStream_t stream) {
     const int npairs = (int)(k / 64);
     const Q8Plan p = plan_q8_0(m, npairs);
     const int lds = stage_bytes(2 * npairs);
     const void* fn = dump_isum ? (const void*)k_gemv_q8_0<true, false> : (const void*)k_gemv_q8_0<false, false>;
-    const int64_t wmax = (int64_t)device_cu_count() * q8_blocks_per_cu(fn, lds) * 4;
+    const int64_t wmax = (int64_t)device_cu_count() * blocks_per_cu(fn, 256, lds) * 4;
     const int64_t per = (p.n_tiles + wmax - 1) / wmax;
     const int64_t waves = (p.n_tiles + per - 1) / per;
     const int grid = (int)((waves + 3) / 4);

@@ -24,7 +24,10 @@ struct Q8Plan {
 };
 Q8Plan plan_q8_0(int64_t m, int npairs);
 
+// CUs of the current device, and resident workgroups per CU of a kernel;
+// both cached, safe to call from several host threads at once.
 int device_cu_count();
+int blocks_per_cu(const void* fn, int threads, int lds);
 
 // Events for the next GEMV launches of this thread (see mq_time_next_launches).
 void set_next_launch_events(const hipEvent_t* starts, const hipEvent_t* stops, int n);

@@ -23,7 +23,11 @@
  *    call (host memory owned by the library, valid until the next call).
  *  - No exceptions cross this boundary; the library never exits or aborts.
  *  - Threads: the stateless entry points may be called from several host
- *    threads at once.  A chain object is not synchronized: calls on one
+ *    threads at once, on the same or different streams: the library's
+ *    caches (CU counts, occupancy) are guarded, and the split-k workspace
+ *    of the batched GEMVs is kept per (device, stream), so calls on
+ *    different streams never share it and calls on one stream are ordered
+ *    by that stream.  A chain object is not synchronized: calls on one
  *    chain (step, reset, info, reads) must not overlap.  mq_read_to_host
  *    serializes on its mutex.  mq_test_set_fault is a process-wide switch
  *    for single-threaded tests.
@@ -93,14 +97,28 @@ int mq_gemv_q4k_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k
  * Batched q4_K x q8_0 GEMV, 1 <= n <= 8 activation columns, weights streamed
  * once for all columns.  xq: [n][k/32] q8_0 blocks (column c at
  * xq + c*(k/32)*34); y: f32 [m][n] row-major, y[r*n + c].
- * Same arithmetic per column as mq_gemv_q4k_q8.  For large n*k the kernel
- * splits k across workgroups and sums the f64 partials in a second pass in
- * split order; the partials live in a device workspace the library grows on
- * demand (MQ_ERR_CAPTURE if it must grow while `stream` is being captured;
- * call once outside capture first).
+ * Same arithmetic per column as mq_gemv_q4k_q8.  For large n*k (the
+ * columns do not fit in 64 KB of LDS) the kernel splits k across
+ * workgroups and sums the f64 partials in a second pass in split order;
+ * the partials (ceil(k/4096)*m*n doubles) live in a device workspace that
+ * the library keeps per (device, stream) and grows on demand to the next
+ * power of two (MQ_ERR_NOMEM if that allocation fails; MQ_ERR_CAPTURE if it
+ * must grow while `stream` is being captured: call once outside capture
+ * first).  A workspace that is outgrown is not freed, because work already
+ * enqueued or a graph captured earlier may still use it; all of them are
+ * freed by mq_workspace_release.
  */
 int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, int64_t k,
                            int n, hipStream_t stream);
+
+/* The split-k workspaces (see mq_gemv_q4k_q8_batched).  Host out-params
+ * (any may be NULL): bytes held in total, the (device, stream) pairs that
+ * have one, and the outgrown buffers still held. */
+int mq_workspace_stats(int64_t* bytes, int* n_streams, int* n_retired);
+/* Waits for each device that holds a workspace, then frees them all; the
+ * next split-k call allocates again.  The caller must not replay a graph
+ * captured with a split-k call after this (it would use freed memory). */
+int mq_workspace_release(void);
 
 /* ---------------------------------------------------------------------------
  * Grouped GEMV for routed experts.  For slot s < n_sel the expert is
@@ -186,6 +204,22 @@ int mq_debug_gemv_q8_0_q8_isums(const void* w, const void* xq, float* y, int32_t
  * LDS (k above about 55,000). */
 int mq_debug_gemv_q4_0_q8_isums(const void* w, const void* xq, float* y, int32_t* isum,
                                 int32_t* ysum, int64_t m, int64_t k, hipStream_t stream);
+
+/* The decode step's fused gate/up kernel on its own (a test hook):
+ * gu = W_gu Q8(RMSNorm(x)) with W_gu's 2*inter rows (gate rows, then up
+ * rows) over k = hidden, g_q8 = Q8(SwiGLU(gu)) (inter/32 blocks), gu_out
+ * (f32 [2*inter], may be NULL) the GEMV values.  x: f32 [k], 16-byte
+ * aligned.  With n_split > 0 the last n_split of the inter/32 output
+ * blocks are each computed as two halves along k by two workgroups that
+ * hand over through part (128 doubles per split block) and cnt (one
+ * unsigned per split block, zero before the call and left zero after it);
+ * the chain passes the surplus over a multiple of the CU count.  When the
+ * count does not fit the shape (n_split > inter/32, fewer than two passes
+ * over k, or part or cnt NULL) every block is computed whole.  Results are
+ * the same either way. */
+int mq_debug_gate_up_swiglu(const void* w, const float* x, float eps, float* gu_out, void* g_q8, int64_t inter,
+                            int64_t k, int n_split, double* part, unsigned* cnt, int weight_format,
+                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Decode-step chain: one decode step of a stand-in model, recorded once as a

@@ -72,24 +72,70 @@ def oracle_chain_parallel(o, model, W, h0, n_layers, pool):
     """The decode step composed from the oracle's stages (the composition is
     the one oracle.chain implements, pinned by pin_chain_structure and
     pin_chain_structure_q4_0), with the GEMV rows spread over threads.
-    Returns logits, s_abs, q8 trace, f32 trace."""
+    Returns logits, s_abs, q8 trace, f32 trace, and the f64 sum_i |w_i x_i|
+    of every f32 trace value (the per-row tolerance of its GEMV)."""
     H, I, eps = model.hidden, model.inter, model.eps
     gemv = o.gemv_q4_0 if getattr(model, "weight_format", "q4_K") == "q4_0" else o.gemv_q4k
     h = np.asarray(h0, np.float32)
-    q8s, f32s = [], []
+    q8s, f32s, sabs = [], [], []
     for l in range(n_layers):
         a = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel(); q8s.append(a)
-        t, _ = oracle_gemv_parallel(gemv, W["qkv"][l], model.qkv_rows, H, a, pool=pool)
+        t, st = oracle_gemv_parallel(gemv, W["qkv"][l], model.qkv_rows, H, a, pool=pool)
         b = o.quantize_q8_0(o.rmsnorm(t[:H], eps)).ravel(); q8s.append(b)
-        ov, _ = oracle_gemv_parallel(gemv, W["o"][l], H, H, b, pool=pool)
+        ov, so = oracle_gemv_parallel(gemv, W["o"][l], H, H, b, pool=pool)
         c = o.quantize_q8_0(o.rmsnorm(ov, eps)).ravel(); q8s.append(c)
-        gu, _ = oracle_gemv_parallel(gemv, W["gu"][l], 2 * I, H, c, pool=pool)
+        gu, sg = oracle_gemv_parallel(gemv, W["gu"][l], 2 * I, H, c, pool=pool)
         g = o.quantize_q8_0(o.swiglu(gu)).ravel(); q8s.append(g)
-        h, _ = oracle_gemv_parallel(gemv, W["down"][l], H, I, g, pool=pool)
+        h, sd = oracle_gemv_parallel(gemv, W["down"][l], H, I, g, pool=pool)
         f32s += [t, ov, gu, h]
+        sabs += [st, so, sg, sd]
     z = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel(); q8s.append(z)
     logits, s_abs = oracle_gemv_parallel(o.gemv_q8_0, W["lm"], model.vocab, H, z, pool=pool)
-    return logits, s_abs, np.concatenate(q8s), np.concatenate(f32s)
+    return logits, s_abs, np.concatenate(q8s), np.concatenate(f32s), np.concatenate(sabs)
+
+
+def trace_stages(model, n_layers):
+    """Names and (q8 byte range | f32 value range) of every stage of a chain
+    trace, in step order: per layer the q8_0 inputs of QKV, O, gate/up and
+    down and the f32 outputs of the four GEMVs; then the lm_head input."""
+    H, I, Q = model.hidden, model.inter, model.qkv_rows
+    qH, qI = H // 32 * 34, I // 32 * 34
+    q8, f32 = [], []
+    qo = fo = 0
+    for l in range(n_layers):
+        for name, n in (("qkv in", qH), ("o in", qH), ("gate/up in", qH), ("down in", qI)):
+            q8.append((f"layer {l} {name}", qo, qo + n))
+            qo += n
+        for name, n in (("qkv", Q), ("o", H), ("gate/up", 2 * I), ("down", H)):
+            f32.append((f"layer {l} {name}", fo, fo + n))
+            fo += n
+    q8.append(("lm_head in", qo, qo + qH))
+    return q8, f32
+
+
+def check_chain_trace(model, n_layers, q8t, f32t, rq8, rf32, rsabs, what):
+    """Stage-by-stage parity of a decode step's trace against the oracle's
+    own step on the same seeded input.  Every q8_0 vector a glue stage formed
+    must equal the oracle's bytes; every GEMV output must be within the
+    per-row gate of the oracle's value (sum_i |w_i x_i| from the oracle).
+    Because the q8_0 inputs are asserted equal first, each GEMV is checked
+    against the oracle on the very input it consumed.  Returns the fraction
+    of f32 values that are bit-identical."""
+    q8s, f32s = trace_stages(model, n_layers)
+    assert q8t.size == q8s[-1][2] and f32t.size == f32s[-1][2], "trace sizes"
+    for name, a, b in q8s:
+        ds, dq, mx = q8_code_diff(q8t[a:b], rq8[a:b])
+        assert ds == 0 and dq == 0, (f"{what}: {name}: q8_0 bytes differ from the oracle's "
+                                     f"(scales {ds}, codes {dq}, max |dq| {mx})")
+    for name, a, b in f32s:
+        y, yr, sa = f32t[a:b], rf32[a:b], rsabs[a:b]
+        err = np.abs(y.astype(np.float64) - yr.astype(np.float64))
+        bad = ~(err <= TOL_REL * sa + TOL_ABS)
+        assert not bad.any(), f"{what}: {name}: {bad.sum()} rows outside tolerance, first {np.argmax(bad)}"
+    same = float(np.mean(f32t.view(np.uint32) == rf32.view(np.uint32)))
+    log(f"  {what}: {len(q8s)} q8_0 stages byte-identical, {len(f32s)} GEMV stages within tolerance, "
+        f"f32 bit-identical {same:.6f}")
+    return same
 
 
 def model_weights(model, n_layers):

@@ -122,3 +122,17 @@ def test_chain_argument_errors(mq):
     m = mq.MoEDesc(64, 8, 2048, 1408, FAKE, 1 << 24, FAKE, 1 << 24, FAKE, FAKE, FAKE, FAKE, 10, 0, 257)
     assert L.mq_moe_create(C.byref(m), None, C.byref(out)) == mq.MQ_ERR_SHAPE          # tokens_per_launch
     assert L.mq_test_set_fault(0) == mq.MQ_OK
+
+
+def test_workspace_and_gate_up_hook_on_the_host(mq):
+    L = mq.lib()
+    # no split-k call has run in this process: nothing held, releasing nothing is fine
+    assert mq.mq_workspace_stats() == {"bytes": 0, "streams": 0, "retired": 0}
+    assert L.mq_workspace_release() == mq.MQ_OK
+    g = L.mq_debug_gate_up_swiglu
+    assert g(None, FAKE, 1e-6, None, FAKE, 64, 256, 0, None, None, 0, None) == mq.MQ_ERR_ARG          # null w
+    assert g(FAKE, FAKE, 1e-6, None, FAKE, 48, 256, 0, None, None, 0, None) == mq.MQ_ERR_SHAPE        # inter % 32
+    assert g(FAKE, FAKE, 1e-6, None, FAKE, 64, 300, 0, None, None, 0, None) == mq.MQ_ERR_SHAPE        # k % 256
+    assert g(FAKE, FAKE, 1e-6, None, FAKE, 64, 256, -1, None, None, 0, None) == mq.MQ_ERR_ARG         # n_split
+    assert g(FAKE, FAKE, 1e-6, None, FAKE, 64, 256, 0, None, None, 5, None) == mq.MQ_ERR_ARG          # format
+    assert g(FAKE, C.c_void_p(0x10004), 1e-6, None, FAKE, 64, 256, 0, None, None, 0, None) == mq.MQ_ERR_ARG
