@@ -58,6 +58,7 @@ SIGNATURES = {
     "mq_quantize_q8_0": ([_vp, _vp, _i64, _int, _vp], _int),
     "mq_gemv_q4k_q8": ([_vp, _vp, _vp, _i64, _i64, _vp], _int),
     "mq_gemv_q4k_q8_batched": ([_vp, _vp, _vp, _i64, _i64, _int, _vp], _int),
+    "mq_gemv_q4k_q8_batched_noalloc": ([_vp, _vp, _vp, _i64, _i64, _int, _vp], _int),
     "mq_gemv_q4k_grouped": ([_vp, _i64, _int, _vp, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _vp], _int),
     "mq_gemv_q8_0_q8": ([_vp, _vp, _vp, _i64, _i64, _vp], _int),
     "mq_gemv_q4_0_q8": ([_vp, _vp, _vp, _i64, _i64, _vp], _int),
@@ -240,6 +241,14 @@ def mq_gemv_q4k_q8_batched(w, xq, m, k, n, y=None, stream=None):
     _check(lib().mq_gemv_q4k_q8_batched(_ptr(w, torch.uint8, q4k_bytes(m, k), "w"),
                                         _ptr(xq, torch.uint8, q8_bytes(n, k), "xq"),
                                         _ptr(y, torch.float32, 4 * m * n, "y"), m, k, n, _stream(stream)))
+    return y
+
+
+def mq_gemv_q4k_q8_batched_noalloc(w, xq, m, k, n, y, stream=None):
+    """The batched GEMV that allocates nothing: the caller passes y."""
+    _check(lib().mq_gemv_q4k_q8_batched_noalloc(_ptr(w, torch.uint8, q4k_bytes(m, k), "w"),
+                                                _ptr(xq, torch.uint8, q8_bytes(n, k), "xq"),
+                                                _ptr(y, torch.float32, 4 * m * n, "y"), m, k, n, _stream(stream)))
     return y
 
 

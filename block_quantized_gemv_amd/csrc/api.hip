@@ -139,6 +139,37 @@ int run_q4k(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t 
     return run_q4(kFmtQ4K, w, xq, col_bytes, y, nullptr, nullptr, m, k, ncols, stream);
 }
 
+// The no-allocation batched entry point keeps its split-k partials in this
+// fixed array instead of a workspace: every GPU the library runs on holds
+// one copy of it until the process ends, and every call on that GPU shares
+// it.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up per device (hipGetSymbolAddress,
+// with that device current) and only that address is ever passed on.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) double scratch[kScratchBytes / sizeof(double)];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The current device's address of `scratch`, looked up on the first call
+// on each device.
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MQ_ERR_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(MQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MQ_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ chains ----
@@ -457,6 +488,25 @@ int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, i
     if (rc != MQ_OK) return rc;
     CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
     return run_q4k(w, xq, (k / 32) * kQ8Bytes, y, m, k, n, stream);
+}
+
+int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n,
+                                   hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
+    const int64_t col_bytes = (k / 32) * kQ8Bytes;
+    if (n * stage_bytes((int)(k / 32)) <= kMaxStageLds)       // one pass over k: no partials
+        return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, nullptr, nullptr, m, k, n, stream, kFmtQ4K),
+                          "4-bit GEMV launch");
+    const size_t need = (size_t)gemv_q4k_splitk_nsplit(k) * (size_t)m * (size_t)n * sizeof(double);
+    CHECK_SHAPE(need <= kScratchBytes, "m=%lld, k=%lld, n=%d need %zu bytes of split-k partials; the fixed "
+                "scratch of the no-allocation entry point holds %zu", (long long)m, (long long)k, n, need,
+                kScratchBytes);
+    void* part = nullptr;
+    if ((rc = scratch_address(&part)) != MQ_OK) return rc;
+    return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)part, m, k, n, stream, kFmtQ4K),
+                      "4-bit split-k GEMV launch");
 }
 
 int mq_gemv_q4_0_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k, hipStream_t stream) {

@@ -111,6 +111,22 @@ int mq_gemv_q4k_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k
 int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, int64_t k,
                            int n, hipStream_t stream);
 
+/* The batched GEMV for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments, kernels and results as
+ * mq_gemv_q4k_q8_batched, but it never allocates.  When the columns do not
+ * fit in LDS its split-k partials go to a fixed 4 MiB device array of the
+ * library instead of a workspace: ceil(k/4096)*m*n doubles must fit (for
+ * example the 3584 x 18944 matrix at n = 8 takes 1.1 MiB), else
+ * MQ_ERR_SHAPE, reported on the host before any HIP call.  Each GPU holds
+ * its own copy of the array until the process ends, and every call on that
+ * GPU uses it: two calls that overlap in time on one GPU (from different
+ * streams or threads) race on the partials and give wrong results, so
+ * order them on one stream.  Nothing in the array needs clearing between
+ * calls (each call writes every partial it reads). */
+int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                                   int n, hipStream_t stream);
+
 /* The split-k workspaces (see mq_gemv_q4k_q8_batched).  Host out-params
  * (any may be NULL): bytes held in total, the (device, stream) pairs that
  * have one, and the outgrown buffers still held. */

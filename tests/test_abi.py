@@ -136,3 +136,13 @@ def test_workspace_and_gate_up_hook_on_the_host(mq):
     assert g(FAKE, FAKE, 1e-6, None, FAKE, 64, 256, -1, None, None, 0, None) == mq.MQ_ERR_ARG         # n_split
     assert g(FAKE, FAKE, 1e-6, None, FAKE, 64, 256, 0, None, None, 5, None) == mq.MQ_ERR_ARG          # format
     assert g(FAKE, C.c_void_p(0x10004), 1e-6, None, FAKE, 64, 256, 0, None, None, 0, None) == mq.MQ_ERR_ARG
+
+
+def test_no_alloc_entry_point_refuses_on_the_host(mq):
+    L = mq.lib()
+    f = L.mq_gemv_q4k_q8_batched_noalloc
+    assert f(None, FAKE, FAKE, 16, 256, 2, None) == mq.MQ_ERR_ARG
+    assert f(FAKE, FAKE, FAKE, 16, 256, 9, None) == mq.MQ_ERR_SHAPE
+    # 14000 rows x 8 columns x 5 splits of f64 partials exceed the fixed 4 MiB scratch
+    assert f(FAKE, FAKE, FAKE, 14000, 18944, 8, None) == mq.MQ_ERR_SHAPE
+    assert "scratch" in L.mq_last_error().decode()
