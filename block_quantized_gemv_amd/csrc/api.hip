@@ -607,6 +607,7 @@ int mq_debug_gate_up_swiglu(const void* w, const float* x, float eps, float* gu_
     CHECK_SHAPE(inter >= 32 && inter % 32 == 0 && 2 * inter <= kMaxRows, "inter must be a positive multiple of 32");
     CHECK_SHAPE(k >= 256 && k % 256 == 0 && stage_bytes((int)(k / 32)) <= kMaxStageLds,
                 "k must be a positive multiple of 256 that fits in LDS");
+    CHECK_SHAPE(2 * inter <= max_rows_per_launch(k), "a matrix of 4 GiB or more");
     CHECK_ARG(eps >= 0.0f, "eps must be >= 0");
     const NormIn nin{x, nullptr, 1, eps, nullptr, nullptr, 0};
     const int fmt = weight_format == MQ_FMT_Q4_0 ? kFmtQ4_0 : kFmtQ4K;
@@ -625,6 +626,9 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
                 "qkv_rows must be >= hidden and a multiple of 4");
     CHECK_SHAPE(d->vocab >= 1 && d->vocab <= kMaxRows, "vocab out of range");
     CHECK_SHAPE(stage_bytes((int)(d->inter / 32)) <= kMaxStageLds, "inter too large");
+    CHECK_SHAPE(d->qkv_rows <= max_rows_per_launch(d->hidden) && 2 * d->inter <= max_rows_per_launch(d->hidden) &&
+                    d->hidden <= max_rows_per_launch(d->inter),
+                "a layer matrix of 4 GiB or more (the chain's kernels address each with 32-bit offsets)");
     CHECK_ARG(d->w_qkv && d->w_o && d->w_gu && d->w_down && d->w_lm && d->x_table && d->logits,
               "null pointer in the descriptor");
     CHECK_ARG(d->n_inputs >= 1, "n_inputs must be >= 1");

@@ -23,6 +23,13 @@ __device__ __forceinline__ uint32_t f32_to_f16(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// The wave's index in its workgroup as a wave-uniform (scalar) value: the
+// compiler cannot tell that threadIdx.x / 64 is the same on every lane, and
+// index arithmetic derived from it would otherwise run on the vector ALUs.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);   // v_dot4_i32_i8
 }
@@ -32,12 +39,14 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 // to its partner's (IEEE addition is commutative), so all lanes of a group
 // end with the same bits and the order of additions is fixed: the sum is
 // deterministic and tree-shaped, which is also the more accurate schedule
-// ('Part 4 · Lecture 08 — Graph-Resident Decode', §8).
+// ('Part 4 · Lecture 08 — Graph-Resident Decode', §8).  The DPP patterns
+// used here read lanes of the same row, all active, so the moves need no
+// fallback value (bound_ctrl set, no zeroing move before each).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 __device__ __forceinline__ double swizzle_xor16_f64(double v) {

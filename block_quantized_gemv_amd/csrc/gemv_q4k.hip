@@ -54,36 +54,45 @@ __device__ __forceinline__ void load_sb(const uint8_t* __restrict__ blk, int jo,
 // in the low six bits of s[j'] and s[j'+4]; j' >= 4 take their low four bits
 // from the nibbles of s[j'+4] and their top two from the top bits of s[j'-4]
 // (scale) and s[j'] (min).  A lane's two sub-blocks sit in one 16-bit half
-// of each dword, so both are decoded at once.
+// of each dword (sh = 0 or 16), so both are decoded at once, and both obey
+// the same rule, so the rule is a set of per-lane masks rather than a
+// branch: mA = 0x3F3F or 0xC0C0, shA = 0 or 2, mC = 0 or 0x0F0F (see
+// Lanes).  hx is the header's d/dmin dword, or 0 for an invalid item so
+// that it adds exactly zero.
 struct SBScales {
     double d, dmin, m0, m1;
     uint32_t scp;      // the two six-bit scales: sc0 | sc1 << 8
 };
-__device__ __forceinline__ void decode_scales(const u32x4& hdr, int sh, bool low, SBScales& s) {
-    const uint32_t a2 = (hdr.y >> sh) & 0xFFFFu;
-    const uint32_t b2 = (hdr.z >> sh) & 0xFFFFu;
-    const uint32_t c2 = (hdr.w >> sh) & 0xFFFFu;
-    const uint32_t scp = low ? (a2 & 0x3F3Fu) : ((c2 & 0x0F0Fu) | ((a2 & 0xC0C0u) >> 2));
-    const uint32_t mp = low ? (b2 & 0x3F3Fu) : (((c2 >> 4) & 0x0F0Fu) | ((b2 & 0xC0C0u) >> 2));
+__device__ __forceinline__ void decode_scales(const u32x4& hdr, uint32_t hx, int sh, uint32_t mA, uint32_t shA,
+                                              uint32_t mC, SBScales& s) {
+    const uint32_t a2 = hdr.y >> sh, b2 = hdr.z >> sh, c2 = hdr.w >> sh;
+    const uint32_t scp = ((a2 & mA) >> shA) | (c2 & mC);
+    const uint32_t mp = ((b2 & mA) >> shA) | ((c2 >> 4) & mC);
     // An empty asm hides scp's range, so that the byte masks where the
     // scales are used survive and both products select 24-bit multiplies.
     uint32_t opaque = scp;
     asm("" : "+v"(opaque));
     s.scp = opaque;
-    s.m0 = (double)(int)(mp & 0xFFu);
-    s.m1 = (double)(int)(mp >> 8);
-    s.d = (double)f16_to_f32(hdr.x);
-    s.dmin = (double)f16_to_f32(hdr.x >> 16);
+    s.m0 = (double)(mp & 0xFFu);
+    s.m1 = (double)(mp >> 8);
+    s.d = (double)f16_to_f32(hx);
+    s.dmin = (double)f16_to_f32(hx >> 16);
 }
 
 // Exact int32 sums of one lane's two sub-blocks against the staged codes.
+// The high nibbles of two dwords come from one 64-bit shift: the bits the
+// low dword takes from the high one land in its top nibble, which the mask
+// clears.
 __device__ __forceinline__ void sb_isums(const SBLoad& L, const StagedPair& x, int& i0, int& i1) {
     const uint32_t q[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
     int a = 0, b = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 8; k += 2) {
+        const uint64_t h = (((uint64_t)q[k + 1] << 32) | q[k]) >> 4;
         a = dot4(q[k] & 0x0F0F0F0Fu, x.c[k], a);
-        b = dot4((q[k] >> 4) & 0x0F0F0F0Fu, x.c[8 + k], b);
+        b = dot4((uint32_t)h & 0x0F0F0F0Fu, x.c[8 + k], b);
+        a = dot4(q[k + 1] & 0x0F0F0F0Fu, x.c[k + 1], a);
+        b = dot4((uint32_t)(h >> 32) & 0x0F0F0F0Fu, x.c[9 + k], b);
     }
     i0 = a;
     i1 = b;
@@ -113,7 +122,8 @@ __device__ __forceinline__ int staged_pair_mask(int nsb) { return nsb >= 4 ? 15 
 
 struct Lanes {
     int lane, log2s, S, R, gpp, row_local, g, j, sh, pmask;
-    bool low;
+    uint32_t mA, shA, mC;       // the lane's scale-decode rule (decode_scales)
+    int lds_lane, lds_inval;    // staging byte offsets: the lane's pair within a pass, and its stand-in
     __device__ Lanes(int log2s_, int nsb) {
         pmask = staged_pair_mask(nsb);
         lane = threadIdx.x & 63;
@@ -125,38 +135,75 @@ struct Lanes {
         g = (lane & (S - 1)) >> 2;
         j = lane & 3;
         sh = (j & 1) * 16;
-        low = j < 2;
+        const bool low = j < 2;
+        mA = low ? 0x3F3Fu : 0xC0C0u;
+        shA = low ? 0u : 2u;
+        mC = low ? 0u : 0x0F0Fu;
+        lds_lane = (4 * g + j) * 16;
+        lds_inval = ((4 * g + j) & pmask) * 16;
     }
 };
 
-// LDS byte offset of the staged pair that lane (g, j) needs in pass p:
-// pair P = 4*(p*gpp + g) + j.
+// The staged pair that lane (g, j) needs in pass p: P = 4*(p*gpp + g) + j.
 __device__ __forceinline__ int pair_of(const Lanes& ln, int p) { return 4 * (p * ln.gpp + ln.g) + ln.j; }
 
+// Staging offset (group base plus slot) where pass p's pairs start.  Pass p
+// covers pairs 4*gpp*p .. 4*gpp*p + 4*gpp - 1, which never cross a 64-pair
+// group (4*gpp divides 64), so the lane's pair is lds_lane bytes further.
+// Wave-uniform.
+__device__ __forceinline__ int pass_lds_base(const Lanes& ln, int p) {
+    const int P0 = 4 * ln.gpp * p;
+    return (P0 >> 6) * kStageGroupBytes + (P0 & 63) * 16;
+}
+
+// The staged data of the pair at byte offset A (its group's base plus
+// (P & 63)*16), as read_pair reads pair P.
+__device__ __forceinline__ void read_pair_at(const uint8_t* __restrict__ lds, int A, StagedPair& sp) {
+    const uint8_t* g = lds + A;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u32x4 v = *(const u32x4*)(g + k * 1024);
+        sp.c[4 * k + 0] = v.x; sp.c[4 * k + 1] = v.y; sp.c[4 * k + 2] = v.z; sp.c[4 * k + 3] = v.w;
+    }
+    sp.d0 = *(const double*)(g + 4096);
+    sp.d1 = *(const double*)(g + 4096 + 8);
+    sp.ds0 = *(const double*)(g + 5120);
+    sp.ds1 = *(const double*)(g + 5120 + 8);
+}
+
 // One q4_K super-block item for NC activation columns: adds the lane's
-// contribution to acc[] (masked by `valid`).
+// contribution to acc[] (nothing for an invalid item).  A: the LDS offset of
+// the lane's staged pair, or, for an invalid item, of a staged stand-in
+// (lds_inval: pair P & pmask, staged whenever the row has the super-blocks
+// pmask implies, and in the same LDS banks), so that its terms are finite
+// and, with zero scales, add exactly zero.  P is only for the dump.
 template <int NC, bool DUMP>
-__device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P, bool valid,
-                                        const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
-                                        int32_t* __restrict__ dump, int64_t dump_row_off) {
+__device__ __forceinline__ void sb_item_at(const SBLoad& L, const Lanes& ln, int A, int P, bool valid,
+                                           const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
+                                           int32_t* __restrict__ dump, int64_t dump_row_off) {
     SBScales s;
-    decode_scales(L.hdr, ln.sh, ln.low, s);
-    const double d = valid ? s.d : 0.0, neg_dmin = valid ? -s.dmin : 0.0;
-    // A lane past the row's last super-block would read an unstaged pair;
-    // an invalid lane reads a staged one, so its terms are finite.
-    P = valid ? P : (P & ln.pmask);
+    decode_scales(L.hdr, valid ? L.hdr.x : 0u, ln.sh, ln.mA, ln.shA, ln.mC, s);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         StagedPair x;
-        read_pair(lds + c * col_bytes, P, x, true);
+        read_pair_at(lds + c * col_bytes, A, x);
         int i0, i1;
         sb_isums(L, x, i0, i1);
-        acc[c] = sb_accumulate(acc[c], d, neg_dmin, s, x, i0, i1);
+        acc[c] = sb_accumulate(acc[c], s.d, -s.dmin, s, x, i0, i1);
         if (DUMP && valid) {
             dump[dump_row_off + 2 * P] = i0;
             dump[dump_row_off + 2 * P + 1] = i1;
         }
     }
+}
+
+// The same item addressed by its staged pair P.
+template <int NC, bool DUMP>
+__device__ __forceinline__ void sb_item(const SBLoad& L, const Lanes& ln, int P, bool valid,
+                                        const uint8_t* __restrict__ lds, int col_bytes, double (&acc)[NC],
+                                        int32_t* __restrict__ dump, int64_t dump_row_off) {
+    const int A = valid ? (P >> 6) * kStageGroupBytes + (P & 63) * 16 : (P & ln.pmask) * 16;
+    sb_item_at<NC, DUMP>(L, ln, A, P, valid, lds, col_bytes, acc, dump, dump_row_off);
 }
 
 // --------------------------------------------------------------------------
@@ -181,6 +228,22 @@ __device__ __forceinline__ void load_group(const uint8_t* __restrict__ grp, int 
 }
 __device__ __forceinline__ void load_group(const uint8_t* __restrict__ grp, int j, SBLoad& L) {
     load_sb(grp, 32 * j, L);
+}
+
+// The same loads at w + off: the base stays in SGPRs and the lane's
+// offset is one 32-bit VGPR (the matrix must be smaller than 4 GiB; the
+// launchers split larger ones by rows).
+__device__ __forceinline__ void load_group_off(const uint8_t* __restrict__ w, uint32_t off, int j, SBLoad& L) {
+    L.hdr = *(const u32x4*)(w + off);
+    const uint32_t oq = off + 32u * (uint32_t)j;
+    L.qa = *(const u32x4*)(w + oq + 16u);
+    L.qb = *(const u32x4*)(w + oq + 32u);
+}
+__device__ __forceinline__ void load_group_off(const uint8_t* __restrict__ w, uint32_t off, int j, Q40Load& L) {
+    const uint32_t o = off + 36u * (uint32_t)j;
+    L.a = *(const u32x4_a4*)(w + o);
+    L.b = *(const u32x4_a4*)(w + o + 16u);
+    L.c = *(const uint32_t*)(w + o + 32u);
 }
 
 template <int FMT> struct GroupLoad { using type = SBLoad; };
@@ -259,8 +322,12 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
     const int W = gridDim.x * (blockDim.x >> 6);
     constexpr bool kEarly = SRC != kSrcQ8;
     static_assert(SRC == kSrcQ8 || (NC == 1 && !DUMP), "early staging takes one column");
-    const int wave = kEarly ? (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x
-                            : blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    // The norm-prologue kernel keeps the wave index (and so its few items'
+    // index arithmetic) in vector registers: measured faster there; the
+    // others take it as a scalar and walk their items with a cursor.
+    constexpr bool kCursor = SRC != kSrcNorm;
+    const int wv = kCursor ? wave_id() : (int)(threadIdx.x >> 6);
+    const int wave = kEarly ? wv * (int)gridDim.x + (int)blockIdx.x : blockIdx.x * (blockDim.x >> 6) + wv;
     const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
@@ -274,17 +341,45 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
         bool valid;
         int row, pass;
     };
+    // Item (tile t, pass p) reads the lane's super-block at byte offset
+    // (t*R + row_local)*row_bytes + (p*gpp + g)*144: a wave-uniform part plus
+    // the lane's constant lane_off.  stream_items fetches items in order, so
+    // with kCursor a wave-uniform cursor (the tile's first row, the pass and
+    // their offset) advances one item per fetch instead of dividing the
+    // item index.  Past the wave's last item the fetch stays on it.
+    const uint32_t lane_off = (uint32_t)ln.row_local * (uint32_t)row_bytes + (uint32_t)(ln.g * kQ4KBytes);
+    int c_row0 = wave * ln.R, c_pass = 0, c_done = 0;
+    uint32_t c_off = (uint32_t)c_row0 * (uint32_t)row_bytes;
+    const uint32_t pass_bytes = (uint32_t)(ln.gpp * kQ4KBytes);
+    const uint32_t wrap_bytes = (uint32_t)(W * ln.R) * (uint32_t)row_bytes - (uint32_t)passes * pass_bytes;
     auto fetch = [&](int i, Item& it) {
-        const bool past = i >= n_items;
-        const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
-        const int t = wave + (ii / passes) * W;
-        it.pass = ii % passes;
-        it.row = t * ln.R + ln.row_local;
-        const int sb = it.pass * ln.gpp + ln.g;
-        const bool inb = n_items > 0 && it.row < M && sb < nsb;
+        int row0;
+        uint32_t off;
+        bool past;
+        if constexpr (kCursor) {
+            past = c_done >= n_items;
+            it.pass = c_pass;
+            row0 = c_row0;
+            off = c_off;
+            if (!past && ++c_done < n_items) {
+                c_off += pass_bytes;
+                if (++c_pass == passes) {
+                    c_pass = 0;
+                    c_row0 += W * ln.R;
+                    c_off += wrap_bytes;
+                }
+            }
+        } else {
+            past = i >= n_items;
+            const int ii = past ? (n_items > 0 ? n_items - 1 : 0) : i;
+            it.pass = ii % passes;
+            row0 = (wave + (ii / passes) * W) * ln.R;
+            off = (uint32_t)row0 * (uint32_t)row_bytes + (uint32_t)it.pass * pass_bytes;
+        }
+        it.row = past ? M : row0 + ln.row_local;
+        const bool inb = n_items > 0 && ln.row_local < M - row0 && ln.g < nsb - it.pass * ln.gpp;
         it.valid = inb && !past;
-        if (past) it.row = M;
-        load_group(inb ? w + (int64_t)(t * ln.R + ln.row_local) * row_bytes + sb * kQ4KBytes : w, ln.j, it.L);
+        load_group_off(w, inb ? off + lane_off : 0u, ln.j, it.L);
     };
 
     // Early sources: the activation is requested first, then items 0 and
@@ -317,8 +412,14 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.0;
     stream_items<kEarly>(n_items, A, B, fetch, [&](const Item& it) {
-        group_item<NC, DUMP>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
-                             (int64_t)it.row * nb);
+        if constexpr (FMT == kFmtQ4K) {
+            const int a = it.valid ? pass_lds_base(ln, it.pass) + ln.lds_lane : ln.lds_inval;
+            sb_item_at<NC, DUMP>(it.L, ln, a, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
+                                 (int64_t)it.row * nb);
+        } else {
+            group_item<NC, DUMP>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, col_bytes, acc, dump_isum,
+                                 (int64_t)it.row * nb);
+        }
         if (it.pass != passes - 1) return;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -344,7 +445,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
     const int nsb_s = min(16, nsb - sb0);
     const Lanes ln(6, nsb_s);
     const int W = gridDim.x * (blockDim.x >> 6);
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int wave = blockIdx.x * (blockDim.x >> 6) + wave_id();
     const int n_items = wave < M ? (M - 1 - wave) / W + 1 : 0;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
     const bool lane_ok = ln.g < nsb_s;
@@ -420,7 +521,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
     const int col_bytes = stage_bytes(nb);
     const int n_cols = xq_stride ? n_sel : 1;
     const int W = gridDim.x * (blockDim.x >> 6);
-    const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int wave = blockIdx.x * (blockDim.x >> 6) + wave_id();
     // COMBINE: units are tiles, each of n_sel*passes items; else units are
     // (slot, tile) pairs of `passes` items.
     const int n_units = COMBINE ? n_tiles : n_tiles * n_sel;
@@ -530,7 +631,7 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     const int p0 = half && hs ? passes_all / 2 : 0;
     const int passes = half ? (hs ? passes_all - passes_all / 2 : passes_all / 2) : passes_all;
     const int n_items = 2 * TPH * passes;
-    const int q = threadIdx.x >> 6;
+    const int q = wave_id();
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
 
     // item i: tile st = i / passes (st / TPH: 0 gate, 1 up; st % TPH: which
@@ -544,15 +645,22 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
         bool valid;
         int st, pass;
     };
-    auto fetch = [&](int i, Item& it) {
-        const bool past = i >= n_items;
-        const int ii = past ? n_items - 1 : i;
-        it.st = ii / passes;
-        it.pass = p0 + ii % passes;
-        const int sb = it.pass * ln.gpp + ln.g;
-        const bool inb = sb < nsb;
+    // An in-order cursor over (st, pass), as in k_gemv_q4k.
+    const uint32_t lane_off = (uint32_t)ln.row_local * (uint32_t)row_bytes + (uint32_t)(ln.g * kQ4KBytes);
+    int c_st = 0, c_pass = 0, c_done = 0;
+    auto fetch = [&](int, Item& it) {
+        const bool past = c_done >= n_items;
+        it.st = c_st;
+        it.pass = p0 + c_pass;
+        const bool inb = ln.g < nsb - it.pass * ln.gpp;
         it.valid = inb && !past;
-        load_group(inb ? w + row_of(it.st) * row_bytes + sb * kQ4KBytes : w, ln.j, it.L);
+        const int row0 = row_of(it.st) - ln.row_local;
+        const uint32_t off = (uint32_t)row0 * (uint32_t)row_bytes + (uint32_t)(it.pass * ln.gpp * kQ4KBytes);
+        load_group_off(w, inb ? off + lane_off : 0u, ln.j, it.L);
+        if (!past && ++c_done < n_items && ++c_pass == passes) {
+            c_pass = 0;
+            ++c_st;
+        }
     };
 
     float4 xr[kNormRegChunks];
@@ -574,7 +682,12 @@ __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
 
     double acc[1] = {0.0};
     stream_items<NORM>(n_items, A, B, fetch, [&](const Item& it) {
-        group_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
+        if constexpr (FMT == kFmtQ4K) {
+            const int a = it.valid ? pass_lds_base(ln, it.pass) + ln.lds_lane : ln.lds_inval;
+            sb_item_at<1, false>(it.L, ln, a, 0, it.valid, lds, 0, acc, nullptr, 0);
+        } else {
+            group_item<1, false>(it.L, ln, pair_of(ln, it.pass), it.valid, lds, 0, acc, nullptr, 0);
+        }
         if (it.pass != p0 + passes - 1) return;
         const double v = group_sum_f64(acc[0], 4);
         acc[0] = 0.0;
@@ -647,7 +760,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_grouped_combine(
     const Lanes ln(log2s, nsb);
     const int nb = nsb * 8;
     const int col_bytes = stage_bytes(nb);
-    const int slot = threadIdx.x >> 6;
+    const int slot = wave_id();
     const int t0 = (int)blockIdx.x * tpw;
     const int n_items = tpw * passes;
     const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
@@ -746,7 +859,7 @@ __global__ __launch_bounds__(512) void k_moe_gate_up(
     __shared__ float gu_s[64];
     __shared__ double gu_d[64];
     const Lanes ln(4, nsb);
-    const int q = threadIdx.x >> 6;
+    const int q = wave_id();
     // One workgroup per (slot, output block), in a 1-D grid.  As in
     // k_gemv_q4k_swiglu, the last n_split working blocks (slot-major) run as
     // two halves along K, workgroups 0 .. 2*n_split-1, which hand over
@@ -1069,13 +1182,25 @@ static hipError_t launch_fmt(const void* w, const void* xq, int64_t xq_col_bytes
     }
 }
 
+int64_t max_rows_per_launch(int64_t k) { return (((int64_t)1 << 32) - 1) / ((k / 256) * kQ4KBytes); }
+
 hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                            int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
                            hipStream_t stream, int fmt) {
     const int nsb = (int)(k / 256);
-    return fmt == kFmtQ4_0
-               ? launch_fmt<kFmtQ4_0>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, ncols, stream)
-               : launch_fmt<kFmtQ4K>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, ncols, stream);
+    // the kernels address the matrix with 32-bit offsets: row blocks under 4 GiB
+    const int64_t step = max_rows_per_launch(k), row_bytes = (int64_t)nsb * kQ4KBytes;
+    for (int64_t r0 = 0; r0 < m; r0 += step) {
+        const int64_t mr = m - r0 < step ? m - r0 : step;
+        const uint8_t* wr = (const uint8_t*)w + r0 * row_bytes;
+        float* yr = y + r0 * ncols;
+        int32_t* ir = dump_isum ? dump_isum + r0 * (k / 32) : nullptr;
+        const hipError_t e =
+            fmt == kFmtQ4_0 ? launch_fmt<kFmtQ4_0>(wr, xq, xq_col_bytes, yr, ir, dump_ysum, mr, nsb, ncols, stream)
+                            : launch_fmt<kFmtQ4K>(wr, xq, xq_col_bytes, yr, ir, dump_ysum, mr, nsb, ncols, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 int gemv_q4k_splitk_nsplit(int64_t k) { return (int)((k / 256 + 15) / 16); }

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* 
     const int row_local = lane >> log2s, slot = lane & (S - 1);
     const int W = gridDim.x * (blockDim.x >> 6);
     // With NORM, consecutive units go to different workgroups (one per CU).
-    const int wave = NORM ? (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x
-                          : blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int wave = NORM ? wave_id() * (int)gridDim.x + (int)blockIdx.x
+                          : blockIdx.x * (blockDim.x >> 6) + wave_id();
     const int my_tiles = wave < n_tiles ? (n_tiles - 1 - wave) / W + 1 : 0;
     const int n_items = my_tiles * passes;
     const int64_t row_bytes = (int64_t)npairs * 2 * kQ8Bytes;

@@ -16,9 +16,10 @@
 
 namespace mq {
 
+// (as dpp_f64: same-row patterns with every lane active)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Max over each aligned group of 32 lanes (all 64 lanes must be active).
@@ -96,7 +97,7 @@ __device__ __forceinline__ void rmsnorm_quantize_range(const float* __restrict__
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 // The f32 input of a GEMV whose q8_0 activation is Q8(RMSNorm(x)), formed in

@@ -42,6 +42,10 @@ constexpr int kMaxStageLds = 64 * 1024;
 // expert kernels take q4_K only).
 constexpr int kFmtQ4K = 0, kFmtQ4_0 = 1;
 
+// Rows of k weights per launch of the 4-bit kernels, which address the
+// matrix with 32-bit byte offsets (launch_gemv_q4k splits taller matrices;
+// the chains and the gate/up hook refuse them).
+int64_t max_rows_per_launch(int64_t k);
 hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                            int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
                            hipStream_t stream, int fmt = kFmtQ4K);
