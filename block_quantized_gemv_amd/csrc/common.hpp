@@ -33,6 +33,13 @@ __device__ __forceinline__ int wave_id() {
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);   // v_dot4_i32_i8
 }
+// The first dot of a chain: the clamped form takes its zero accumulator as
+// an inline constant (the unclamped one becomes a move plus the accumulating
+// v_dot4c).  A q4 x q8 sum of 4 products stays far inside int32, so the
+// clamp never acts.
+__device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, 0, true);
+}
 
 // ------------------------------------------------------ wave reductions ----
 // All-reduce steps over aligned lane groups.  Every step adds a lane's value
@@ -140,6 +147,44 @@ __device__ __forceinline__ void stage_q8(const uint8_t* __restrict__ xq, int b0,
         const uint32_t dbits = load_q8_block(xq + (int64_t)(b0 + b) * kQ8Bytes, q);
         const int s = stage_q8_block(b, dbits, q, lds);
         if (ysum_out) ysum_out[b0 + b] = s;
+    }
+}
+
+// Stage blocks [b0, b0 + nb) of ncols columns (column c at xq + c*col_stride)
+// into lds + c*col_bytes, relative block index from 0.  The workgroup's
+// blocks are taken as one flat list; each thread first requests up to R of
+// them into registers and only then writes them, so the columns' loads are
+// in flight together instead of one column after another.  ysum_out, if
+// set, receives column 0's code sums at b0 + b.
+template <int R>
+__device__ __forceinline__ void stage_q8_cols(const uint8_t* __restrict__ xq, int64_t col_stride, int b0, int nb,
+                                              int ncols, uint8_t* __restrict__ lds, int col_bytes,
+                                              int32_t* __restrict__ ysum_out) {
+    const int total = nb * ncols, T = blockDim.x, tid = threadIdx.x;
+    uint32_t q[R][8], d[R];
+    int cc[R], bb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int f = tid + r * T;
+        const bool in = f < total;
+        const int c = in ? f / nb : 0;
+        cc[r] = c;
+        bb[r] = in ? f - c * nb : 0;
+        d[r] = load_q8_block(xq + c * col_stride + (int64_t)(b0 + bb[r]) * kQ8Bytes, q[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (tid + r * T < total) {
+            const int s = stage_q8_block(bb[r], d[r], q[r], lds + cc[r] * col_bytes);
+            if (ysum_out && cc[r] == 0) ysum_out[b0 + bb[r]] = s;
+        }
+    }
+    for (int f = tid + R * T; f < total; f += T) {
+        const int c = f / nb, b = f - c * nb;
+        uint32_t qq[8];
+        const uint32_t dd = load_q8_block(xq + c * col_stride + (int64_t)(b0 + b) * kQ8Bytes, qq);
+        const int s = stage_q8_block(b, dd, qq, lds + c * col_bytes);
+        if (ysum_out && c == 0) ysum_out[b0 + b] = s;
     }
 }
 

@@ -85,9 +85,13 @@ __device__ __forceinline__ void decode_scales(const u32x4& hdr, uint32_t hx, int
 // clears.
 __device__ __forceinline__ void sb_isums(const SBLoad& L, const StagedPair& x, int& i0, int& i1) {
     const uint32_t q[8] = {L.qa.x, L.qa.y, L.qa.z, L.qa.w, L.qb.x, L.qb.y, L.qb.z, L.qb.w};
-    int a = 0, b = 0;
+    const uint64_t h0 = (((uint64_t)q[1] << 32) | q[0]) >> 4;
+    int a = dot4_first(q[0] & 0x0F0F0F0Fu, x.c[0]);
+    int b = dot4_first((uint32_t)h0 & 0x0F0F0F0Fu, x.c[8]);
+    a = dot4(q[1] & 0x0F0F0F0Fu, x.c[1], a);
+    b = dot4((uint32_t)(h0 >> 32) & 0x0F0F0F0Fu, x.c[9], b);
 #pragma unroll
-    for (int k = 0; k < 8; k += 2) {
+    for (int k = 2; k < 8; k += 2) {
         const uint64_t h = (((uint64_t)q[k + 1] << 32) | q[k]) >> 4;
         a = dot4(q[k] & 0x0F0F0F0Fu, x.c[k], a);
         b = dot4((uint32_t)h & 0x0F0F0F0Fu, x.c[8 + k], b);
@@ -101,16 +105,18 @@ __device__ __forceinline__ void sb_isums(const SBLoad& L, const StagedPair& x, i
 // acc + d8_0*(d*sc0*i0 - dmin*m0*ysum_0) + d8_1*(d*sc1*i1 - dmin*m1*ysum_1)
 // in f64, as acc + d*t - dmin*u.  Every product is exact (sc*isum < 2^22 and
 // d8*ysum < 2^24 significant bits against 53), so only the additions round.
-// The caller passes d = dmin = 0 for an invalid item and points it at a
-// staged activation pair: t and u are then finite (six-bit scales and mins,
-// exact integer sums, finite activation scales), so it adds exactly zero.  The scales are masked where they are
-// used, so that both products select 24-bit multiplies.
-__device__ __forceinline__ double sb_accumulate(double acc, double d, double neg_dmin, const SBScales& s,
-                                                const StagedPair& x, int i0, int i1) {
+// An invalid item has zero scales and a staged stand-in pair: t and u are
+// then finite (six-bit scales and mins, exact integer sums, finite
+// activation scales), so it adds exactly zero.  The scales are masked where
+// they are used, so that both products select 24-bit multiplies.  Every
+// column count uses this same sequence (measured: per-row products shared
+// by the columns save time only at n = 8 and cost the one-column GEMV
+// more), so a batched column equals the one-column GEMV bit for bit.
+__device__ __forceinline__ double sb_accumulate(double acc, const SBScales& s, const StagedPair& x, int i0, int i1) {
     const int sc0 = (int)(s.scp & 0xFFu), sc1 = (int)((s.scp >> 8) & 0xFFu);
     const double t = fma((double)__mul24(sc1, i1), x.d1, (double)__mul24(sc0, i0) * x.d0);
     const double u = fma(s.m1, x.ds1, s.m0 * x.ds0);
-    return fma(neg_dmin, u, fma(d, t, acc));
+    return fma(-s.dmin, u, fma(s.d, t, acc));
 }
 
 // Per-lane constants of the lane layout.
@@ -183,13 +189,20 @@ __device__ __forceinline__ void sb_item_at(const SBLoad& L, const Lanes& ln, int
                                            int32_t* __restrict__ dump, int64_t dump_row_off) {
     SBScales s;
     decode_scales(L.hdr, valid ? L.hdr.x : 0u, ln.sh, ln.mA, ln.shA, ln.mC, s);
+    // With many columns they are double-buffered: column c+1's staged pair
+    // is read before column c is computed, so its LDS latency overlaps that
+    // work (with few columns the extra registers would cost occupancy).
+    constexpr bool kPipe = NC >= 5;
+    StagedPair xb[2];
+    if (kPipe) read_pair_at(lds, A, xb[0]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        StagedPair x;
-        read_pair_at(lds + c * col_bytes, A, x);
+        if (kPipe && c + 1 < NC) read_pair_at(lds + (c + 1) * col_bytes, A, xb[(c + 1) & 1]);
+        if (!kPipe) read_pair_at(lds + c * col_bytes, A, xb[c & 1]);
+        const StagedPair& x = xb[c & 1];
         int i0, i1;
         sb_isums(L, x, i0, i1);
-        acc[c] = sb_accumulate(acc[c], s.d, -s.dmin, s, x, i0, i1);
+        acc[c] = sb_accumulate(acc[c], s, x, i0, i1);
         if (DUMP && valid) {
             dump[dump_row_off + 2 * P] = i0;
             dump[dump_row_off + 2 * P + 1] = i1;
@@ -311,7 +324,7 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
 constexpr int kSrcQ8 = 0, kSrcQ8Early = 1, kSrcNorm = 2;
 
 template <int FMT, int NC, bool DUMP, int SRC>
-__global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
+__global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) __attribute__((amdgpu_waves_per_eu(1, NC >= 5 ? 3 : 8))) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
     int M, int nsb, int log2s, int passes, int n_tiles, NormIn nin) {
@@ -401,10 +414,7 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) void k_gemv_q4k(
     } else if constexpr (SRC == kSrcQ8Early) {
         stage_q8_store(xq, nb, qr, lds);
     } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            stage_q8(xq + c * xq_col_bytes, 0, nb, lds + c * col_bytes, threadIdx.x, blockDim.x,
-                     (DUMP && blockIdx.x == 0 && c == 0) ? dump_ysum : nullptr);
+        stage_q8_cols<4>(xq, xq_col_bytes, 0, nb, NC, lds, col_bytes, (DUMP && blockIdx.x == 0) ? dump_ysum : nullptr);
     }
     __syncthreads();
 
@@ -462,10 +472,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_splitk(
         where(0, pa, ra);
         load_group(pa, ln.j, A);
     }
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-        stage_q8(xq + c * xq_col_bytes, 8 * sb0, 8 * nsb_s, lds + c * kStageGroupBytes, threadIdx.x,
-                 blockDim.x, nullptr);
+    stage_q8_cols<4>(xq, xq_col_bytes, 8 * sb0, 8 * nsb_s, NC, lds, kStageGroupBytes, nullptr);
     __syncthreads();
 
     auto item = [&](const typename GroupLoad<FMT>::type& L, int row) {
