@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--workload", default="7b", choices=["7b", "05b", "05b_q4_0", "single", "batched", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ab", action="store_true", help="skip the interleaved A/B arms (for counter runs)")
+    p.add_argument("--no-extra", action="store_true",
+                   help="the default 7B line only (skip the compact lines of the other four workloads)")
     p.add_argument("--kernel-reps", type=int, default=3, help="passes of the dominant-kernel timing region")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of this many MiB (counter calibration)")
@@ -398,12 +400,12 @@ def host_step_latency(args, mq, model, W, X, chain):
     return res
 
 
-def run_decode(args, model, cpu_layers):
+def run_decode(args, model, cpu_layers, probe=None):
     import torch
     from block_quantized_gemv_amd import binding as mq
     from block_quantized_gemv_amd import synth
     dev = torch.device("cuda:0")
-    probe = stream_probe(mq)
+    probe = probe or stream_probe(mq)
     log(f"generating and uploading {model.weight_bytes() / 1e9:.2f} GB of weights")
     W, host_w = upload_model(model, dev, keep_host=not args.no_cpu_baseline)
     X = torch.from_numpy(synth.normal_f32(model.seed, (synth.KEY_STEP_INPUTS,), (16, model.hidden))).to(dev)
@@ -653,6 +655,47 @@ def run_moe(args):
     return out
 
 
+def other_configs(args, probe):
+    """Compact results of the four other workloads (0.5B step, single GEMV,
+    batched 7B shapes, routed-expert token), GPU side only, for the default
+    line: each with its time, its algorithmic-byte rate and that rate as a
+    fraction of 8 TB/s."""
+    import copy
+    from block_quantized_gemv_amd import workloads
+    a = copy.copy(args)
+    a.steps, a.warmup, a.no_cpu_baseline, a.no_ab, a.kernel_reps = min(args.steps, 100), 10, True, True, 1
+
+    def frac(gbs):
+        return round(gbs / HBM_PEAK_GBS, 4)
+
+    out = {}
+    t0 = time.perf_counter()
+    d = run_decode(a, workloads.DECODE_05B, cpu_layers=0, probe=probe)
+    out["c1_05b_decode_step"] = {"workload": d["config"]["workload"], "ms_per_step": d["ms_per_step"],
+                                 "tok_per_s": d["tok_per_s"], "GB_s": d["value"], "frac_of_8TBs": frac(d["value"]),
+                                 "graph_nodes": d["config"]["graph_nodes"],
+                                 "dominant_kernel_us": d["roofline"]["us_per_launch"]}
+    log(f"extra: 0.5B step {d['ms_per_step']} ms ({time.perf_counter() - t0:.1f} s)")
+    s1 = run_single(a)
+    out["c0_single_gemv"] = {"workload": s1["config"]["workload"],
+                             "us_cold": s1["modes"]["cold"]["us"], "GB_s_cold": s1["modes"]["cold"]["GB_s"],
+                             "frac_of_8TBs_cold": frac(s1["modes"]["cold"]["GB_s"]),
+                             "us_hot": s1["modes"]["hot"]["us"], "GB_s_hot": s1["modes"]["hot"]["GB_s"],
+                             "note": "launch-latency bound (0.6 MB per GEMV)"}
+    log(f"extra: single GEMV {s1['modes']['cold']['us']} us ({time.perf_counter() - t0:.1f} s)")
+    b = run_batched(a)
+    out["c3_batched_7b_shapes"] = {"workload": b["config"]["workload"],
+                                   "cold_median_us": {k: {"us": v["us"], "GB_s": v["GB_s"], "frac_of_8TBs": frac(v["GB_s"])}
+                                                      for k, v in b["shapes"].items()}}
+    log(f"extra: batched ({time.perf_counter() - t0:.1f} s)")
+    m = run_moe(a)
+    out["c4_moe_token"] = {"workload": m["config"]["workload"], "us_per_token": m["us_per_token"],
+                           "tokens_per_s": m["tokens_per_s"], "GB_s": m["value"], "frac_of_8TBs": frac(m["value"]),
+                           "tokens_per_graph_launch": m["config"]["tokens_per_graph_launch"]}
+    log(f"extra: routed-expert token {m['us_per_token']} us ({time.perf_counter() - t0:.1f} s)")
+    return out
+
+
 def calibrate_copy(mib):
     import torch
     n = mib * (1 << 20)
@@ -678,7 +721,11 @@ def main():
         return
     from block_quantized_gemv_amd import workloads
     if args.workload == "7b":
-        out = run_decode(args, workloads.DECODE_7B, cpu_layers=workloads.DECODE_7B.n_layers)
+        from block_quantized_gemv_amd import binding as mq
+        probe = stream_probe(mq)
+        out = run_decode(args, workloads.DECODE_7B, cpu_layers=workloads.DECODE_7B.n_layers, probe=probe)
+        if not args.no_extra:
+            out["other_configs"] = other_configs(args, probe)
     elif args.workload == "05b":
         out = run_decode(args, workloads.DECODE_05B, cpu_layers=workloads.DECODE_05B.n_layers)
     elif args.workload == "05b_q4_0":

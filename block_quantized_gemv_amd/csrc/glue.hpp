@@ -268,6 +268,31 @@ __device__ __forceinline__ void norm_load(const float* __restrict__ x, int k, fl
     }
 }
 
+// RN_f32(1/sqrt(ss/k + eps)) with the f64 operations of the definition
+// (each correctly rounded) replaced by a reciprocal and a reciprocal square
+// root refined by Newton steps.  Each step squares the relative error, so
+// three steps from any hardware estimate better than 2^-8 reach the f64
+// rounding level; the result t is then within a few f64 ulps of the exactly
+// computed chain's value, and RN_f32(t) is that chain's f32 unless t lies
+// within 16 f64 ulps of an f32 midpoint (f32_checked), where the chain
+// itself is evaluated.  The reciprocal of k does not depend on ss and
+// overlaps the sum's reduction.  exact forces the chain (a test hook).
+__device__ __forceinline__ float rms_scale_of(double ss, int k, float eps, bool exact) {
+#pragma clang fp contract(off)
+    const double kd = (double)k;
+    double rk = __builtin_amdgcn_rcp(kd);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) rk = fma(rk, fma(-kd, rk, 1.0), rk);
+    const double v = ss * rk + (double)eps;
+    double y = __builtin_amdgcn_rsq(v);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) y = fma(0.5 * y, fma(-v * y, y, 1.0), y);
+    bool bad = exact;
+    const float f = f32_checked(y, bad);
+    if (!bad) return f;
+    return (float)(1.0 / sqrt(ss / kd + (double)eps));
+}
+
 // Q8(x * scale) of k values (k % 32 == 0) into lds in the layout of
 // stage_q8: each value is the f32 product x * scale (x itself when scale
 // is 1), then quantized as described above; q8_copy, if set, also
@@ -326,7 +351,7 @@ __device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, in
         ss += (double)v.w * (double)v.w;
     }
     ss = block_sum_f64(ss, sh);
-    stage_scaled_q8(x, k, xr, (float)(1.0 / sqrt(ss / (double)k + (double)eps)), exact, lds, q8_copy);
+    stage_scaled_q8(x, k, xr, rms_scale_of(ss, k, eps, exact), exact, lds, q8_copy);
 }
 
 // The input row of a GEMV fed by a NormIn.
