@@ -18,6 +18,11 @@ in HBM.  Prints one JSON line (rank 0):
                byte-weighted aggregate of the four per-layer q4_K GEMVs
   stream_probe = the rate of a plain 16-byte-load read of 4 GiB
                (mq_probe_stream_read), measured first in the same run
+  span_stamps = the step's replay span against the sum of its kernels' own
+               spans (first wave start to last wave end), both from the
+               kernels' real-time-counter stamps with no tracer present
+               (MQ_SPAN_STAMPS); the roofline object adds the dominant
+               kernel's in-graph span from the same stamps
   cpu_baseline = the reference oracle on the host, on a bounded sample
 
 Other workloads (--workload 05b|single|batched|moe) print their own line.
@@ -52,6 +57,7 @@ def parse():
     p.add_argument("--workload", default="7b", choices=["7b", "05b", "05b_q4_0", "single", "batched", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ab", action="store_true", help="skip the interleaved A/B arms (for counter runs)")
+    p.add_argument("--no-stamps", action="store_true", help="skip the span-stamp measurement of the step")
     p.add_argument("--no-extra", action="store_true",
                    help="the default 7B line only (skip the compact lines of the other four workloads)")
     p.add_argument("--kernel-reps", type=int, default=3, help="passes of the dominant-kernel timing region")
@@ -159,14 +165,14 @@ def gemv_kinds(model):
     H, I, Q = model.hidden, model.inter, model.qkv_rows
     wb = model.layer_matrix_bytes
     f = 1 if model.weight_format == "q4_0" else 0      # the kernels' format template argument
-    norm = f"mq::k_gemv_q4k<{f},1,false,2>"
+    norm = f"mq::k_gemv_q4k<{f},1,false,2,false>"
     kinds = []
     for _ in range(model.n_layers):
         kinds += [("qkv", norm, wb(Q, H) + 4 * H + 4 * Q),
                   ("o", norm, wb(H, H) + 4 * H + 4 * H),
-                  ("gate/up", f"mq::k_gemv_q4k_swiglu<{f},true>", wb(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
-                  ("down", f"mq::k_gemv_q4k<{f},1,false,1>", wb(H, I) + wl.q8_bytes(1, I) + 4 * H)]
-    kinds.append(("lm_head", "mq::k_gemv_q8_0<false,true>", wl.q8_bytes(model.vocab, H) + 4 * H + 4 * model.vocab))
+                  ("gate/up", f"mq::k_gemv_q4k_swiglu<{f},true,false>", wb(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
+                  ("down", f"mq::k_gemv_q4k<{f},1,false,1,false>", wb(H, I) + wl.q8_bytes(1, I) + 4 * H)]
+    kinds.append(("lm_head", "mq::k_gemv_q8_0<false,true,false>", wl.q8_bytes(model.vocab, H) + 4 * H + 4 * model.vocab))
     return kinds
 
 
@@ -343,6 +349,64 @@ def interleaved_arms(args, mq, model, W, X, chain, eager):
     return ab
 
 
+def span_stamps(args, mq, model, W, X, steps=100):
+    """The replay span of one step against the sum of its kernels' own spans,
+    from the kernels' real-time-counter stamps (MQ_SPAN_STAMPS: first wave
+    start and last wave end of every GEMV kernel, 100 MHz), with no tracer in
+    the process.  Each measured step directly follows a warm step and its
+    stamps are read after it.  Also: the stamped chain's own back-to-back time per step
+    (events over 20 replays, to set against the plain chain's), and a check
+    of the counter's rate against the host clock over 0.2 s."""
+    import torch
+    tick_us = 0.01
+    c = mq.DecodeChain(model, W, X, flags=mq.MQ_SPAN_STAMPS)
+    for _ in range(max(args.warmup, 3)):
+        c.step(mq.MQ_GRAPH)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(20):
+        c.step(mq.MQ_GRAPH)
+    b.record()
+    torch.cuda.synchronize()
+    b2b_us = a.elapsed_time(b) * 1e3 / 20
+    h0 = time.perf_counter()
+    c.step(mq.MQ_GRAPH)
+    s0 = int(c.read_stamps()[0, 0])
+    time.sleep(0.2)
+    h1 = time.perf_counter()
+    c.step(mq.MQ_GRAPH)
+    s1 = int(c.read_stamps()[0, 0])
+    clock = (h1 - h0) * 1e6 / ((s1 - s0) * tick_us)
+    spans, sums, gaps = [], [], []
+    per = None
+    for _ in range(steps):
+        # a warm step, then the measured step right behind it (the GPU does
+        # not idle before it); its waves overwrite the warm step's stamps
+        c.step(mq.MQ_GRAPH)
+        c.step(mq.MQ_GRAPH)
+        st = c.read_stamps().astype(np.int64)
+        d = (st[:, 1] - st[:, 0]) * tick_us
+        per = d if per is None else per + d
+        spans.append((st[:, 1].max() - st[:, 0].min()) * tick_us)
+        sums.append(d.sum())
+        gaps.append(float(np.mean((st[1:, 0] - st[:-1, 1]) * tick_us)))
+    c.close()
+    per /= steps
+    L = model.n_layers
+    kinds = {"qkv": per[0:4 * L:4], "o": per[1:4 * L:4], "gate_up": per[2:4 * L:4], "down": per[3:4 * L:4]}
+    res = {"steps": steps, "kernels_per_step": int(st.shape[0]),
+           "replay_span_us": round(float(np.mean(spans)), 2), "replay_span_sem_us": round(sem(spans), 3),
+           "kernel_sum_us": round(float(np.mean(sums)), 2),
+           "span_over_sum": round(float(np.mean(spans)) / float(np.mean(sums)), 4),
+           "mean_gap_between_kernels_us": round(float(np.mean(gaps)), 3),
+           "per_kernel_us": {k: round(float(v.mean()), 3) for k, v in kinds.items()},
+           "lm_head_us": round(float(per[-1]), 3),
+           "stamped_chain_back_to_back_us_per_step": round(float(b2b_us), 2),
+           "host_over_stamp_clock_0p2s": round(float(clock), 5)}
+    log(f"span stamps: {res}")
+    return res
+
+
 def host_step_latency(args, mq, model, W, X, chain):
     import torch
     # End-to-end step latency as a caller sees it: launch the step, wait for
@@ -430,6 +494,7 @@ def run_decode(args, model, cpu_layers, probe=None):
     ms = wall * 1e3 / args.steps
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
+    stamps = None if args.no_stamps else span_stamps(args, mq, model, W, X)
     ab = None if args.no_ab else interleaved_arms(args, mq, model, W, X, chain, eager)
     lat = None if args.no_ab else host_step_latency(args, mq, model, W, X, chain)
 
@@ -452,6 +517,12 @@ def run_decode(args, model, cpu_layers, probe=None):
            "step_event_ms": round(float(np.mean(per_step)), 4), "step_event_sem_ms": round(sem(per_step), 5),
            "gemv_kernel_sum_ms": round(kernel_sum_ms, 4),
            "roofline": roof}
+    if stamps and roof["kernel"].startswith("mq::k_gemv_q4k_swiglu"):
+        us = stamps["per_kernel_us"]["gate_up"]
+        roof["in_graph_stamped_us_per_launch"] = us
+        roof["frac_in_graph_stamped"] = round(roof["bytes_per_launch"] / us / 1e3 / HBM_PEAK_GBS, 4)
+    if stamps:
+        out["span_stamps"] = stamps
     if ab:
         out["ab_interleaved"] = ab
     if lat:
@@ -675,6 +746,10 @@ def other_configs(args, probe):
                                  "tok_per_s": d["tok_per_s"], "GB_s": d["value"], "frac_of_8TBs": frac(d["value"]),
                                  "graph_nodes": d["config"]["graph_nodes"],
                                  "dominant_kernel_us": d["roofline"]["us_per_launch"]}
+    if "span_stamps" in d:
+        ss = d["span_stamps"]
+        out["c1_05b_decode_step"].update({"replay_span_us": ss["replay_span_us"], "kernel_sum_us": ss["kernel_sum_us"],
+                                          "span_over_kernel_sum": ss["span_over_sum"]})
     log(f"extra: 0.5B step {d['ms_per_step']} ms ({time.perf_counter() - t0:.1f} s)")
     s1 = run_single(a)
     out["c0_single_gemv"] = {"workload": s1["config"]["workload"],

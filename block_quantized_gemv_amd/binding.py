@@ -19,6 +19,7 @@ LIBRARY = os.path.join(HERE, "libmq.so")
 
 MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_HIP, MQ_ERR_CAPTURE, MQ_ERR_NOMEM = 0, -1, -2, -3, -4, -5
 MQ_EAGER_ONLY, MQ_KEEP_INTERMEDIATES, MQ_EXACT_GLUE, MQ_UNFUSED_GLUE, MQ_LAZY_CAPTURE, MQ_HOST_LOGITS = 1, 2, 4, 8, 16, 32
+MQ_SPAN_STAMPS = 64
 MQ_GRAPH, MQ_EAGER = 0, 1
 MQ_READ_PINNED, MQ_READ_PAGEABLE = 0, 1
 MQ_FMT_Q4_K, MQ_FMT_Q4_0 = 0, 1
@@ -83,6 +84,8 @@ SIGNATURES = {
     "mq_workspace_release": ([], _int),
     "mq_chain_trace_sizes": ([_vp, C.POINTER(_i64), C.POINTER(_i64)], _int),
     "mq_chain_read_trace": ([_vp, _vp, _vp, _vp], _int),
+    "mq_chain_read_stamps": ([_vp, _vp, _i64, _vp], _int),
+    "mq_chain_clear_stamps": ([_vp, _vp], _int),
     "mq_chain_destroy": ([_vp], _int),
     "mq_moe_create": ([C.POINTER(MoEDesc), _vp, C.POINTER(_vp)], _int),
     "mq_moe_step": ([_vp, _int, _vp], _int),
@@ -385,6 +388,7 @@ class DecodeChain:
         h = _vp()
         _check(lib().mq_chain_create(C.byref(d), _stream(stream), C.byref(h)))
         self.handle = h
+        self.n_stamped = 4 * L + 1 if flags & MQ_SPAN_STAMPS and not flags & MQ_UNFUSED_GLUE else 0
 
     def step(self, mode=MQ_GRAPH, stream=None):
         _check(lib().mq_decode_chain(self.handle, mode, _stream(stream)))
@@ -432,6 +436,19 @@ class DecodeChain:
         _check(lib().mq_chain_read_trace(self.handle, _ptr(q8), _ptr(f32), _stream(stream)))
         return q8, f32
 
+    def read_stamps(self, stream=None):
+        """MQ_SPAN_STAMPS: numpy uint64 [4*L + 1, 2] of [first wave start, last
+        wave end] (100 MHz ticks) of each GEMV kernel's most recent launch, in
+        step order (per layer QKV, O, gate/up, down; then the lm_head).
+        Blocking."""
+        out = np.zeros((self.n_stamped, 2), dtype=np.uint64)
+        _check(lib().mq_chain_read_stamps(self.handle, out.ctypes.data, self.n_stamped, _stream(stream)))
+        return out
+
+    def clear_stamps(self, stream=None):
+        """MQ_SPAN_STAMPS: reset the stamps on the stream (asynchronous)."""
+        _check(lib().mq_chain_clear_stamps(self.handle, _stream(stream)))
+
     def close(self):
         if getattr(self, "handle", None):
             lib().mq_chain_destroy(self.handle)
@@ -464,6 +481,7 @@ class MoEChain:
         h = _vp()
         _check(lib().mq_moe_create(C.byref(d), _stream(stream), C.byref(h)))
         self.handle = h
+        self.n_stamped = 4 * L + 1 if flags & MQ_SPAN_STAMPS and not flags & MQ_UNFUSED_GLUE else 0
 
     def step(self, mode=MQ_GRAPH, stream=None):
         _check(lib().mq_moe_step(self.handle, mode, _stream(stream)))
@@ -475,6 +493,19 @@ class MoEChain:
 
     def reset(self, step=0, stream=None):
         _check(lib().mq_chain_reset(self.handle, step, _stream(stream)))
+
+    def read_stamps(self, stream=None):
+        """MQ_SPAN_STAMPS: numpy uint64 [4*L + 1, 2] of [first wave start, last
+        wave end] (100 MHz ticks) of each GEMV kernel's most recent launch, in
+        step order (per layer QKV, O, gate/up, down; then the lm_head).
+        Blocking."""
+        out = np.zeros((self.n_stamped, 2), dtype=np.uint64)
+        _check(lib().mq_chain_read_stamps(self.handle, out.ctypes.data, self.n_stamped, _stream(stream)))
+        return out
+
+    def clear_stamps(self, stream=None):
+        """MQ_SPAN_STAMPS: reset the stamps on the stream (asynchronous)."""
+        _check(lib().mq_chain_clear_stamps(self.handle, _stream(stream)))
 
     def close(self):
         if getattr(self, "handle", None):

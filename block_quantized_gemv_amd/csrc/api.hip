@@ -195,6 +195,8 @@ struct mq_chain {
     double* gu_part = nullptr;        // decode step: row sums of the split gate/up blocks' halves
     unsigned* gu_cnt = nullptr;       // decode step: one hand-over counter per split gate/up block
     int gu_split = 0;                 // number of split gate/up blocks
+    uint64_t* stamps = nullptr;       // MQ_SPAN_STAMPS: [first-wave start, last-wave end] per GEMV kernel
+    int n_stamped = 0;                // number of stamped kernels (4 per layer + the lm_head)
     const int32_t* ids_table = nullptr;
     int n_tokens = 0, n_sel = 0;
     bool capture_tried = false;
@@ -212,6 +214,28 @@ void* chain_alloc(mq_chain* c, size_t bytes, int* rc) {
     }
     c->allocs.push_back(p);
     return p;
+}
+
+// Stamp pairs per kernel: one per wave slot (SpanStamp).
+constexpr int kStampPairs = kStampSlots * kStampWaves;
+
+__global__ void k_stamp_clear(uint64_t* __restrict__ p, int64_t n_pairs) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_pairs; i += (int64_t)gridDim.x * blockDim.x) {
+        p[2 * i] = ~(uint64_t)0;
+        p[2 * i + 1] = 0;
+    }
+}
+
+// Span stamps start as [max, 0] so that the kernels' atomic min / max
+// take their first values.
+int reset_stamps(mq_chain* c) {
+    std::vector<uint64_t> init((size_t)c->n_stamped * kStampPairs * 2);
+    for (size_t i = 0; i < init.size(); i += 2) {
+        init[i] = ~(uint64_t)0;
+        init[i + 1] = 0;
+    }
+    return hip_status(hipMemcpy(c->stamps, init.data(), init.size() * sizeof(uint64_t), hipMemcpyHostToDevice),
+                      "span stamp reset");
 }
 
 void chain_free(mq_chain* c) {
@@ -672,6 +696,12 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         if (rc == MQ_OK) c->gu_cnt = (unsigned*)chain_alloc(c, (size_t)gu_split * sizeof(unsigned), &rc);
         if (rc == MQ_OK) c->gu_split = gu_split;
     }
+    const bool stamped = (d->flags & MQ_SPAN_STAMPS) != 0 && !(d->flags & MQ_UNFUSED_GLUE);
+    if (rc == MQ_OK && stamped) {
+        c->n_stamped = 4 * L + 1;
+        c->stamps = (uint64_t*)chain_alloc(c, (size_t)c->n_stamped * kStampPairs * 2 * sizeof(uint64_t), &rc);
+        if (rc == MQ_OK) rc = reset_stamps(c);
+    }
     if (rc != MQ_OK) { chain_free(c); return rc; }
 
     const float eps = d->eps;
@@ -727,24 +757,31 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         float *t = f, *o = f + QKV, *gu = f + QKV + H, *h = f + QKV + H + 2 * I;
         const void *wq = d->w_qkv[l], *wo = d->w_o[l], *wg = d->w_gu[l], *wd = d->w_down[l];
         float* gu_keep = keep ? gu : nullptr;
-        const NormIn na = l == 0 ? NormIn{x_table, step, n_inputs, eps, keep ? qa : nullptr, nullptr, exact}
-                                 : NormIn{h_prev, nullptr, 1, eps, keep ? qa : nullptr, nullptr, exact};
-        const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr, exact};
-        const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr, exact};
+        // stamp regions: kStampPairs pairs per kernel, in step order
+        const int64_t sr = 2 * kStampPairs;
+        uint64_t* st = c->stamps ? c->stamps + 4 * l * sr : nullptr;
+        const NormIn na = l == 0 ? NormIn{x_table, step, n_inputs, eps, keep ? qa : nullptr, nullptr, exact, st}
+                                 : NormIn{h_prev, nullptr, 1, eps, keep ? qa : nullptr, nullptr, exact, st};
+        const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr, exact, st ? st + sr : nullptr};
+        const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr, exact, st ? st + 2 * sr : nullptr};
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s, fmt); });
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s, fmt); });
         double* gp = c->gu_part;
         unsigned* gc = c->gu_cnt;
         const int gn = c->gu_split;
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_swiglu(wg, nullptr, &nc, gu_keep, qg, I, H, s, fmt, gp, gc, gn); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s, fmt); });
+        if (st)
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_q8_stamped(wd, qg, h, H, I, s, fmt, st + 3 * sr); });
+        else
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wd, qg, 0, h, nullptr, nullptr, H, I, 1, s, fmt); });
         h_prev = h;
     }
     uint8_t* qz = c->q8_trace + (keep ? L * q8_layer : q8_layer);
     const void* wlm = d->w_lm;
     float* logits = d->logits;
     const int64_t V = d->vocab;
-    const NormIn nz{h_prev, nullptr, 1, eps, keep ? qz : nullptr, step, exact};
+    const NormIn nz{h_prev, nullptr, 1, eps, keep ? qz : nullptr, step, exact,
+                    c->stamps ? c->stamps + (int64_t)4 * L * 2 * kStampPairs : nullptr};
     c->ops.push_back([=](hipStream_t s) { return launch_gemv_q8_0_norm(wlm, nz, logits, V, H, s); });
     if (d->flags & MQ_HOST_LOGITS) add_host_logits(c);
     if (!keep) c->q8_bytes = c->f32_count = 0;
@@ -905,6 +942,36 @@ int mq_chain_read_trace(const mq_chain* c, void* q8_out, float* f32_out, hipStre
     if (e == hipSuccess && f32_out)
         e = hipMemcpyAsync(f32_out, c->f32_trace, c->f32_count * sizeof(float), hipMemcpyDeviceToDevice, stream);
     return hip_status(e, "trace copy");
+}
+
+int mq_chain_read_stamps(mq_chain* c, uint64_t* host_out, int64_t n_pairs, hipStream_t stream) {
+    CHECK_ARG(c && host_out, "null chain or output");
+    CHECK_ARG(c->stamps, "chain was created without MQ_SPAN_STAMPS");
+    CHECK_SHAPE(n_pairs == c->n_stamped, "n_pairs must be %d (4 per layer + 1)", c->n_stamped);
+    if (capturing(stream)) return fail(MQ_ERR_CAPTURE, "mq_chain_read_stamps cannot run inside a stream capture");
+    hipError_t e = hipStreamSynchronize(stream);
+    std::vector<uint64_t> all((size_t)n_pairs * kStampPairs * 2);
+    if (e == hipSuccess)
+        e = hipMemcpy(all.data(), c->stamps, all.size() * sizeof(uint64_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e, "span stamp read");
+    for (int64_t k = 0; k < n_pairs; ++k) {
+        uint64_t lo = ~(uint64_t)0, hi = 0;
+        for (int j = 0; j < kStampPairs; ++j) {
+            lo = std::min(lo, all[(k * kStampPairs + j) * 2]);
+            hi = std::max(hi, all[(k * kStampPairs + j) * 2 + 1]);
+        }
+        host_out[2 * k] = lo;
+        host_out[2 * k + 1] = hi;
+    }
+    return ok();
+}
+
+int mq_chain_clear_stamps(mq_chain* c, hipStream_t stream) {
+    CHECK_ARG(c, "null chain");
+    CHECK_ARG(c->stamps, "chain was created without MQ_SPAN_STAMPS");
+    const int64_t n = (int64_t)c->n_stamped * kStampPairs;
+    hipLaunchKernelGGL(k_stamp_clear, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, c->stamps, n);
+    return hip_status(hipGetLastError(), "span stamp clear");
 }
 
 int mq_chain_destroy(mq_chain* c) {

@@ -30,6 +30,37 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Kernel span stamps, compiled only into the instantiations that take them
+// (ON).  Each wave reads the real-time counter (100 MHz) when it starts and
+// again at its end, and lane 0 stores the pair [start, end] to its own slot
+// p[2*slot], p[2*slot+1], slot = workgroup * kStampWaves + wave: one plain
+// 16-byte store that nothing waits for, so the kernel's tail is the one it
+// has without stamps.  A launch overwrites the slots of the launch before
+// it (the grid is the same every step).  The host takes the minimum start
+// and the maximum end over the slots: the time from the kernel's first wave
+// start to its last wave end (the end is the wave's last instruction; its
+// stores drain after it).  Workgroups from kStampSlots on are not stamped.
+// The production instantiations carry none of this.
+constexpr int kStampSlots = 1024, kStampWaves = 16;
+template <bool ON>
+struct SpanStamp {
+    __device__ explicit SpanStamp(uint64_t*) {}
+};
+template <>
+struct SpanStamp<true> {
+    unsigned long long t0;
+    unsigned long long* p;
+    __device__ explicit SpanStamp(uint64_t* q)
+        : t0((unsigned long long)__builtin_amdgcn_s_memrealtime()), p((unsigned long long*)q) {}
+    __device__ ~SpanStamp() {
+        if (!p || (threadIdx.x & 63) != 0) return;
+        const unsigned long long t1 = (unsigned long long)__builtin_amdgcn_s_memrealtime();
+        if (blockIdx.x >= (unsigned)kStampSlots) return;
+        const unsigned slot = blockIdx.x * kStampWaves + (threadIdx.x >> 6);
+        *(ulonglong2*)(p + 2 * slot) = make_ulonglong2(t0, t1);
+    }
+};
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);   // v_dot4_i32_i8
 }

@@ -323,11 +323,12 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
 // tiles to different workgroups, so that every CU gets the same share.
 constexpr int kSrcQ8 = 0, kSrcQ8Early = 1, kSrcNorm = 2;
 
-template <int FMT, int NC, bool DUMP, int SRC>
+template <int FMT, int NC, bool DUMP, int SRC, bool ST = false>
 __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) __attribute__((amdgpu_waves_per_eu(1, NC >= 5 ? 3 : 8))) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
     int M, int nsb, int log2s, int passes, int n_tiles, NormIn nin) {
+    const SpanStamp<ST> span(nin.stamp);
     extern __shared__ __align__(16) uint8_t lds[];
     const Lanes ln(log2s, nsb);
     const int nb = nsb * 8;
@@ -612,11 +613,12 @@ __global__ __launch_bounds__(256) void k_gemv_q4k_grouped(
 // values are the ones the plain GEMV would write.  With NORM the input is
 // Q8(RMSNorm(x)) formed in the prologue (8 waves, so that fewer
 // workgroups repeat it); otherwise xq (4 waves).
-template <int FMT, bool NORM>
+template <int FMT, bool NORM, bool ST = false>
 __global__ __launch_bounds__(NORM ? 512 : 256) void k_gemv_q4k_swiglu(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* __restrict__ gu_out,
     uint8_t* __restrict__ g_q8, int inter, int nsb, NormIn nin, double* __restrict__ part,
     unsigned* __restrict__ cnt) {
+    const SpanStamp<ST> span(nin.stamp);
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ float gu_s[64];
     __shared__ double gu_d[64];
@@ -1137,7 +1139,7 @@ void prologue_grid(int64_t units, int64_t prologue, int* grid, int* threads, int
 // One q8_0 column with early staging (see k_gemv_q4k).
 template <int FMT>
 static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64_t m, int nsb,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, uint64_t* stamp = nullptr) {
     const Q4KPlan p = plan_q4k(m, nsb);
     const int lds = stage_bytes(nsb * 8);
     // waves per CU for about kItemsPerWave items each, within [7, 12]
@@ -1146,10 +1148,24 @@ static hipError_t launch_q8_early(const void* w, const void* xq, float* y, int64
     const int cap = (int)(want < kWavesQ8EarlyMin ? kWavesQ8EarlyMin : want > kWavesQ8EarlyMax ? kWavesQ8EarlyMax : want);
     int grid = 1, threads = 64;
     prologue_grid(p.n_tiles, (nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads, cap);
-    MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream,
-              (const uint8_t*)w, (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m,
-              nsb, p.log2s, p.passes, p.n_tiles, NormIn{});
+    if (stamp) {
+        MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcQ8Early, true>), dim3(grid), dim3(threads), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr,
+                  (int)m, nsb, p.log2s, p.passes, p.n_tiles, NormIn{nullptr, nullptr, 0, 0.0f, nullptr, nullptr, 0, stamp});
+    } else {
+        MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)xq, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr,
+                  (int)m, nsb, p.log2s, p.passes, p.n_tiles, NormIn{});
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_q4k_q8_stamped(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                                      hipStream_t stream, int fmt, uint64_t* stamp) {
+    if (m > max_rows_per_launch(k)) return hipErrorInvalidValue;
+    const int nsb = (int)(k / 256);
+    return fmt == kFmtQ4_0 ? launch_q8_early<kFmtQ4_0>(w, xq, y, m, nsb, stream, stamp)
+                           : launch_q8_early<kFmtQ4K>(w, xq, y, m, nsb, stream, stamp);
 }
 
 template <int FMT>
@@ -1160,9 +1176,15 @@ static hipError_t launch_norm(const void* w, const NormIn& nin, float* y, int64_
     const int lds = stage_bytes(nsb * 8);
     int grid = 1, threads = 64;
     prologue_grid(p.n_tiles, k / 4, &grid, &threads, kWavesNorm);
-    MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcNorm>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
-              (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb,
-              p.log2s, p.passes, p.n_tiles, nin);
+    if (nin.stamp) {
+        MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcNorm, true>), dim3(grid), dim3(threads), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr,
+                  (int)m, nsb, p.log2s, p.passes, p.n_tiles, nin);
+    } else {
+        MQ_LAUNCH((k_gemv_q4k<FMT, 1, false, kSrcNorm>), dim3(grid), dim3(threads), lds, stream,
+                  (const uint8_t*)w, (const uint8_t*)nullptr, (int64_t)0, y, (int32_t*)nullptr, (int32_t*)nullptr,
+                  (int)m, nsb, p.log2s, p.passes, p.n_tiles, nin);
+    }
     return hipGetLastError();
 }
 
@@ -1266,8 +1288,14 @@ static hipError_t launch_swiglu(const void* w, const void* xq, const NormIn* nin
         // halves need two passes or more; the hand-over space is the caller's
         const bool ok = part && cnt && n_split > 0 && n_split <= (int)nblk && (nsb + 3) / 4 >= 2;
         const int ns = ok ? n_split : 0;
-        MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true>), dim3(nblk + (unsigned)ns), dim3(512), lds, stream,
-                  (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin, part, cnt);
+        if (nin->stamp)
+            MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true, true>), dim3(nblk + (unsigned)ns), dim3(512), lds, stream,
+                      (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin, part,
+                      cnt);
+        else
+            MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, true>), dim3(nblk + (unsigned)ns), dim3(512), lds, stream,
+                      (const uint8_t*)w, (const uint8_t*)nullptr, gu_out, (uint8_t*)g_q8, (int)inter, nsb, *nin, part,
+                      cnt);
     } else {
         MQ_LAUNCH((k_gemv_q4k_swiglu<FMT, false>), dim3(nblk), dim3(256), lds, stream,
                   (const uint8_t*)w, (const uint8_t*)xq, gu_out, (uint8_t*)g_q8, (int)inter, nsb, NormIn{},

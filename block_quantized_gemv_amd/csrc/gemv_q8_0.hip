@@ -57,13 +57,14 @@ __device__ __forceinline__ double pair_item(const PairLoad& L, const uint8_t* __
 // With NORM the activation is Q8(RMSNorm(x)) of the f32 vector `nin`
 // describes, formed in each workgroup's prologue (workgroups of up to 1024
 // threads, about one per CU); otherwise xq holds it.
-template <bool DUMP, bool NORM>
+template <bool DUMP, bool NORM, bool ST = false>
 __global__ __launch_bounds__(NORM ? 1024 : 256) void k_gemv_q8_0(const uint8_t* __restrict__ w,
                                                                 const uint8_t* __restrict__ xq,
                                                                 float* __restrict__ y,
                                                                 int32_t* __restrict__ dump_isum, int M,
                                                                 int npairs, int log2s, int passes,
                                                                 int n_tiles, NormIn nin) {
+    const SpanStamp<ST> span(nin.stamp);
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
     const int S = 1 << log2s, R = 64 >> log2s;
@@ -182,6 +183,10 @@ hipError_t launch_gemv_q8_0_norm(const void* w, const NormIn& nin, float* y, int
         hipExtLaunchKernelGGL((k_gemv_q8_0<false, true>), dim3(grid), dim3(threads), lds, stream, e0, e1, 0,
                               (const uint8_t*)w, (const uint8_t*)nullptr, y, (int32_t*)nullptr, (int)m, npairs,
                               p.log2s, p.passes, p.n_tiles, nin);
+    } else if (nin.stamp) {
+        hipLaunchKernelGGL((k_gemv_q8_0<false, true, true>), dim3(grid), dim3(threads), lds, stream,
+                           (const uint8_t*)w, (const uint8_t*)nullptr, y, (int32_t*)nullptr, (int)m, npairs, p.log2s,
+                           p.passes, p.n_tiles, nin);
     } else {
         hipLaunchKernelGGL((k_gemv_q8_0<false, true>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
                            (const uint8_t*)nullptr, y, (int32_t*)nullptr, (int)m, npairs, p.log2s, p.passes,

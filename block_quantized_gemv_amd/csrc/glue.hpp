@@ -115,6 +115,7 @@ struct NormIn {
     uint8_t* q8_copy;
     int64_t* inc_step;
     int exact;          // take the division path for every value (test hook)
+    uint64_t* stamp;    // kernel span stamps (SpanStamp), or null
 };
 
 // ------------------------------------------- RMSNorm -> q8_0 in a prologue ----
@@ -355,9 +356,14 @@ __device__ __forceinline__ void stage_rmsnorm_q8(const float* __restrict__ x, in
 }
 
 // The input row of a GEMV fed by a NormIn.
+// The step counter is read through the constant address space: no kernel
+// that selects a row with it also writes it, so the load may always go
+// through the scalar unit (the compiler cannot prove that on its own once
+// a side-effecting instruction, such as a clock read, precedes it).
 __device__ __forceinline__ const float* norm_row(const NormIn& in, int k) {
+    typedef const __attribute__((address_space(4))) int64_t const_i64;
     const float* x = in.x;
-    if (in.sel_step) x += (int64_t)((uint64_t)*in.sel_step % (uint64_t)in.n_inputs) * k;
+    if (in.sel_step) x += (int64_t)((uint64_t)*(const_i64*)(uintptr_t)in.sel_step % (uint64_t)in.n_inputs) * k;
     return x;
 }
 

@@ -49,6 +49,10 @@ int64_t max_rows_per_launch(int64_t k);
 hipError_t launch_gemv_q4k(const void* w, const void* xq, int64_t xq_col_bytes, float* y,
                            int32_t* dump_isum, int32_t* dump_ysum, int64_t m, int64_t k, int ncols,
                            hipStream_t stream, int fmt = kFmtQ4K);
+// One q8_0 column, m <= max_rows_per_launch(k), with the kernel's span
+// stamps folded into stamp[0..1] (SpanStamp) when stamp is set.
+hipError_t launch_gemv_q4k_q8_stamped(const void* w, const void* xq, float* y, int64_t m, int64_t k,
+                                      hipStream_t stream, int fmt, uint64_t* stamp);
 // The 4-bit GEMV of one activation Q8(RMSNorm(x)) formed in the kernel's
 // prologue from the f32 input nin describes (the decode-step chain).
 hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int64_t m, int64_t k,

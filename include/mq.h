@@ -281,8 +281,19 @@ typedef struct mq_chain mq_chain;
  * no host-side copy: a host copy that follows a DMA reads cold memory and
  * costs more than the DMA.  If pinning fails the chain is created without
  * the copy (mq_chain_host_logits gives NULL) and one warning is printed. */
+/* MQ_SPAN_STAMPS (measurement; fused step only, ignored with
+ * MQ_UNFUSED_GLUE) gives each of the step's 4*n_layers + 1 GEMV kernels a
+ * [start, end] pair: the GPU's 100 MHz real-time counter when the
+ * kernel's first wave started (minimum over its waves) and when its last
+ * wave ended (maximum, taken after the wave's memory operations complete).
+ * Each wave stores its own pair (256 KiB of device words per kernel,
+ * allocated with the chain); mq_chain_read_stamps reduces and returns
+ * them, so that a replay's span (last end minus first start) can be set
+ * against the sum of the kernels' own spans without a tracer in the
+ * process.  Chains without the flag pass no stamp words; the kernels read
+ * the counter at wave start either way (one scalar instruction). */
 enum { MQ_EAGER_ONLY = 1u, MQ_KEEP_INTERMEDIATES = 2u, MQ_EXACT_GLUE = 4u, MQ_UNFUSED_GLUE = 8u,
-       MQ_LAZY_CAPTURE = 16u, MQ_HOST_LOGITS = 32u };
+       MQ_LAZY_CAPTURE = 16u, MQ_HOST_LOGITS = 32u, MQ_SPAN_STAMPS = 64u };
 enum { MQ_GRAPH = 0, MQ_EAGER = 1 };
 /* Weight format of the four layer GEMVs (the lm_head is q8_0 either way). */
 enum { MQ_FMT_Q4_K = 0, MQ_FMT_Q4_0 = 1 };
@@ -300,7 +311,7 @@ typedef struct {
     float* logits;                     /* device f32 [vocab] */
     float eps;
     unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE | MQ_UNFUSED_GLUE
-                                          | MQ_LAZY_CAPTURE | MQ_HOST_LOGITS */
+                                          | MQ_LAZY_CAPTURE | MQ_HOST_LOGITS | MQ_SPAN_STAMPS */
     int weight_format;                 /* MQ_FMT_Q4_K or MQ_FMT_Q4_0 (layer matrices) */
 } mq_chain_desc;
 
@@ -352,6 +363,19 @@ int mq_chain_reset(mq_chain* c, int64_t step, hipStream_t stream);
  * Sizes: mq_chain_trace_sizes. */
 int mq_chain_trace_sizes(const mq_chain* c, int64_t* q8_bytes, int64_t* f32_count);
 int mq_chain_read_trace(const mq_chain* c, void* q8_out, float* f32_out, hipStream_t stream);
+/* With MQ_SPAN_STAMPS: synchronize `stream` and write into HOST memory
+ * host_out[2*n_pairs] the stamp pair of each GEMV kernel (per layer QKV, O,
+ * gate/up, down, then the lm_head): [first wave start, last wave end] in
+ * 100 MHz ticks of its most recent launch (each launch overwrites the
+ * previous one's words; a kernel not launched since creation or the last
+ * mq_chain_clear_stamps reads [UINT64_MAX, 0]).  n_pairs must be
+ * 4*n_layers + 1 (MQ_ERR_SHAPE otherwise); MQ_ERR_ARG without the flag;
+ * MQ_ERR_CAPTURE while `stream` is being captured.  Blocking. */
+int mq_chain_read_stamps(mq_chain* c, uint64_t* host_out, int64_t n_pairs, hipStream_t stream);
+/* With MQ_SPAN_STAMPS: enqueue on `stream` a kernel that resets every
+ * stamp word to "not launched" (no synchronization).  MQ_ERR_ARG without
+ * the flag. */
+int mq_chain_clear_stamps(mq_chain* c, hipStream_t stream);
 int mq_chain_destroy(mq_chain* c);
 
 /* ---------------------------------------------------------------------------

@@ -116,6 +116,9 @@ def test_chain_argument_errors(mq):
     assert "weight_format" in L.mq_last_error().decode()
     d.weight_format = mq.MQ_FMT_Q4_K
     assert L.mq_decode_chain(None, 0, None) == mq.MQ_ERR_ARG
+    buf = (C.c_uint64 * 4)()
+    assert L.mq_chain_read_stamps(None, buf, 2, None) == mq.MQ_ERR_ARG
+    assert L.mq_chain_clear_stamps(None, None) == mq.MQ_ERR_ARG
     assert L.mq_chain_destroy(None) == mq.MQ_OK
     m = mq.MoEDesc(64, 8, 2048, 1408, FAKE, 16, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 10, 0)
     assert L.mq_moe_create(C.byref(m), None, C.byref(out)) == mq.MQ_ERR_SHAPE          # expert bytes too small

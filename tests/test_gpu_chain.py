@@ -154,6 +154,42 @@ def test_graph_aa_control(mq, small_model):
         assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), "A/A graph mismatch"
 
 
+def test_span_stamps(mq, small_model):
+    """MQ_SPAN_STAMPS: the stamped step gives the same bytes as the plain one;
+    every GEMV kernel's stamp pair is filled (start < end), the kernels follow
+    one another (each starts after the previous one's last wave ended, within
+    the counter's 10 ns tick), every step overwrites the pairs, a read
+    changes nothing, a clear resets them, and the chain refuses a wrong pair
+    count or a chain without the flag."""
+    model, W, Wd, X = small_model
+    xd = to_dev(X)
+    plain, stamped = mq.DecodeChain(model, Wd, xd), mq.DecodeChain(model, Wd, xd, flags=mq.MQ_SPAN_STAMPS)
+    n = 4 * model.n_layers + 1
+    assert stamped.n_stamped == n
+    prev = None
+    for _ in range(3):
+        assert _same(to_host(plain.step()), to_host(stamped.step()))
+        st = stamped.read_stamps().astype(np.int64)
+        assert st.shape == (n, 2)
+        assert (st[:, 1] > st[:, 0]).all(), st
+        assert (st[1:, 0] >= st[:-1, 1] - 1).all(), "kernels of one replay overlap"
+        span_us = (st[-1, 1] - st[0, 0]) * 0.01
+        assert 0 < span_us < 10000, span_us
+        if prev is not None:
+            assert st[0, 0] > prev[-1, 1], "a step did not overwrite the previous step's stamps"
+        prev = st
+    assert np.array_equal(stamped.read_stamps().astype(np.int64), prev)   # a read changes nothing
+    stamped.clear_stamps()              # the device-side clear
+    st = stamped.read_stamps()
+    assert (st[:, 0] == np.iinfo(np.uint64).max).all() and (st[:, 1] == 0).all()
+    buf = np.zeros((n, 2), dtype=np.uint64)
+    L = mq.lib()
+    assert L.mq_chain_read_stamps(stamped.handle, buf.ctypes.data, n - 1, None) == mq.MQ_ERR_SHAPE
+    assert L.mq_chain_read_stamps(plain.handle, buf.ctypes.data, n, None) == mq.MQ_ERR_ARG
+    plain.close()
+    stamped.close()
+
+
 def test_capture_failure_falls_back_to_eager(mq, small_model):
     model, W, Wd, X = small_model
     xd = to_dev(X)
