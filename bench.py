@@ -18,6 +18,9 @@ in HBM.  Prints one JSON line (rank 0):
                byte-weighted aggregate of the four per-layer q4_K GEMVs
   stream_probe = the rate of a plain 16-byte-load read of 4 GiB
                (mq_probe_stream_read), measured first in the same run
+  sync_probe = per GEMV boundary, what a resident (persistent) step would
+               pay (a grid barrier carrying the hidden vector between the
+               XCDs) against the graph's own cost per kernel boundary
   span_stamps = the step's replay span against the sum of its kernels' own
                spans (first wave start to last wave end), both from the
                kernels' real-time-counter stamps with no tracer present
@@ -407,6 +410,34 @@ def span_stamps(args, mq, model, W, X, steps=100):
     return res
 
 
+def sync_probe(mq, model, stamps=None):
+    """What a resident (persistent) step would pay per GEMV boundary against
+    what the graph pays: grid-barrier rounds on one 512-thread workgroup per
+    CU (flat and per-XCD counters), bare and carrying the model's hidden
+    vector (each workgroup writes its slice with agent-scope stores, then all
+    read all of it), and the graph's cost per empty kernel on the same grid."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    words = -(-model.hidden // cus)
+    res = {"threads": 512, "workgroups": cus, "exchange_words_per_workgroup": words,
+           "exchange": f"each workgroup writes {words} f32 of the {model.hidden}-wide vector, then reads all of it"}
+    for hier, name in ((0, "flat"), (1, "xcd_hierarchical")):
+        bare, bad0 = mq.mq_probe_grid_barrier(hier, 0, rounds=2000)
+        ex, bad1 = mq.mq_probe_grid_barrier(hier, words, rounds=2000)
+        assert bad0 == 0 and bad1 == 0, "the barrier probe read a stale word"
+        res[f"barrier_{name}_us"] = round(bare, 3)
+        res[f"barrier_{name}_with_exchange_us"] = round(ex, 3)
+    res["graph_empty_kernel_us"] = round(mq.mq_probe_graph_boundary(n_kernels=200, threads=512, reps=10), 3)
+    best = min(res["barrier_flat_with_exchange_us"], res["barrier_xcd_hierarchical_with_exchange_us"])
+    res["best_barrier_with_exchange_us"] = best
+    if stamps:
+        n = stamps["kernels_per_step"]
+        res["graph_gaps_per_step_us"] = round((n - 1) * stamps["mean_gap_between_kernels_us"], 1)
+        res["persistent_barriers_per_step_us"] = round((n - 1) * best, 1)
+    log(f"sync probe: {res}")
+    return res
+
+
 def host_step_latency(args, mq, model, W, X, chain):
     import torch
     # End-to-end step latency as a caller sees it: launch the step, wait for
@@ -495,6 +526,7 @@ def run_decode(args, model, cpu_layers, probe=None):
     log(f"graph: {ms:.4f} ms/step wall, event mean {np.mean(per_step):.4f} sem {sem(per_step):.4f}")
 
     stamps = None if args.no_stamps else span_stamps(args, mq, model, W, X)
+    sync = None if args.no_stamps else sync_probe(mq, model, stamps)
     ab = None if args.no_ab else interleaved_arms(args, mq, model, W, X, chain, eager)
     lat = None if args.no_ab else host_step_latency(args, mq, model, W, X, chain)
 
@@ -523,6 +555,8 @@ def run_decode(args, model, cpu_layers, probe=None):
         roof["frac_in_graph_stamped"] = round(roof["bytes_per_launch"] / us / 1e3 / HBM_PEAK_GBS, 4)
     if stamps:
         out["span_stamps"] = stamps
+    if sync:
+        out["sync_probe"] = sync
     if ab:
         out["ab_interleaved"] = ab
     if lat:
@@ -749,7 +783,12 @@ def other_configs(args, probe):
     if "span_stamps" in d:
         ss = d["span_stamps"]
         out["c1_05b_decode_step"].update({"replay_span_us": ss["replay_span_us"], "kernel_sum_us": ss["kernel_sum_us"],
-                                          "span_over_kernel_sum": ss["span_over_sum"]})
+                                          "span_over_kernel_sum": ss["span_over_sum"],
+                                          "mean_gap_between_kernels_us": ss["mean_gap_between_kernels_us"]})
+    if "sync_probe" in d:
+        sp = d["sync_probe"]
+        out["c1_05b_decode_step"].update({"best_grid_barrier_with_exchange_us": sp["best_barrier_with_exchange_us"],
+                                          "graph_empty_kernel_us": sp["graph_empty_kernel_us"]})
     log(f"extra: 0.5B step {d['ms_per_step']} ms ({time.perf_counter() - t0:.1f} s)")
     s1 = run_single(a)
     out["c0_single_gemv"] = {"workload": s1["config"]["workload"],

@@ -92,6 +92,8 @@ SIGNATURES = {
     "mq_test_set_fault": ([_u32], _int),
     "mq_time_next_launches": ([C.POINTER(_vp), C.POINTER(_vp), _int], _int),
     "mq_probe_stream_read": ([_vp, _i64, _vp, _int, _vp], _int),
+    "mq_probe_grid_barrier": ([_int, _int, _int, _int, _vp, _vp, _vp], _int),
+    "mq_probe_graph_boundary": ([_int, _int, _int, _vp], _int),
 }
 
 _LIB = None
@@ -162,6 +164,21 @@ def mq_time_next_launches(starts, stops):
     n = len(starts)
     a, b = (_vp * max(n, 1))(*starts), (_vp * max(n, 1))(*stops)
     _check(lib().mq_time_next_launches(a, b, n))
+
+
+def mq_probe_grid_barrier(hierarchical, exchange_words, rounds=2000, threads=512, stream=None):
+    """Grid-barrier probe (one workgroup per CU): (us per round, mismatched words)."""
+    us, bad = C.c_double(), C.c_uint32()
+    _check(lib().mq_probe_grid_barrier(int(hierarchical), exchange_words, rounds, threads, C.byref(us), C.byref(bad),
+                                       _stream(stream)))
+    return us.value, bad.value
+
+
+def mq_probe_graph_boundary(n_kernels=200, threads=512, reps=10):
+    """Microseconds per empty kernel in a graph replay (one workgroup per CU)."""
+    us = C.c_double()
+    _check(lib().mq_probe_graph_boundary(n_kernels, threads, reps, C.byref(us)))
+    return us.value
 
 
 def mq_probe_stream_read(buf, xor_out=None, workgroups=0, stream=None):

@@ -413,6 +413,35 @@ int mq_probe_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int wo
     return hip_status(launch_stream_read(p, bytes, xor_out, workgroups, stream), "stream probe launch");
 }
 
+int mq_probe_grid_barrier(int hierarchical, int exchange_words, int rounds, int threads, double* us_per_round,
+                          uint32_t* bad_words, hipStream_t stream) {
+    CHECK_ARG(us_per_round && bad_words, "null output pointer");
+    CHECK_ARG(hierarchical == 0 || hierarchical == 1, "hierarchical must be 0 or 1");
+    CHECK_ARG(exchange_words >= 0 && exchange_words <= 4096, "exchange_words=%d out of range [0, 4096]", exchange_words);
+    CHECK_ARG(rounds >= 1 && rounds <= 100000, "rounds=%d out of range [1, 100000]", rounds);
+    CHECK_ARG(threads >= 64 && threads <= 1024 && threads % 64 == 0, "threads=%d must be a multiple of 64 in [64, 1024]",
+              threads);
+    if (capturing(stream)) return fail(MQ_ERR_CAPTURE, "the barrier probe cannot run inside a stream capture");
+    int limit_hit = 0;
+    const int rc = grid_barrier_probe(hierarchical, exchange_words, rounds, threads, us_per_round, bad_words,
+                                      &limit_hit, stream);
+    if (rc == 1) return fail(MQ_ERR_SHAPE, "a grid of one %d-thread workgroup per CU cannot be co-resident", threads);
+    if (rc != 0) return fail(MQ_ERR_HIP, "barrier probe: a HIP call failed");
+    if (limit_hit) return fail(MQ_ERR_HIP, "barrier probe: a wait ran out of polls");
+    return ok();
+}
+
+int mq_probe_graph_boundary(int n_kernels, int threads, int reps, double* us_per_kernel) {
+    CHECK_ARG(us_per_kernel, "null output pointer");
+    CHECK_ARG(n_kernels >= 1 && n_kernels <= 4096, "n_kernels=%d out of range [1, 4096]", n_kernels);
+    CHECK_ARG(reps >= 1 && reps <= 10000, "reps=%d out of range [1, 10000]", reps);
+    CHECK_ARG(threads >= 64 && threads <= 1024 && threads % 64 == 0, "threads=%d must be a multiple of 64 in [64, 1024]",
+              threads);
+    if (graph_boundary_probe(n_kernels, threads, reps, us_per_kernel) != 0)
+        return fail(MQ_ERR_HIP, "graph boundary probe: a HIP call failed");
+    return ok();
+}
+
 int mq_read_to_host(const void* src, void* host_dst, int64_t bytes, unsigned flags, hipStream_t stream) {
     CHECK_ARG((flags & ~(unsigned)MQ_READ_PAGEABLE) == 0, "unknown flags %#x", flags);
     CHECK_ARG(bytes >= 0, "bytes=%lld must be >= 0", (long long)bytes);

@@ -137,6 +137,11 @@ hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 // XOR of the 32-bit words of bytes (multiple of 16) at p (16-byte aligned)
 // into *xor_out; workgroups <= 0 means one per CU.
+// Synchronization probes (sync_probe.hip); 0 = measured, 1 = the grid
+// cannot be co-resident, 2 = a HIP call failed.
+int grid_barrier_probe(int hierarchical, int words, int rounds, int threads, double* us_per_round,
+                       uint32_t* bad_words, int* spin_limit_hit, hipStream_t stream);
+int graph_boundary_probe(int n_kernels, int threads, int reps, double* us_per_kernel);
 hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int workgroups,
                               hipStream_t stream);
 

@@ -451,6 +451,34 @@ int mq_probe_stream_read(const void* p, int64_t bytes, uint32_t* xor_out, int wo
                          hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Measurement: what a resident ("persistent") step would pay at each GEMV
+ * boundary ('Part 4 · Lecture 08', References: one resident kernel as the
+ * endpoint of graph capture), against what a graph replay pays.
+ *
+ * mq_probe_grid_barrier runs one workgroup of `threads` per CU (refused with
+ * MQ_ERR_SHAPE if such a grid cannot be co-resident) for `rounds` rounds of:
+ * write this workgroup's exchange_words 32-bit words of a vector with
+ * agent-scope stores, wait for them, meet every workgroup at a grid
+ * barrier, read the whole vector (CUs * exchange_words words) back with
+ * agent-scope loads and check each word.  hierarchical = 0: one agent-scope
+ * counter that every workgroup polls; 1: per-XCD counters (XCD from the
+ * XCC_ID register), a global count of XCDs, and a per-XCD release flag.
+ * Writes the time per round in microseconds (the device's 100 MHz counter)
+ * and the number of mismatched words read (0 unless the barrier failed to
+ * order the exchange).  Every wait is bounded; a wait that runs out of polls
+ * ends the kernel and returns MQ_ERR_HIP.  Allocates and frees its own
+ * device buffers; blocking; MQ_ERR_CAPTURE under capture.
+ *
+ * mq_probe_graph_boundary captures n_kernels empty kernels on one workgroup
+ * of `threads` per CU into a graph on a private stream, replays it 3 times,
+ * then `reps` times under events, and writes the time per kernel in
+ * microseconds: the cost of one kernel boundary inside a replay.  Blocking.
+ */
+int mq_probe_grid_barrier(int hierarchical, int exchange_words, int rounds, int threads, double* us_per_round,
+                          uint32_t* bad_words, hipStream_t stream);
+int mq_probe_graph_boundary(int n_kernels, int threads, int reps, double* us_per_kernel);
+
+/* ---------------------------------------------------------------------------
  * Device-to-host readback through a pinned staging buffer ('07 · R3', §2 and
  * §3.1).  A copy into pageable host memory makes the driver bounce it
  * through a pinned buffer of its own (two hops); a copy into memory pinned

@@ -74,6 +74,14 @@ def test_stream_probe_argument_errors(mq):
     assert L.mq_probe_stream_read(C.c_void_p(0x10008), 64, FAKE, 0, None) == mq.MQ_ERR_ARG   # not 16-aligned
     assert L.mq_probe_stream_read(FAKE, 40, FAKE, 0, None) == mq.MQ_ERR_ARG                  # not a multiple of 16
     assert L.mq_probe_stream_read(FAKE, 64, FAKE, 70000, None) == mq.MQ_ERR_ARG              # workgroups
+    us, bad = C.c_double(), C.c_uint32()
+    assert L.mq_probe_grid_barrier(2, 4, 10, 512, C.byref(us), C.byref(bad), None) == mq.MQ_ERR_ARG   # hierarchical
+    assert L.mq_probe_grid_barrier(0, 5000, 10, 512, C.byref(us), C.byref(bad), None) == mq.MQ_ERR_ARG
+    assert L.mq_probe_grid_barrier(0, 4, 0, 512, C.byref(us), C.byref(bad), None) == mq.MQ_ERR_ARG    # rounds
+    assert L.mq_probe_grid_barrier(0, 4, 10, 100, C.byref(us), C.byref(bad), None) == mq.MQ_ERR_ARG   # threads
+    assert L.mq_probe_grid_barrier(0, 4, 10, 512, None, C.byref(bad), None) == mq.MQ_ERR_ARG
+    assert L.mq_probe_graph_boundary(0, 512, 10, C.byref(us)) == mq.MQ_ERR_ARG
+    assert L.mq_probe_graph_boundary(10, 512, 10, None) == mq.MQ_ERR_ARG
 
 
 def test_readback_argument_errors(mq):

@@ -460,6 +460,22 @@ def test_grouped_down_combine_kernel(mq, o, experts):
 
 # ------------------------------------------------------ measurement probe ----
 
+def test_sync_probes(mq):
+    """The grid-barrier probe orders its exchange (every word read back after
+    each barrier is the one written before it, flat and per-XCD barriers, with
+    and without an exchange), its per-round time is positive and finite, and
+    the graph-boundary probe gives a positive time per kernel."""
+    for hier in (0, 1):
+        for words in (0, 4, 64):
+            us, bad = mq.mq_probe_grid_barrier(hier, words, rounds=300)
+            log(f"grid barrier hier={hier} words={words}: {us:.3f} us/round")
+            assert bad == 0, (hier, words, bad)
+            assert 0.0 < us < 1000.0, (hier, words, us)
+    us = mq.mq_probe_graph_boundary(n_kernels=50, reps=3)
+    log(f"graph boundary: {us:.3f} us/kernel")
+    assert 0.0 < us < 1000.0
+
+
 def test_stream_probe_reads_every_word(mq):
     """The streaming-read probe's XOR over all 32-bit words equals numpy's, for
     sizes that end inside the four-load body and inside the tail loop, and for
