@@ -93,6 +93,7 @@ SIGNATURES = {
     "mq_time_next_launches": ([C.POINTER(_vp), C.POINTER(_vp), _int], _int),
     "mq_probe_stream_read": ([_vp, _i64, _vp, _int, _vp], _int),
     "mq_probe_grid_barrier": ([_int, _int, _int, _int, _vp, _vp, _vp], _int),
+    "mq_debug_gemv_q4k_batched_path": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp], _int),
     "mq_probe_graph_boundary": ([_int, _int, _int, _vp], _int),
 }
 
@@ -261,6 +262,17 @@ def mq_gemv_q4k_q8_batched(w, xq, m, k, n, y=None, stream=None):
     _check(lib().mq_gemv_q4k_q8_batched(_ptr(w, torch.uint8, q4k_bytes(m, k), "w"),
                                         _ptr(xq, torch.uint8, q8_bytes(n, k), "xq"),
                                         _ptr(y, torch.float32, 4 * m * n, "y"), m, k, n, _stream(stream)))
+    return y
+
+
+def mq_debug_gemv_q4k_batched_path(w, xq, m, k, n, path, y=None, stream=None):
+    """The batched GEMV forced onto path 0 (vector kernels) or 1 (matrix cores)."""
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check(lib().mq_debug_gemv_q4k_batched_path(_ptr(w, torch.uint8, q4k_bytes(m, k), "w"),
+                                                _ptr(xq, torch.uint8, q8_bytes(n, k), "xq"),
+                                                _ptr(y, torch.float32, 4 * m * n, "y"), m, k, n, path,
+                                                _stream(stream)))
     return y
 
 

@@ -20,6 +20,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # matrix-core results in ordinary VGPRs (no copies out of AGPRs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

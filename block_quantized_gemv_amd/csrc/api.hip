@@ -118,8 +118,31 @@ int workspace(size_t need, hipStream_t stream, void** out) {
 
 // Chooses full staging or split-k for a 4-bit GEMV with ncols columns
 // (the debug dump runs with full staging only).
+// Batched q4_K GEMVs with at least this many columns run on the matrix
+// cores (gemv_mfma.hip); fewer columns, q4_0 and the dump run the vector
+// kernels.  Measured on MI355X at the 7B shapes (cold, n = 2..8): the
+// matrix cores take the same time for any n, the vector kernels' time
+// grows with n; they tie at n = 4 and the matrix cores lead from n = 5
+// (gate/up 24 vs 37 us at n = 8).
+constexpr int kMfmaMinCols = 5;
+
+bool use_mfma(int fmt, int ncols) { return fmt == kFmtQ4K && ncols >= kMfmaMinCols; }
+
+int run_q4k_mfma(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t m, int64_t k, int ncols,
+                 hipStream_t stream) {
+    void* ws = nullptr;
+    const int64_t need = gemv_q4k_mfma_partial_bytes(m, k, ncols);
+    if (need > 0) {
+        const int rc = workspace((size_t)need, stream, &ws);
+        if (rc != MQ_OK) return rc;
+    }
+    return hip_status(launch_gemv_q4k_mfma(w, xq, col_bytes, y, (double*)ws, m, k, ncols, stream),
+                      "matrix-core GEMV launch");
+}
+
 int run_q4(int fmt, const void* w, const void* xq, int64_t col_bytes, float* y, int32_t* isum, int32_t* ysum,
            int64_t m, int64_t k, int ncols, hipStream_t stream) {
+    if (!isum && use_mfma(fmt, ncols)) return run_q4k_mfma(w, xq, col_bytes, y, m, k, ncols, stream);
     const int lds = ncols * stage_bytes((int)(k / 32));
     if (lds <= kMaxStageLds)
         return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, isum, ysum, m, k, ncols, stream, fmt),
@@ -549,6 +572,16 @@ int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int6
     if (rc != MQ_OK) return rc;
     CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
     const int64_t col_bytes = (k / 32) * kQ8Bytes;
+    if (use_mfma(kFmtQ4K, n)) {
+        const size_t need = (size_t)gemv_q4k_mfma_partial_bytes(m, k, n);
+        CHECK_SHAPE(need <= kScratchBytes, "m=%lld, k=%lld, n=%d need %zu bytes of split-k partials; the fixed "
+                    "scratch of the no-allocation entry point holds %zu", (long long)m, (long long)k, n, need,
+                    kScratchBytes);
+        void* part = nullptr;
+        if (need > 0 && (rc = scratch_address(&part)) != MQ_OK) return rc;
+        return hip_status(launch_gemv_q4k_mfma(w, xq, col_bytes, y, (double*)part, m, k, n, stream),
+                          "matrix-core GEMV launch");
+    }
     if (n * stage_bytes((int)(k / 32)) <= kMaxStageLds)       // one pass over k: no partials
         return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, nullptr, nullptr, m, k, n, stream, kFmtQ4K),
                           "4-bit GEMV launch");
@@ -559,6 +592,26 @@ int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int6
     void* part = nullptr;
     if ((rc = scratch_address(&part)) != MQ_OK) return rc;
     return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)part, m, k, n, stream, kFmtQ4K),
+                      "4-bit split-k GEMV launch");
+}
+
+int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n, int path,
+                                   hipStream_t stream) {
+    int rc = check_q4k(w, xq, y, m, k);
+    if (rc != MQ_OK) return rc;
+    CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
+    CHECK_ARG(path == 0 || path == 1, "path must be 0 (vector kernels) or 1 (matrix cores)");
+    CHECK_SHAPE(path == 0 || n >= 2, "the matrix-core path takes n >= 2");
+    const int64_t col_bytes = (k / 32) * kQ8Bytes;
+    if (path == 1) return run_q4k_mfma(w, xq, col_bytes, y, m, k, n, stream);
+    const int lds = n * stage_bytes((int)(k / 32));
+    if (lds <= kMaxStageLds)
+        return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, nullptr, nullptr, m, k, n, stream, kFmtQ4K),
+                          "4-bit GEMV launch");
+    void* ws = nullptr;
+    const size_t need = (size_t)gemv_q4k_splitk_nsplit(k) * (size_t)m * n * sizeof(double);
+    if ((rc = workspace(need, stream, &ws)) != MQ_OK) return rc;
+    return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)ws, m, k, n, stream, kFmtQ4K),
                       "4-bit split-k GEMV launch");
 }
 

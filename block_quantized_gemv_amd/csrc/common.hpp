@@ -12,6 +12,7 @@ constexpr int kQ8Bytes = 34;       // q8_0 block: 32 values
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- f16 ----
 // Hardware conversions: v_cvt_f32_f16 is exact; v_cvt_f16_f32 rounds to

@@ -1,0 +1,334 @@
+// Batched q4_K x q8_0 GEMV on the matrix cores: y[r][c] = sum_k W[r][k] *
+// X[c][k] for n <= 8 activation columns, the integer part of every
+// sub-block's dot product by v_mfma_i32_16x16x64_i8.
+//
+// One MFMA covers 16 weight rows and one 32-byte chunk t of a super-block's
+// quants: the low nibbles of those bytes are sub-block 2t, the high ones
+// sub-block 2t+1 (q4_K's layout).  Its A operand (16 "rows" i = 8h + c) is
+// the activation: row i holds column c's codes of sub-block 2t+h where the
+// weights hold that sub-block's nibbles and zeros where they hold the other
+// one; its B operand (16 columns j) is the 16 weight rows' nibbles.  So
+// C[8h + c][j] is the exact int32 sum of sub-block 2t+h of row j against
+// column c: both sub-blocks stay separate, as their scales differ, and all
+// 16 output columns are used at n = 8.  Lane group g = lane/16 of either
+// operand carries bytes 8g..8g+7 of the chunk (low nibbles first, then high
+// nibbles, as 16 int8): the instruction pairs A's and B's bytes position by
+// position, so any such split works if both operands use it.
+//
+// The output lane (g, j) holds C[4g + r][j], r = 0..3: weight row j and
+// columns c = 4(g & 1) + r of sub-block 2t + (g >> 1), and folds them into
+// f64 accumulators as acc += isum * (d*sc * d8), every product exact (d,
+// d8 are f16, sc six-bit, |isum| < 2^16), so each step rounds once.  The
+// mins' part, sum over sub-blocks s of (dmin*m_s) * (d8*ysum)_s, is itself
+// a product of a (column x sub-block) and a (sub-block x row) matrix: one
+// v_mfma_f64_16x16x4_f64 per four sub-blocks accumulates it for the tile
+// (products exact: 17 and 24 significant bits).  That instruction's output
+// lane (g, j) holds rows 4r + g; its A row i is given column 4((i % 4) & 1)
+// + i/4, so that the lane's four rows are the same four columns its own
+// accumulators hold (each column is computed twice, by lanes g and g + 2).
+// At the end of a row tile the two halves of a (row, column) pair, held by
+// lanes l and l ^ 32, are added and the mins' part subtracted.  The sums
+// are grouped differently from the vector kernels', so results agree with
+// them to rounding, not bit for bit.
+//
+// Staging (per workgroup, for its k range of nb blocks, np = nb/2 pairs):
+//   codes:  byte P*512 + g*128 + (8h + c)*8: codes 8g..8g+7 of block 2P+h of
+//           column c, so that the 64 lanes of an A operand read 512
+//           consecutive bytes;
+//   scales: byte np*512 + P*256 + h*64 + c*8: d8 of block 2P+h of column c
+//           (f64), and 128 bytes further d8*ysum.
+// Columns c >= n hold zero codes and scales (they add zero).
+//
+// A wave owns 16-row tiles (strided across the CUs) and streams their
+// super-blocks in k order, kMfmaDepth in flight; blockIdx.y splits k, each
+// split leaving f64 partials that k_splitk_finalize sums in split order.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaPairBytes = 768;         // codes 512 + scales 256 per block pair
+__host__ __device__ constexpr int mfma_stage_bytes(int sb_per_split) { return sb_per_split * 4 * kMfmaPairBytes; }
+constexpr int kMfmaMaxSbPerSplit = 16;      // 48 KiB of staging
+#ifndef MQ_MFMA_DEPTH
+#define MQ_MFMA_DEPTH 2
+#endif
+constexpr int kMfmaDepth = MQ_MFMA_DEPTH;   // items in flight per wave
+
+// Writes block b (relative) of column c into the staging layout above.
+__device__ __forceinline__ void stage_mfma_block(uint8_t* __restrict__ lds, int np, int c, int b, uint32_t dbits,
+                                                 const uint32_t (&q)[8], bool real) {
+    const int P = b >> 1, h = b & 1;
+    double d = 0.0, ds = 0.0;
+    if (real) {
+        int s = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = dot4(q[i], 0x01010101u, s);
+        d = (double)f16_to_f32(dbits);
+        ds = d * (double)s;
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        *(uint2*)(lds + P * 512 + g * 128 + (8 * h + c) * 8) =
+            real ? make_uint2(q[2 * g], q[2 * g + 1]) : make_uint2(0u, 0u);
+    uint8_t* scl = lds + np * 512 + P * 256 + h * 64 + c * 8;
+    *(double*)scl = d;
+    *(double*)(scl + 128) = ds;
+}
+
+// Stages blocks [b0, b0 + nb) of the n = NC columns (zeros for columns NC..7).
+// Each thread first requests up to R of its blocks, then writes them, so
+// that their loads are in flight together.
+template <int NC, int R>
+__device__ __forceinline__ void stage_mfma(const uint8_t* __restrict__ xq, int64_t col_stride, int b0, int nb,
+                                           uint8_t* __restrict__ lds) {
+    const int np = nb >> 1, T = blockDim.x, tid = threadIdx.x;
+    const int real = NC * nb;
+    for (int base = tid; base < real; base += R * T) {
+        uint32_t q[R][8], dbits[R];
+        int cc[R], bb[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            // the column varies fastest, so that neighbouring threads write
+            // neighbouring LDS words
+            const int f = base + r * T;
+            const bool in = f < real;
+            const int b = in ? f / NC : 0;
+            bb[r] = b;
+            cc[r] = in ? f - b * NC : 0;
+            dbits[r] = load_q8_block(xq + cc[r] * col_stride + (int64_t)(b0 + b) * kQ8Bytes, q[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (base + r * T < real) stage_mfma_block(lds, np, cc[r], bb[r], dbits[r], q[r], true);
+    }
+    if (NC < 8) {
+        const uint32_t z[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        for (int f = tid; f < (8 - NC) * nb; f += T) {
+            const int b = f / (8 - NC);
+            stage_mfma_block(lds, np, NC + (f - b * (8 - NC)), b, 0u, z, false);
+        }
+    }
+}
+
+// Six-bit scale and min of sub-block s = 2t + h of a q4_K header (bytes
+// 4..15 are the packed scales s[0..11], in hdr.y, hdr.z, hdr.w): s < 4
+// (t < 2) keeps them in the low six bits of s[s] and s[s+4]; s >= 4 takes
+// the nibbles of s[s+4] and the top two bits of s[s-4] (scale) and s[s]
+// (min).  t is a compile-time chunk index, h = 0 or 1.
+__device__ __forceinline__ void scale_min_of(const u32x4& hdr, int t, int h, uint32_t& sc, uint32_t& m) {
+    if (t < 2) {
+        const int sh = 16 * t + 8 * h;
+        sc = (hdr.y >> sh) & 63u;
+        m = (hdr.z >> sh) & 63u;
+    } else {
+        const int u = 16 * (t - 2) + 8 * h;
+        const uint32_t lo = hdr.w >> u;
+        sc = (lo & 15u) | (((hdr.y >> u) >> 2) & 48u);
+        m = ((lo >> 4) & 15u) | (((hdr.z >> u) >> 2) & 48u);
+    }
+}
+
+// Items 0..n-1 through a ring of D register buffers: items 0..D-1 are
+// fetched by the caller, then item i is used and item i + D fetched into
+// its buffer, so that D items' loads are in flight while one computes.
+// The fetches of full rounds are unconditional (past the end they re-read
+// the last item, which the fetch must allow) so that the compiler can wait
+// for exactly the buffer about to be used; the last, partial round only
+// uses.
+template <int D, class Buf, class Fetch, class Use>
+__device__ __forceinline__ void stream_ring(int n, Buf (&buf)[D], Fetch&& fetch, Use&& use) {
+    int i = 0;
+    for (; i + D <= n; i += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            use(buf[u]);
+            fetch(i + u + D, buf[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        if (i + u < n) use(buf[u]);
+}
+
+// One workgroup per CU and k split (so that every CU gets the same share):
+// wave w of workgroup b owns row tiles b + GX*w, b + GX*(w + W), ... (GX
+// workgroups per split, W waves each) and walks their super-blocks in k
+// order with a cursor, kMfmaDepth items in flight.
+template <int NC, int D>
+__global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq,
+                                                        int64_t xq_col_bytes, float* __restrict__ y,
+                                                        double* __restrict__ part, int M, int nsb, int sb_per_split,
+                                                        int n_tiles) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int sb0 = (int)blockIdx.y * sb_per_split;
+    const int nsb_s = min(sb_per_split, nsb - sb0);
+    const int nb = 8 * nsb_s, np = nb >> 1;
+    const int lane = threadIdx.x & 63, g = lane >> 4, i16 = lane & 15;
+    const int GX = (int)gridDim.x, WPG = (int)(blockDim.x >> 6);
+    const int t0 = (int)blockIdx.x + GX * wave_id();            // the wave's first tile
+    const int stride = GX * WPG;
+    const int my_tiles = t0 < n_tiles ? (n_tiles - 1 - t0) / stride + 1 : 0;
+    const int n_items = my_tiles * nsb_s;
+    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+
+    // Items are (tile, super-block) in that order, walked by a cursor that
+    // stays on the last item past the end (its lines are re-read, nothing is
+    // computed from them).  Rows past M read row M-1 and are not stored.
+    struct Item {
+        u32x4 hdr;
+        uint2 q[4];
+        int tile, sbl;
+    };
+    int c_tile = t0, c_sb = 0, c_done = 0;
+    auto fetch = [&](int, Item& it) {
+        it.tile = c_tile;
+        it.sbl = c_sb;
+        if (c_done < n_items && ++c_done < n_items && ++c_sb == nsb_s) {
+            c_sb = 0;
+            c_tile += stride;
+        }
+        const int row0 = it.tile * 16 + i16;
+        const int row = row0 < M ? row0 : M - 1;
+        const uint8_t* p = w + (int64_t)row * row_bytes + (int64_t)(sb0 + it.sbl) * kQ4KBytes;
+        it.hdr = *(const u32x4*)p;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) it.q[t] = *(const uint2*)(p + 16 + 32 * t + 8 * g);
+    };
+
+    Item ring[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) fetch(u, ring[u]);
+    stage_mfma<NC, 2>(xq, xq_col_bytes, 8 * sb0, nb, lds);
+    __syncthreads();
+
+    const int h = g >> 1, cb = 4 * (g & 1);
+    const uint8_t* xa = lds + g * 128 + i16 * 8;                    // this lane's A bytes, pair 0
+    const uint8_t* xd = lds + np * 512 + h * 64 + cb * 8;            // its four columns' d8, pair 0
+    // the mins' operand: column 4((i % 4) & 1) + i/4 of row i = i16, sub-blocks
+    // g (pair g/2, half g%2) and 4 + g (two pairs further)
+    const uint8_t* xm = lds + np * 512 + 128 + (g >> 1) * 256 + (g & 1) * 64 + (4 * ((i16 & 3) & 1) + (i16 >> 2)) * 8;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    v4d mins = {0.0, 0.0, 0.0, 0.0};
+    stream_ring<D>(n_items, ring, fetch, [&](const Item& it) {
+        const int P0 = 4 * it.sbl;
+        v4i C[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint2 q = it.q[t];
+            const uint64_t hq = ((((uint64_t)q.y) << 32) | q.x) >> 4;
+            const v4i wb = {(int)(q.x & 0x0F0F0F0Fu), (int)(q.y & 0x0F0F0F0Fu), (int)((uint32_t)hq & 0x0F0F0F0Fu),
+                            (int)((uint32_t)(hq >> 32) & 0x0F0F0F0Fu)};
+            const uint2 x = *(const uint2*)(xa + (P0 + t) * 512);
+            const v4i xv = i16 < 8 ? v4i{(int)x.x, (int)x.y, 0, 0} : v4i{0, 0, (int)x.x, (int)x.y};
+            C[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
+        // mins: row j = i16's (dmin * m_s) against (d8 * ysum)_s, s = g and 4 + g
+        const double dmin = (double)f16_to_f32(it.hdr.x >> 16);
+        {
+            const uint32_t z = it.hdr.z >> (8 * g);
+            const uint32_t m_lo = z & 63u;
+            const uint32_t m_hi = ((it.hdr.w >> (8 * g)) >> 4 & 15u) | ((z >> 2) & 48u);
+            const uint8_t* mp = xm + P0 * 256;
+            mins = __builtin_amdgcn_mfma_f64_16x16x4f64(*(const double*)mp, dmin * (double)m_lo, mins, 0, 0, 0);
+            mins = __builtin_amdgcn_mfma_f64_16x16x4f64(*(const double*)(mp + 512), dmin * (double)m_hi, mins, 0, 0, 0);
+        }
+        const double d = (double)f16_to_f32(it.hdr.x);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t sc, m;
+            scale_min_of(it.hdr, t, h, sc, m);
+            (void)m;
+            const double a1 = d * (double)sc;
+            const f64x2 d01 = *(const f64x2*)(xd + (P0 + t) * 256);
+            const f64x2 d23 = *(const f64x2*)(xd + (P0 + t) * 256 + 16);
+            acc[0] = fma((double)C[t][0], a1 * d01.x, acc[0]);
+            acc[1] = fma((double)C[t][1], a1 * d01.y, acc[1]);
+            acc[2] = fma((double)C[t][2], a1 * d23.x, acc[2]);
+            acc[3] = fma((double)C[t][3], a1 * d23.y, acc[3]);
+        }
+        if (it.sbl != nsb_s - 1) return;
+        // tile done: the two sub-block parities (lanes l and l ^ 32) added and
+        // the mins' part subtracted; lanes g < 2 hold (row i16, columns cb..cb+3)
+        const int row = it.tile * 16 + i16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const double tot = (acc[r] + __shfl_xor(acc[r], 32, 64)) - mins[r];
+            acc[r] = 0.0;
+            const int c = cb + r;
+            if (g < 2 && c < NC && row < M) {
+                if (part) part[((int64_t)blockIdx.y * M + row) * NC + c] = tot;
+                else y[(int64_t)row * NC + c] = (float)tot;
+            }
+        }
+        mins = v4d{0.0, 0.0, 0.0, 0.0};
+    });
+}
+
+}  // namespace
+
+// The split of k for m rows of nsb super-blocks: enough (tile, split) units
+// for the GPU's waves, at most kMfmaMaxSbPerSplit super-blocks staged per
+// workgroup; then about one workgroup per CU, split evenly among the k
+// ranges, each with the waves its tiles need (at most 16; past that waves
+// take several tiles).
+MfmaPlan plan_gemv_q4k_mfma(int64_t m, int nsb) {
+    MfmaPlan p;
+    const int64_t tiles = (m + 15) / 16;
+    const int64_t cus = device_cu_count();
+    const int64_t target = cus * 8;
+    int64_t ns = (nsb + kMfmaMaxSbPerSplit - 1) / kMfmaMaxSbPerSplit;
+    const int64_t want = (target + tiles - 1) / tiles;
+    if (want > ns) ns = want < nsb ? want : nsb;
+    p.sb_per_split = (int)((nsb + ns - 1) / ns);
+    p.n_split = (nsb + p.sb_per_split - 1) / p.sb_per_split;
+    p.n_tiles = (int)tiles;
+    p.lds = mfma_stage_bytes(p.sb_per_split);
+    int64_t gx = cus / p.n_split;
+    if (gx < 1) gx = 1;
+    if (gx > tiles) gx = tiles;
+    int64_t wpg = (tiles + gx - 1) / gx;
+    if (wpg > 16) wpg = 16;
+    p.grid_x = (int)gx;
+    p.threads = (int)(64 * wpg);
+    return p;
+}
+
+template <int NC>
+static hipError_t launch_mfma_nc(const void* w, const void* xq, int64_t xq_col_bytes, float* y, double* part,
+                                 int64_t m, int nsb, hipStream_t stream) {
+    const MfmaPlan p = plan_gemv_q4k_mfma(m, nsb);
+    if (p.n_split > 1 && !part) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemv_q4k_mfma<NC, kMfmaDepth>), dim3((unsigned)p.grid_x, (unsigned)p.n_split),
+                       dim3((unsigned)p.threads), p.lds, stream, (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes,
+                       y, p.n_split > 1 ? part : nullptr, (int)m, nsb, p.sb_per_split, p.n_tiles);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_split == 1) return e;
+    return launch_splitk_finalize(part, y, m * NC, p.n_split, stream);
+}
+
+int64_t gemv_q4k_mfma_partial_bytes(int64_t m, int64_t k, int ncols) {
+    const MfmaPlan p = plan_gemv_q4k_mfma(m, (int)(k / 256));
+    return p.n_split > 1 ? (int64_t)p.n_split * m * ncols * (int64_t)sizeof(double) : 0;
+}
+
+hipError_t launch_gemv_q4k_mfma(const void* w, const void* xq, int64_t xq_col_bytes, float* y, double* part,
+                                int64_t m, int64_t k, int ncols, hipStream_t stream) {
+    const int nsb = (int)(k / 256);
+    switch (ncols) {
+        case 2: return launch_mfma_nc<2>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 3: return launch_mfma_nc<3>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 4: return launch_mfma_nc<4>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 5: return launch_mfma_nc<5>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 6: return launch_mfma_nc<6>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 7: return launch_mfma_nc<7>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        case 8: return launch_mfma_nc<8>(w, xq, xq_col_bytes, y, part, m, nsb, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mq

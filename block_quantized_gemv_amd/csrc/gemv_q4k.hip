@@ -1248,9 +1248,12 @@ static hipError_t launch_split_nc(const void* w, const void* xq, int64_t xq_col_
                        (const uint8_t*)w, (const uint8_t*)xq, xq_col_bytes, part, (int)m, nsb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = m * NC;
-    hipLaunchKernelGGL(k_splitk_finalize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       (const double*)part, y, n, n_split);
+    return launch_splitk_finalize(part, y, m * NC, n_split, stream);
+}
+
+hipError_t launch_splitk_finalize(const double* part, float* y, int64_t n, int n_split, hipStream_t stream) {
+    hipLaunchKernelGGL(k_splitk_finalize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part, y, n,
+                       n_split);
     return hipGetLastError();
 }
 

@@ -137,6 +137,21 @@ hipError_t launch_set_i64(int64_t* p, int64_t v, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 // XOR of the 32-bit words of bytes (multiple of 16) at p (16-byte aligned)
 // into *xor_out; workgroups <= 0 means one per CU.
+// y[i] = sum over s < n_split of part[s*n + i], in that order, as f32.
+hipError_t launch_splitk_finalize(const double* part, float* y, int64_t n, int n_split, hipStream_t stream);
+
+// Batched q4_K x q8_0 GEMV on the matrix cores (gemv_mfma.hip), 2 <= ncols
+// <= 8, k % 256 == 0.  k is split over n_split ranges of sb_per_split
+// super-blocks; with n_split > 1, part receives n_split*m*ncols f64
+// partials (gemv_q4k_mfma_partial_bytes; 0 when k is not split).
+struct MfmaPlan {
+    int n_split, sb_per_split, n_tiles, lds, grid_x, threads;
+};
+MfmaPlan plan_gemv_q4k_mfma(int64_t m, int nsb);
+int64_t gemv_q4k_mfma_partial_bytes(int64_t m, int64_t k, int ncols);
+hipError_t launch_gemv_q4k_mfma(const void* w, const void* xq, int64_t xq_col_bytes, float* y, double* part,
+                                int64_t m, int64_t k, int ncols, hipStream_t stream);
+
 // Synchronization probes (sync_probe.hip); 0 = measured, 1 = the grid
 // cannot be co-resident, 2 = a HIP call failed.
 int grid_barrier_probe(int hierarchical, int words, int rounds, int threads, double* us_per_round,

@@ -127,6 +127,17 @@ int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, i
 int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int64_t m, int64_t k,
                                    int n, hipStream_t stream);
 
+/* Test and measurement hook (for comparing the two kernel families): the
+ * batched q4_K GEMV of mq_gemv_q4k_q8_batched, forced onto path 0 (the
+ * vector kernels: v_dot4 sums, one column per pass over the staged
+ * activation) or path 1 (the matrix cores, n >= 2: v_mfma_i32_16x16x64_i8
+ * sums of 16 rows x 8 columns x 2 sub-blocks).  The batched entry point
+ * itself takes path 1 for n >= 5.  Same arguments, errors and workspace as
+ * mq_gemv_q4k_q8_batched; MQ_ERR_ARG for another path, MQ_ERR_SHAPE for
+ * path 1 with n = 1. */
+int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n, int path,
+                                   hipStream_t stream);
+
 /* The split-k workspaces (see mq_gemv_q4k_q8_batched).  Host out-params
  * (any may be NULL): bytes held in total, the (device, stream) pairs that
  * have one, and the outgrown buffers still held. */

@@ -130,18 +130,65 @@ def test_gemv_q4k_full_size(mq, o, pool, name, m, k):
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_batched_small(mq, o, n):
+    """301 x 2560, n columns: the batched entry point (the matrix cores for
+    n >= 5) and the vector kernels (path 0), each column against the
+    oracle; the vector kernels' columns equal the n = 1 GEMV bit for bit."""
     synth = _synth()
     m, k = 301, 2560
     w = synth.q4k_matrix(3, (synth.KEY_MATRIX, n), m, k)
     x = synth.normal_f32(3, (synth.KEY_COLUMNS, n), (n, k))
     xq = o.quantize_q8_0(x).reshape(n, -1)
-    wd = to_dev(w)
-    y = to_host(mq.mq_gemv_q4k_q8_batched(wd, to_dev(xq.ravel()), m, k, n))
+    wd, xd = to_dev(w), to_dev(xq.ravel())
+    y = to_host(mq.mq_gemv_q4k_q8_batched(wd, xd, m, k, n))
+    yv = to_host(mq.mq_debug_gemv_q4k_batched_path(wd, xd, m, k, n, 0))
     for c in range(n):
         y_ref, s_abs = o.gemv_q4k(w, m, k, xq[c])
         check_tolerance(y[:, c], y_ref, s_abs, f"batched n={n} col {c}")
+        check_tolerance(yv[:, c], y_ref, s_abs, f"batched n={n} col {c}, vector kernels")
         y1 = to_host(mq.mq_gemv_q4k_q8(wd, to_dev(xq[c]), m, k))
-        assert np.array_equal(y1.view(np.uint32), y[:, c].copy().view(np.uint32)), f"col {c} differs from n = 1"
+        assert np.array_equal(y1.view(np.uint32), yv[:, c].copy().view(np.uint32)), f"col {c} differs from n = 1"
+        if n < 5:
+            assert np.array_equal(y1.view(np.uint32), y[:, c].copy().view(np.uint32))
+
+
+def _exact_friendly(rng, m, k, n):
+    """q4_K weights with d = 1 and dmin = 1/2 (random six-bit scales and
+    mins, random nibbles) and q8_0 columns with power-of-two scales 2^-2 ..
+    2^-6 (random codes in [-127, 127]): every weight d*sc*q - dmin*m and
+    activation d8*code is a short dyadic number and every partial sum of
+    their products stays below 2^36 in units of 2^-7, so any summation order
+    in f64 gives the exact dot product."""
+    nsb = k // 256
+    wb = rng.integers(0, 256, size=(m * nsb, 144), dtype=np.uint8)
+    wb[:, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    wb[:, 2:4] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
+    nb = k // 32
+    xb = np.empty((n * nb, 34), np.uint8)
+    d = np.float16(2.0) ** -rng.integers(2, 7, size=n * nb)
+    xb[:, 0:2] = d.astype(np.float16).view(np.uint8).reshape(-1, 2)
+    xb[:, 2:] = rng.integers(-127, 128, size=(n * nb, 32)).astype(np.int8).view(np.uint8)
+    return wb.ravel(), xb.reshape(n, -1)
+
+
+MFMA_SMALL = [(1, 256, 2), (15, 512, 8), (17, 768, 3), (16, 256 * 40, 8), (301, 2560, 8), (64, 18944, 5),
+              (1000, 4864, 8), (33, 256 * 33, 4), (2049, 1024, 6), (200, 4096, 7)]
+
+
+@pytest.mark.parametrize("m,k,n", MFMA_SMALL)
+def test_batched_matrix_cores_exact(mq, o, m, k, n):
+    """The matrix-core path on inputs whose dot products f64 forms exactly
+    in any order (_exact_friendly): every output equals the oracle's bit
+    for bit, so any error in the integer sums, the scale and min decoding,
+    the sub-block split or the k splits would show.  Shapes: ragged row
+    tiles, one super-block, k split into several ranges (and not evenly)."""
+    rng = np.random.default_rng(1000 + m + k + n)
+    w, xq = _exact_friendly(rng, m, k, n)
+    y = to_host(mq.mq_debug_gemv_q4k_batched_path(to_dev(w), to_dev(xq.ravel()), m, k, n, 1))
+    for c in range(n):
+        y_ref, _ = o.gemv_q4k(w, m, k, xq[c])
+        bad = y[:, c].copy().view(np.uint32) != y_ref.view(np.uint32)
+        assert not bad.any(), (f"{m}x{k} n={n} col {c}: {bad.sum()} rows differ, first {np.argmax(bad)}: "
+                               f"{y[bad, c][:3]} vs {y_ref[bad][:3]}")
 
 
 BATCH_SHAPES = [("qkv", 4608, 3584), ("o", 3584, 3584), ("gate/up", 37888, 3584), ("down", 3584, 18944)]
@@ -157,9 +204,10 @@ def _single_pass(m, k, n):
 @pytest.mark.parametrize("name,m,k", BATCH_SHAPES, ids=[s[0] for s in BATCH_SHAPES])
 def test_batched_full_size(mq, o, pool, name, m, k, n):
     """7B-class shapes, n columns, every row of every column against the
-    oracle; each column also against the n = 1 kernel, bit for bit where
-    both take one pass over K (the same per-row order), within the gate
-    where the batched call splits K."""
+    oracle, through the batched entry point (the matrix cores) and through
+    the vector kernels; the vector kernels' columns also against the n = 1
+    kernel, bit for bit where both take one pass over K (the same per-row
+    order), within the gate where they split K."""
     synth = _synth()
     from block_quantized_gemv_amd import workloads
     seed = workloads.BATCHED.seed
@@ -171,12 +219,14 @@ def test_batched_full_size(mq, o, pool, name, m, k, n):
     assert np.array_equal(to_host(xq_dev), xq.ravel())
     wd = to_dev(w)
     y = to_host(mq.mq_gemv_q4k_q8_batched(wd, xq_dev, m, k, n))
+    yv = to_host(mq.mq_debug_gemv_q4k_batched_path(wd, xq_dev, m, k, n, 0))
     for c in range(n):
         y_ref, s_abs = oracle_gemv_parallel(o.gemv_q4k, w, m, k, xq[c], pool=pool)
         check_tolerance(y[:, c], y_ref, s_abs, f"{name} n={n} col {c}")
+        check_tolerance(yv[:, c], y_ref, s_abs, f"{name} n={n} col {c}, vector kernels")
         y1 = to_host(mq.mq_gemv_q4k_q8(wd, xq_dev[c * xq.shape[1]:(c + 1) * xq.shape[1]], m, k))
-        same = float(np.mean(y1.view(np.uint32) == y[:, c].copy().view(np.uint32)))
-        log(f"    col {c}: bit-identical to the n=1 kernel on {same:.4f} of rows")
+        same = float(np.mean(y1.view(np.uint32) == yv[:, c].copy().view(np.uint32)))
+        log(f"    col {c}: vector kernels bit-identical to the n=1 kernel on {same:.4f} of rows")
         if _single_pass(m, k, n):
             assert same == 1.0, f"{name} n={n} col {c}: batched column differs from the n = 1 kernel"
 
