@@ -97,10 +97,16 @@ int mq_gemv_q4k_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k
  * Batched q4_K x q8_0 GEMV, 1 <= n <= 8 activation columns, weights streamed
  * once for all columns.  xq: [n][k/32] q8_0 blocks (column c at
  * xq + c*(k/32)*34); y: f32 [m][n] row-major, y[r*n + c].
- * Same arithmetic per column as mq_gemv_q4k_q8.  For large n*k (the
- * columns do not fit in 64 KB of LDS) the kernel splits k across
- * workgroups and sums the f64 partials in a second pass in split order;
- * the partials (ceil(k/4096)*m*n doubles) live in a device workspace that
+ * Same arithmetic per column as mq_gemv_q4k_q8 for n <= 4 (v_dot4 kernels);
+ * for n >= 5 the integer sums come from the matrix cores and the f64 fixup
+ * adds the same exact products in another order (results within the same
+ * tolerance).  When the kernel splits k across workgroups (n <= 4: the
+ * columns do not fit in 64 KB of LDS; n >= 5: rows of more than 16
+ * super-blocks, or too few row tiles to fill the GPU) it sums the f64
+ * partials in a second pass in split order;
+ * the partials (n <= 4: ceil(k/4096)*m*n doubles; n >= 5: n_split*m*n
+ * doubles, n_split <= k/256, e.g. 10 splits for the 3584 x 18944 matrix)
+ * live in a device workspace that
  * the library keeps per (device, stream) and grows on demand to the next
  * power of two (MQ_ERR_NOMEM if that allocation fails; MQ_ERR_CAPTURE if it
  * must grow while `stream` is being captured: call once outside capture
@@ -114,10 +120,11 @@ int mq_gemv_q4k_q8_batched(const void* w, const void* xq, float* y, int64_t m, i
 /* The batched GEMV for callers that cannot allocate device memory (code
  * under graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): same arguments, kernels and results as
- * mq_gemv_q4k_q8_batched, but it never allocates.  When the columns do not
- * fit in LDS its split-k partials go to a fixed 4 MiB device array of the
- * library instead of a workspace: ceil(k/4096)*m*n doubles must fit (for
- * example the 3584 x 18944 matrix at n = 8 takes 1.1 MiB), else
+ * mq_gemv_q4k_q8_batched, but it never allocates.  When the kernel splits k
+ * its partials go to a fixed 4 MiB device array of the library instead of a
+ * workspace: the partials described there must fit (for
+ * example the 3584 x 18944 matrix takes 0.55 MiB at n = 4 and 2.2 MiB at
+ * n = 8), else
  * MQ_ERR_SHAPE, reported on the host before any HIP call.  Each GPU holds
  * its own copy of the array until the process ends, and every call on that
  * GPU uses it: two calls that overlap in time on one GPU (from different

@@ -25,8 +25,9 @@ def test_no_alloc_matches_the_allocating_entry_point(mq):
     from block_quantized_gemv_amd import synth
     o = oracle.Oracle()
     mq.mq_workspace_release()
-    # (m, k, n): the 7B down projection at n = 8 (five splits, 1.1 MiB of
-    # partials), a smaller split-k call after it, then a one-pass shape
+    # (m, k, n): the 7B down projection at n = 8 (the matrix cores, ten k
+    # ranges, 2.2 MiB of partials), a smaller split-k call of the vector
+    # kernels after it, then a one-pass shape
     cases = [(3584, 18944, 8), (515, 18944, 4), (301, 2560, 3)]
     outs = []
     for m, k, n in cases:
