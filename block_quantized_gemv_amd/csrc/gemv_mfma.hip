@@ -2,39 +2,41 @@
 // X[c][k] for n <= 8 activation columns, the integer part of every
 // sub-block's dot product by v_mfma_i32_16x16x64_i8.
 //
-// One MFMA covers 16 weight rows and one 32-byte chunk t of a super-block's
-// quants: the low nibbles of those bytes are sub-block 2t, the high ones
-// sub-block 2t+1 (q4_K's layout).  Its A operand (16 "rows" i = 8h + c) is
-// the activation: row i holds column c's codes of sub-block 2t+h where the
-// weights hold that sub-block's nibbles and zeros where they hold the other
-// one; its B operand (16 columns j) is the 16 weight rows' nibbles.  So
-// C[8h + c][j] is the exact int32 sum of sub-block 2t+h of row j against
-// column c: both sub-blocks stay separate, as their scales differ, and all
-// 16 output columns are used at n = 8.  Lane group g = lane/16 of either
-// operand carries bytes 8g..8g+7 of the chunk (low nibbles first, then high
-// nibbles, as 16 int8): the instruction pairs A's and B's bytes position by
-// position, so any such split works if both operands use it.
+// A lane group g = lane/16 of the weight operand loads 16 bytes per row:
+// bytes 16g..16g+15 of the 64 bytes that hold chunks 2u and 2u+1 of a
+// super-block's quants (u = 0, 1; a chunk is 32 bytes, its low nibbles are
+// sub-block 2*chunk and its high nibbles sub-block 2*chunk+1, q4_K's
+// layout), so that each load instruction moves 1 KB.  One MFMA (u, e) takes
+// the e-nibbles (e = 0 low, 1 high) of those 16 bytes as its B operand (16
+// columns j = the weight rows): lane groups 0 and 1 then hold sub-block
+// 4u + e, groups 2 and 3 sub-block 4u + 2 + e.  Its A operand has 16 rows
+// i = 8h + c: row i holds column c's codes of sub-block 4u + 2h + e in the
+// lane groups that hold that sub-block's nibbles (g >> 1 == h) and zeros in
+// the others.  So C[8h + c][j] is the exact int32 sum of sub-block
+// 4u + 2h + e of row j against column c: the sub-blocks stay separate, as
+// their scales differ, and all 16 output rows are used at n = 8.  The
+// instruction pairs A's and B's bytes position by position within a lane
+// group, so any split of k over the groups works if both operands use it.
 //
 // The output lane (g, j) holds C[4g + r][j], r = 0..3: weight row j and
-// columns c = 4(g & 1) + r of sub-block 2t + (g >> 1), and folds them into
-// f64 accumulators as acc += isum * (d*sc * d8), every product exact (d,
-// d8 are f16, sc six-bit, |isum| < 2^16), so each step rounds once.  The
-// mins' part, sum over sub-blocks s of (dmin*m_s) * (d8*ysum)_s, is itself
-// a product of a (column x sub-block) and a (sub-block x row) matrix: one
-// v_mfma_f64_16x16x4_f64 per four sub-blocks accumulates it for the tile
-// (products exact: 17 and 24 significant bits).  That instruction's output
-// lane (g, j) holds rows 4r + g; its A row i is given column 4((i % 4) & 1)
-// + i/4, so that the lane's four rows are the same four columns its own
-// accumulators hold (each column is computed twice, by lanes g and g + 2).
-// At the end of a row tile the two halves of a (row, column) pair, held by
-// lanes l and l ^ 32, are added and the mins' part subtracted.  The sums
-// are grouped differently from the vector kernels', so results agree with
-// them to rounding, not bit for bit.
+// columns c = 4(g & 1) + r of sub-block 4u + 2(g >> 1) + e, and folds them
+// into f64 accumulators as acc += isum * (d*sc * d8), every product exact
+// (d, d8 are f16, sc six-bit, |isum| < 2^16), so each step rounds once.
+// The mins' part, sum over sub-blocks s of (dmin*m_s) * (d8*ysum)_s, is
+// itself a product of a (column x sub-block) and a (sub-block x row)
+// matrix: one v_mfma_f64_16x16x4_f64 per four sub-blocks accumulates it for
+// the tile (products exact: 17 and 24 significant bits).  That
+// instruction's output lane (g, j) holds rows 4r + g; its A row i is given
+// column 4((i % 4) & 1) + i/4, so that the lane's four rows are the same
+// four columns its own accumulators hold (each column is computed twice,
+// by lanes g and g + 2).  At the end of a row tile the two halves of a
+// (row, column) pair, held by lanes l and l ^ 32, are added and the mins'
+// part subtracted.  The sums are grouped differently from the vector
+// kernels', so results agree with them to rounding, not bit for bit.
 //
 // Staging (per workgroup, for its k range of nb blocks, np = nb/2 pairs):
-//   codes:  byte P*512 + g*128 + (8h + c)*8: codes 8g..8g+7 of block 2P+h of
-//           column c, so that the 64 lanes of an A operand read 512
-//           consecutive bytes;
+//   codes:  byte b*256 + c*32: the 32 codes of block b of column c, so that
+//           an A operand's live lanes read 256 consecutive bytes per half;
 //   scales: byte np*512 + P*256 + h*64 + c*8: d8 of block 2P+h of column c
 //           (f64), and 128 bytes further d8*ysum.
 // Columns c >= n hold zero codes and scales (they add zero).
@@ -71,10 +73,9 @@ __device__ __forceinline__ void stage_mfma_block(uint8_t* __restrict__ lds, int 
         d = (double)f16_to_f32(dbits);
         ds = d * (double)s;
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-        *(uint2*)(lds + P * 512 + g * 128 + (8 * h + c) * 8) =
-            real ? make_uint2(q[2 * g], q[2 * g + 1]) : make_uint2(0u, 0u);
+    uint8_t* cp = lds + b * 256 + c * 32;
+    *(u32x4*)cp = real ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(cp + 16) = real ? u32x4{q[4], q[5], q[6], q[7]} : u32x4{0u, 0u, 0u, 0u};
     uint8_t* scl = lds + np * 512 + P * 256 + h * 64 + c * 8;
     *(double*)scl = d;
     *(double*)(scl + 128) = ds;
@@ -115,21 +116,21 @@ __device__ __forceinline__ void stage_mfma(const uint8_t* __restrict__ xq, int64
     }
 }
 
-// Six-bit scale and min of sub-block s = 2t + h of a q4_K header (bytes
-// 4..15 are the packed scales s[0..11], in hdr.y, hdr.z, hdr.w): s < 4
-// (t < 2) keeps them in the low six bits of s[s] and s[s+4]; s >= 4 takes
-// the nibbles of s[s+4] and the top two bits of s[s-4] (scale) and s[s]
-// (min).  t is a compile-time chunk index, h = 0 or 1.
-__device__ __forceinline__ void scale_min_of(const u32x4& hdr, int t, int h, uint32_t& sc, uint32_t& m) {
-    if (t < 2) {
-        const int sh = 16 * t + 8 * h;
+// Six-bit scale and min of sub-block s = 4*HI + j (j = 0..3) of a q4_K
+// header (bytes 4..15 are the packed scales s[0..11], in hdr.y, hdr.z,
+// hdr.w): s < 4 keeps them in the low six bits of s[s] and s[s+4]; s >= 4
+// takes the nibbles of s[s+4] and the top two bits of s[s-4] (scale) and
+// s[s] (min).  HI is compile-time; j may differ between lanes.
+template <int HI>
+__device__ __forceinline__ void scale_min_of(const u32x4& hdr, int j, uint32_t& sc, uint32_t& m) {
+    const int sh = 8 * j;
+    if constexpr (HI == 0) {
         sc = (hdr.y >> sh) & 63u;
         m = (hdr.z >> sh) & 63u;
     } else {
-        const int u = 16 * (t - 2) + 8 * h;
-        const uint32_t lo = hdr.w >> u;
-        sc = (lo & 15u) | (((hdr.y >> u) >> 2) & 48u);
-        m = ((lo >> 4) & 15u) | (((hdr.z >> u) >> 2) & 48u);
+        const uint32_t lo = hdr.w >> sh;
+        sc = (lo & 15u) | (((hdr.y >> sh) >> 2) & 48u);
+        m = ((lo >> 4) & 15u) | (((hdr.z >> sh) >> 2) & 48u);
     }
 }
 
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
     // computed from them).  Rows past M read row M-1 and are not stored.
     struct Item {
         u32x4 hdr;
-        uint2 q[4];
+        u32x4 q[2];     // bytes 16g..16g+15 of chunks 2u, 2u+1 (64 bytes from 16 + 64u)
         int tile, sbl;
     };
     int c_tile = t0, c_sb = 0, c_done = 0;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
         const uint8_t* p = w + (int64_t)row * row_bytes + (int64_t)(sb0 + it.sbl) * kQ4KBytes;
         it.hdr = *(const u32x4*)p;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) it.q[t] = *(const uint2*)(p + 16 + 32 * t + 8 * g);
+        for (int u = 0; u < 2; ++u) it.q[u] = *(const u32x4*)(p + 16 + 64 * u + 16 * g);
     };
 
     Item ring[D];
@@ -207,8 +208,12 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
     __syncthreads();
 
     const int h = g >> 1, cb = 4 * (g & 1);
-    const uint8_t* xa = lds + g * 128 + i16 * 8;                    // this lane's A bytes, pair 0
-    const uint8_t* xd = lds + np * 512 + h * 64 + cb * 8;            // its four columns' d8, pair 0
+    // A operand: row i16 = 8*ha + c takes, in lane group g, codes 16(g&1)..16(g&1)+15 of
+    // block 4u + 2ha + e (of the item's super-block) of column c when g >> 1 == ha, else zeros
+    const int ha = i16 >> 3;
+    const bool a_live = (g >> 1) == ha;
+    const uint8_t* xa = lds + (2 * ha) * 256 + (i16 & 7) * 32 + 16 * (g & 1);
+    const uint8_t* xd = lds + np * 512 + h * 256 + cb * 8;           // its four columns' d8 (pair 2u + h, half e)
     // the mins' operand: column 4((i % 4) & 1) + i/4 of row i = i16, sub-blocks
     // g (pair g/2, half g%2) and 4 + g (two pairs further)
     const uint8_t* xm = lds + np * 512 + 128 + (g >> 1) * 256 + (g & 1) * 64 + (4 * ((i16 & 3) & 1) + (i16 >> 2)) * 8;
@@ -216,16 +221,20 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
     v4d mins = {0.0, 0.0, 0.0, 0.0};
     stream_ring<D>(n_items, ring, fetch, [&](const Item& it) {
         const int P0 = 4 * it.sbl;
+        // C[2u + e]: sub-block 4u + 2h + e of this lane's rows (h = g >> 1)
         v4i C[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint2 q = it.q[t];
-            const uint64_t hq = ((((uint64_t)q.y) << 32) | q.x) >> 4;
-            const v4i wb = {(int)(q.x & 0x0F0F0F0Fu), (int)(q.y & 0x0F0F0F0Fu), (int)((uint32_t)hq & 0x0F0F0F0Fu),
-                            (int)((uint32_t)(hq >> 32) & 0x0F0F0F0Fu)};
-            const uint2 x = *(const uint2*)(xa + (P0 + t) * 512);
-            const v4i xv = i16 < 8 ? v4i{(int)x.x, (int)x.y, 0, 0} : v4i{0, 0, (int)x.x, (int)x.y};
-            C[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+            const u32x4 q = it.q[u];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t sh = 4 * e;
+                const v4i wb = {(int)((q.x >> sh) & 0x0F0F0F0Fu), (int)((q.y >> sh) & 0x0F0F0F0Fu),
+                                (int)((q.z >> sh) & 0x0F0F0F0Fu), (int)((q.w >> sh) & 0x0F0F0F0Fu)};
+                const u32x4 x = *(const u32x4*)(xa + (2 * P0 + 4 * u + e) * 256);
+                const v4i xv = a_live ? v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w} : v4i{0, 0, 0, 0};
+                C[2 * u + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
+            }
         }
         // mins: row j = i16's (dmin * m_s) against (d8 * ysum)_s, s = g and 4 + g
         const double dmin = (double)f16_to_f32(it.hdr.x >> 16);
@@ -239,17 +248,23 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
         }
         const double d = (double)f16_to_f32(it.hdr.x);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            uint32_t sc, m;
-            scale_min_of(it.hdr, t, h, sc, m);
-            (void)m;
-            const double a1 = d * (double)sc;
-            const f64x2 d01 = *(const f64x2*)(xd + (P0 + t) * 256);
-            const f64x2 d23 = *(const f64x2*)(xd + (P0 + t) * 256 + 16);
-            acc[0] = fma((double)C[t][0], a1 * d01.x, acc[0]);
-            acc[1] = fma((double)C[t][1], a1 * d01.y, acc[1]);
-            acc[2] = fma((double)C[t][2], a1 * d23.x, acc[2]);
-            acc[3] = fma((double)C[t][3], a1 * d23.y, acc[3]);
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                uint32_t sc, m;
+                if (u == 0) scale_min_of<0>(it.hdr, 2 * h + e, sc, m);
+                else scale_min_of<1>(it.hdr, 2 * h + e, sc, m);
+                (void)m;
+                const double a1 = d * (double)sc;
+                const uint8_t* dp = xd + (P0 + 2 * u) * 256 + e * 64;
+                const f64x2 d01 = *(const f64x2*)dp;
+                const f64x2 d23 = *(const f64x2*)(dp + 16);
+                const v4i& Ct = C[2 * u + e];
+                acc[0] = fma((double)Ct[0], a1 * d01.x, acc[0]);
+                acc[1] = fma((double)Ct[1], a1 * d01.y, acc[1]);
+                acc[2] = fma((double)Ct[2], a1 * d23.x, acc[2]);
+                acc[3] = fma((double)Ct[3], a1 * d23.y, acc[3]);
+            }
         }
         if (it.sbl != nsb_s - 1) return;
         // tile done: the two sub-block parities (lanes l and l ^ 32) added and
