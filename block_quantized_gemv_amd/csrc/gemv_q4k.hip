@@ -1,13 +1,14 @@
 // q4_K x q8_0 GEMV kernels for gfx950.
 //
 // The decode-step matvec over block-quantized weights: the weight stream is
-// read once, in 16-byte non-temporal loads, while the q8_0 activation sits
-// in LDS.  Integer 4-way dot products (v_dot4_i32_i8) form the exact int32
-// sum of each 32-value sub-block, the f16 d/dmin fixup is applied in f64
-// and each row is reduced across its lanes with DPP/swizzle steps in a fixed
-// order.  This is the MMVQ "dp4a x q8_0" decode kernel of '07 · R3 —
-// Small-model per-token overhead' (§1) redesigned for wave64/CDNA4; that
-// page describes it only by name.
+// read once, in 16-byte loads, while the q8_0 activation sits in LDS.
+// Integer 4-way dot products (v_dot4_i32_i8) form the exact int32 sum of
+// each 32-value sub-block, the f16 d/dmin fixup is applied in f64 and each
+// row is reduced across its lanes with DPP/swizzle steps in a fixed order.
+// '07 · R3 — Small-model per-token overhead' (§1) credits this kind of
+// decode kernel (MMVQ: 4-way integer dot products against activations
+// re-quantized to q8_0) with a large q4_K decode gain but describes it only
+// by name; this is a wave64/CDNA4 design of it.
 //
 // Lane work: a super-block (144 B = 16 B header + 128 B nibbles) is shared
 // by 4 lanes; lane j takes nibble chunk j (32 bytes = sub-blocks 2j, 2j+1:

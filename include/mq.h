@@ -3,8 +3,8 @@
  *
  * The per-token decode-step GEMV over block-quantized weights: a q4_K weight
  * matrix times an activation requantized to q8_0, with integer 4-way dot
- * products (the MMVQ "dp4a x q8_0" decode kernel that gave q4_K +37% in
- * '07 · R3 — Small-model per-token overhead', §1), plus the fixed per-step
+ * products (the MMVQ decode kernel to which '07 · R3 — Small-model
+ * per-token overhead', §1, credits a 37% q4_K decode gain), plus the fixed per-step
  * cost around it: one graph per decode step, captured once and replayed
  * ('Part 4 · Lecture 08 — Graph-Resident Decode', §1-§4).
  *

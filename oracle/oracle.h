@@ -25,9 +25,10 @@
  *     16+i in its high nibble; weight = d*(q - 8).  Rows hold k/32 blocks.
  *     The pages measure a 0.5B model in this format ('07 · R3', §5) without
  *     laying it out; this is the plain reading of the name.
- * The pages name both formats (the MMVQ "dp4a x q8_0" decode kernel that
- * gave q4_K +37%, '07 · R3 — Small-model per-token overhead', §1) but do
- * not lay them out; the layout above is the synthetic workload's.
+ * The pages name both formats ('07 · R3 — Small-model per-token overhead',
+ * §1, credits a 37% q4_K decode gain to an MMVQ kernel that dots q4_K
+ * weights against q8_0 activations with 4-way integer products) but do not
+ * lay them out; the layout above is the synthetic workload's.
  *
  * Parity pins: see tests/oracle_pins.py.  Every function here is pinned by
  * at least one check that does not re-run its own formula.
