@@ -154,10 +154,11 @@ def test_batched_small(mq, o, n):
 def _exact_friendly(rng, m, k, n):
     """q4_K weights with d = 1 and dmin = 1/2 (random six-bit scales and
     mins, random nibbles) and q8_0 columns with power-of-two scales 2^-2 ..
-    2^-6 (random codes in [-127, 127]): every weight d*sc*q - dmin*m and
-    activation d8*code is a short dyadic number and every partial sum of
-    their products stays below 2^36 in units of 2^-7, so any summation order
-    in f64 gives the exact dot product."""
+    2^-6 (random codes in [-127, 127]): every weight d*sc*q - dmin*m is a
+    multiple of 1/2 below 2^10 and every activation d8*code a multiple of
+    2^-6 below 2^5, so every product is a multiple of 2^-7 below 2^15 and,
+    for k <= 65536, every partial sum stays below 2^38 units of 2^-7: any
+    summation order in f64 gives the exact dot product."""
     nsb = k // 256
     wb = rng.integers(0, 256, size=(m * nsb, 144), dtype=np.uint8)
     wb[:, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
@@ -170,8 +171,10 @@ def _exact_friendly(rng, m, k, n):
     return wb.ravel(), xb.reshape(n, -1)
 
 
+# (m, k, n): ragged and single 16-row tiles, one super-block, uneven k ranges; (24, 65536, 8) plans one
+# super-block per k range (256 ranges), (1, 4096, 8) a single row at n = 8
 MFMA_SMALL = [(1, 256, 2), (15, 512, 8), (17, 768, 3), (16, 256 * 40, 8), (301, 2560, 8), (64, 18944, 5),
-              (1000, 4864, 8), (33, 256 * 33, 4), (2049, 1024, 6), (200, 4096, 7)]
+              (1000, 4864, 8), (33, 256 * 33, 4), (2049, 1024, 6), (200, 4096, 7), (24, 65536, 8), (1, 4096, 8)]
 
 
 @pytest.mark.parametrize("m,k,n", MFMA_SMALL)
