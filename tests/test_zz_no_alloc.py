@@ -50,3 +50,43 @@ def test_no_alloc_matches_the_allocating_entry_point(mq):
     with pytest.raises(mq.MQError) as e:
         mq.mq_gemv_q4k_q8_batched_noalloc(w, xq, big_m, 18944, 8, y)
     assert e.value.code == mq.MQ_ERR_SHAPE and "scratch" in str(e.value)
+
+
+def test_no_alloc_under_graph_capture(mq):
+    """The entry point inside a captured graph (the callers it exists for):
+    the graph is replayed four times, with eager GEMVs and synchronizations
+    between the replays, and every replay's output must equal the eager
+    output byte for byte.  Shapes: the matrix-core path with k split into
+    ranges (partials in the fixed array), and the vector kernels' split-k."""
+    import torch
+    import oracle
+    from block_quantized_gemv_amd import synth
+    o = oracle.Oracle()
+    for m, k, n in ((2049, 4096, 8), (515, 18944, 3)):
+        log(f"no-alloc batched under capture {m}x{k} n={n}")
+        w = to_dev(synth.q4k_matrix(17, (synth.KEY_MATRIX, m, k), m, k))
+        xq = to_dev(o.quantize_q8_0(synth.normal_f32(17, (synth.KEY_COLUMNS, n, k), (n, k))).ravel())
+        y_eager = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        mq.mq_gemv_q4k_q8_batched_noalloc(w, xq, m, k, n, y_eager)
+        want = to_host(y_eager).copy()
+        y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                mq.mq_gemv_q4k_q8_batched_noalloc(w, xq, m, k, n, y)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        other = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        for r in range(4):
+            y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            got = to_host(y).copy()
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{m}x{k} n={n}: replay {r} differs"
+            # eager work on the same fixed array between replays
+            mq.mq_gemv_q4k_q8_batched_noalloc(w, xq, m, k, n, other)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(other).view(np.uint32), want.view(np.uint32))
+        del g
