@@ -473,6 +473,36 @@ def test_gate_up_split_blocks_7b_width(mq, o, pool, fmt):
     _split_case(mq, o, pool, m, f"7B {fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["q4_K", "q4_0"])
+def test_span_stamps_7b_width(mq, fmt):
+    """The stamped kernels at 7B widths (two layers, vocabulary 8192), where
+    gate/up has split blocks, in both weight formats: over three graph
+    steps and an eager one, the stamped chain's logits and every traced
+    intermediate equal the plain chain's byte for byte, and every kernel's
+    stamp pair is filled and ordered."""
+    from block_quantized_gemv_amd import synth, workloads
+    m = dataclasses.replace(workloads.DECODE_7B, n_layers=2, vocab=8192)
+    if fmt == "q4_0":
+        m = dataclasses.replace(m, weight_format="q4_0")
+    W = model_weights(m, 2)
+    Wd = _dev_weights(W)
+    xd = to_dev(synth.normal_f32(m.seed, (synth.KEY_STEP_INPUTS,), (3, m.hidden)))
+    plain = mq.DecodeChain(m, Wd, xd, flags=mq.MQ_KEEP_INTERMEDIATES)
+    stamped = mq.DecodeChain(m, Wd, xd, flags=mq.MQ_KEEP_INTERMEDIATES | mq.MQ_SPAN_STAMPS)
+    n = 4 * m.n_layers + 1
+    for i, mode in enumerate((mq.MQ_GRAPH, mq.MQ_GRAPH, mq.MQ_EAGER, mq.MQ_GRAPH)):
+        a = to_host(plain.step(mode)).copy()
+        qa, fa = (to_host(t).copy() for t in plain.trace())
+        b = to_host(stamped.step(mode)).copy()
+        qb, fb = (to_host(t).copy() for t in stamped.trace())
+        assert _same(a, b) and _same(qa, qb) and _same(fa, fb), f"{fmt}: stamped step {i} differs"
+        st = stamped.read_stamps()
+        assert st.shape == (n, 2) and (st[:, 0] < st[:, 1]).all(), f"{fmt}: unfilled stamp pair at step {i}"
+        assert (st[1:, 0] >= st[:-1, 1] - 1).all(), f"{fmt}: kernels overlap at step {i}"
+    plain.close()
+    stamped.close()
+
+
 @pytest.mark.parametrize("inter", [8448, 16128])
 def test_gate_up_split_block_counts(mq, o, pool, inter):
     """Few and many split blocks: hidden 1280 (two passes over K), 264 and 504
