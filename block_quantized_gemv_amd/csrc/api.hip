@@ -249,8 +249,9 @@ __global__ void k_stamp_clear(uint64_t* __restrict__ p, int64_t n_pairs) {
     }
 }
 
-// Span stamps start as [max, 0] so that the kernels' atomic min / max
-// take their first values.
+// Every stamp pair starts as [max, 0], the mark of a slot that no wave has
+// written (a kernel's grid may use fewer slots than it has), so that the
+// host's min / max reduction in mq_chain_read_stamps skips it.
 int reset_stamps(mq_chain* c) {
     std::vector<uint64_t> init((size_t)c->n_stamped * kStampPairs * 2);
     for (size_t i = 0; i < init.size(); i += 2) {
