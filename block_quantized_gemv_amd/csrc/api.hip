@@ -123,10 +123,13 @@ int workspace(size_t need, hipStream_t stream, void** out) {
 // kernels.  Measured on MI355X at the 7B shapes (cold, n = 2..8): the
 // matrix cores take the same time for any n, the vector kernels' time
 // grows with n; they tie at n = 4 and the matrix cores lead from n = 5
-// (gate/up 24 vs 37 us at n = 8).
+// (gate/up 24 vs 37 us at n = 8).  Matrices too large for the matrix-core
+// kernel's 32-bit offsets (mfma_rows_fit) take the vector kernels.
 constexpr int kMfmaMinCols = 5;
 
-bool use_mfma(int fmt, int ncols) { return fmt == kFmtQ4K && ncols >= kMfmaMinCols; }
+bool use_mfma(int fmt, int ncols, int64_t m, int64_t k) {
+    return fmt == kFmtQ4K && ncols >= kMfmaMinCols && mfma_rows_fit(m, k);
+}
 
 int run_q4k_mfma(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t m, int64_t k, int ncols,
                  hipStream_t stream) {
@@ -142,7 +145,7 @@ int run_q4k_mfma(const void* w, const void* xq, int64_t col_bytes, float* y, int
 
 int run_q4(int fmt, const void* w, const void* xq, int64_t col_bytes, float* y, int32_t* isum, int32_t* ysum,
            int64_t m, int64_t k, int ncols, hipStream_t stream) {
-    if (!isum && use_mfma(fmt, ncols)) return run_q4k_mfma(w, xq, col_bytes, y, m, k, ncols, stream);
+    if (!isum && use_mfma(fmt, ncols, m, k)) return run_q4k_mfma(w, xq, col_bytes, y, m, k, ncols, stream);
     const int lds = ncols * stage_bytes((int)(k / 32));
     if (lds <= kMaxStageLds)
         return hip_status(launch_gemv_q4k(w, xq, col_bytes, y, isum, ysum, m, k, ncols, stream, fmt),
@@ -573,7 +576,7 @@ int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int6
     if (rc != MQ_OK) return rc;
     CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
     const int64_t col_bytes = (k / 32) * kQ8Bytes;
-    if (use_mfma(kFmtQ4K, n)) {
+    if (use_mfma(kFmtQ4K, n, m, k)) {
         const size_t need = (size_t)gemv_q4k_mfma_partial_bytes(m, k, n);
         CHECK_SHAPE(need <= kScratchBytes, "m=%lld, k=%lld, n=%d need %zu bytes of split-k partials; the fixed "
                     "scratch of the no-allocation entry point holds %zu", (long long)m, (long long)k, n, need,
@@ -603,6 +606,8 @@ int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int6
     CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
     CHECK_ARG(path == 0 || path == 1, "path must be 0 (vector kernels) or 1 (matrix cores)");
     CHECK_SHAPE(path == 0 || n >= 2, "the matrix-core path takes n >= 2");
+    CHECK_SHAPE(path == 0 || mfma_rows_fit(m, k), "m=%lld rows of k=%lld exceed the matrix-core path's 32-bit offsets",
+                (long long)m, (long long)k);
     const int64_t col_bytes = (k / 32) * kQ8Bytes;
     if (path == 1) return run_q4k_mfma(w, xq, col_bytes, y, m, k, n, stream);
     const int lds = n * stage_bytes((int)(k / 32));

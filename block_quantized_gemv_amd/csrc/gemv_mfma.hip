@@ -44,6 +44,13 @@
 // A wave owns 16-row tiles (strided across the CUs) and streams their
 // super-blocks in k order, kMfmaDepth in flight; blockIdx.y splits k, each
 // split leaving f64 partials that k_splitk_finalize sums in split order.
+// The weights are read through a raw buffer descriptor sized to the matrix:
+// a lane's byte offset is a per-lane constant plus the wave's cursor (one
+// add per load), and the rows of the last tile past M lie beyond the
+// descriptor's range, so the hardware returns zeros for them (they are
+// never stored).  The whole offset is in the lane's offset register, which
+// the range check covers; the matrix plus one tile must fit 32-bit offsets
+// (mfma_rows_fit).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -54,7 +61,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaPairBytes = 768;         // codes 512 + scales 256 per block pair
-__host__ __device__ constexpr int mfma_stage_bytes(int sb_per_split) { return sb_per_split * 4 * kMfmaPairBytes; }
+// After the staged blocks: zeros that the A operand's lane groups without
+// live codes read (at offsets (4u + e) * 256, 16 bytes each).
+constexpr int kMfmaZeroBytes = 1536;
+__host__ __device__ constexpr int mfma_stage_bytes(int sb_per_split) {
+    return sb_per_split * 4 * kMfmaPairBytes + kMfmaZeroBytes;
+}
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;   // raw (untyped) buffer, 32-bit data format
 constexpr int kMfmaMaxSbPerSplit = 16;      // 48 KiB of staging
 #ifndef MQ_MFMA_DEPTH
 #define MQ_MFMA_DEPTH 2
@@ -175,44 +188,58 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
     const int stride = GX * WPG;
     const int my_tiles = t0 < n_tiles ? (n_tiles - 1 - t0) / stride + 1 : 0;
     const int n_items = my_tiles * nsb_s;
-    const int64_t row_bytes = (int64_t)nsb * kQ4KBytes;
+    const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)((uint32_t)M * row_bytes), (int)kRawBufferWord3);
 
-    // Items are (tile, super-block) in that order, walked by a cursor that
-    // stays on the last item past the end (its lines are re-read, nothing is
-    // computed from them).  Rows past M read row M-1 and are not stored.
+    // Items are (tile, super-block) in that order, walked by a wave-uniform
+    // cursor (the item's byte offset, tile * 16 rows + super-block) that
+    // stays on the last item past the end (its lines are re-read, nothing
+    // is computed from them).
     struct Item {
         u32x4 hdr;
         u32x4 q[2];     // bytes 16g..16g+15 of chunks 2u, 2u+1 (64 bytes from 16 + 64u)
         int tile, sbl;
     };
+    const uint32_t lane_hdr = (uint32_t)i16 * row_bytes, lane_q = lane_hdr + 16u + 16u * (uint32_t)g;
+    const uint32_t tile_wrap = (uint32_t)stride * 16u * row_bytes - (uint32_t)(nsb_s - 1) * kQ4KBytes;
     int c_tile = t0, c_sb = 0, c_done = 0;
+    uint32_t c_off = (uint32_t)t0 * 16u * row_bytes + (uint32_t)sb0 * kQ4KBytes;
     auto fetch = [&](int, Item& it) {
         it.tile = c_tile;
         it.sbl = c_sb;
-        if (c_done < n_items && ++c_done < n_items && ++c_sb == nsb_s) {
-            c_sb = 0;
-            c_tile += stride;
+        const uint32_t off = c_off;
+        if (c_done < n_items && ++c_done < n_items) {
+            if (++c_sb == nsb_s) {
+                c_sb = 0;
+                c_tile += stride;
+                c_off += tile_wrap;
+            } else {
+                c_off += kQ4KBytes;
+            }
         }
-        const int row0 = it.tile * 16 + i16;
-        const int row = row0 < M ? row0 : M - 1;
-        const uint8_t* p = w + (int64_t)row * row_bytes + (int64_t)(sb0 + it.sbl) * kQ4KBytes;
-        it.hdr = *(const u32x4*)p;
+        it.hdr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_hdr + off, 0, 0));
 #pragma unroll
-        for (int u = 0; u < 2; ++u) it.q[u] = *(const u32x4*)(p + 16 + 64 * u + 16 * g);
+        for (int u = 0; u < 2; ++u)
+            it.q[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_q + off + 64u * u, 0, 0));
     };
 
     Item ring[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) fetch(u, ring[u]);
     stage_mfma<NC, 2>(xq, xq_col_bytes, 8 * sb0, nb, lds);
+    uint8_t* const zeros = lds + mfma_stage_bytes(sb_per_split) - kMfmaZeroBytes;
+    for (int t = threadIdx.x; t < kMfmaZeroBytes / 16; t += blockDim.x) *(u32x4*)(zeros + 16 * t) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 
     const int h = g >> 1, cb = 4 * (g & 1);
     // A operand: row i16 = 8*ha + c takes, in lane group g, codes 16(g&1)..16(g&1)+15 of
     // block 4u + 2ha + e (of the item's super-block) of column c when g >> 1 == ha, else zeros
+    // (lanes without live codes read the zeros, at the same offsets, whatever the item)
     const int ha = i16 >> 3;
     const bool a_live = (g >> 1) == ha;
-    const uint8_t* xa = lds + (2 * ha) * 256 + (i16 & 7) * 32 + 16 * (g & 1);
+    const uint8_t* xa = a_live ? lds + (2 * ha) * 256 + (i16 & 7) * 32 + 16 * (g & 1) : zeros;
+    const int xa_step = a_live ? 8 * 256 : 0;                       // per super-block
     const uint8_t* xd = lds + np * 512 + h * 256 + cb * 8;           // its four columns' d8 (pair 2u + h, half e)
     // the mins' operand: column 4((i % 4) & 1) + i/4 of row i = i16, sub-blocks
     // g (pair g/2, half g%2) and 4 + g (two pairs further)
@@ -221,6 +248,7 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
     v4d mins = {0.0, 0.0, 0.0, 0.0};
     stream_ring<D>(n_items, ring, fetch, [&](const Item& it) {
         const int P0 = 4 * it.sbl;
+        const uint8_t* xi = xa + it.sbl * xa_step;
         // C[2u + e]: sub-block 4u + 2h + e of this lane's rows (h = g >> 1)
         v4i C[4];
 #pragma unroll
@@ -231,8 +259,8 @@ __global__ __launch_bounds__(1024) void k_gemv_q4k_mfma(const uint8_t* __restric
                 const uint32_t sh = 4 * e;
                 const v4i wb = {(int)((q.x >> sh) & 0x0F0F0F0Fu), (int)((q.y >> sh) & 0x0F0F0F0Fu),
                                 (int)((q.z >> sh) & 0x0F0F0F0Fu), (int)((q.w >> sh) & 0x0F0F0F0Fu)};
-                const u32x4 x = *(const u32x4*)(xa + (2 * P0 + 4 * u + e) * 256);
-                const v4i xv = a_live ? v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w} : v4i{0, 0, 0, 0};
+                const u32x4 x = *(const u32x4*)(xi + (4 * u + e) * 256);
+                const v4i xv = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
                 C[2 * u + e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xv, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
             }
         }
@@ -331,8 +359,11 @@ int64_t gemv_q4k_mfma_partial_bytes(int64_t m, int64_t k, int ncols) {
     return p.n_split > 1 ? (int64_t)p.n_split * m * ncols * (int64_t)sizeof(double) : 0;
 }
 
+bool mfma_rows_fit(int64_t m, int64_t k) { return (m + 16) * (k / 256) * kQ4KBytes <= (int64_t)0xFFFFFFFF; }
+
 hipError_t launch_gemv_q4k_mfma(const void* w, const void* xq, int64_t xq_col_bytes, float* y, double* part,
                                 int64_t m, int64_t k, int ncols, hipStream_t stream) {
+    if (!mfma_rows_fit(m, k)) return hipErrorInvalidValue;
     const int nsb = (int)(k / 256);
     switch (ncols) {
         case 2: return launch_mfma_nc<2>(w, xq, xq_col_bytes, y, part, m, nsb, stream);

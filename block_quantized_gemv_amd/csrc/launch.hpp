@@ -148,6 +148,10 @@ struct MfmaPlan {
     int n_split, sb_per_split, n_tiles, lds, grid_x, threads;
 };
 MfmaPlan plan_gemv_q4k_mfma(int64_t m, int nsb);
+// The matrix-core kernel addresses the matrix with 32-bit byte offsets: the
+// m rows and one more 16-row tile must fit (else launch_gemv_q4k_mfma
+// refuses the shape and the batched GEMV takes the vector kernels).
+bool mfma_rows_fit(int64_t m, int64_t k);
 int64_t gemv_q4k_mfma_partial_bytes(int64_t m, int64_t k, int ncols);
 hipError_t launch_gemv_q4k_mfma(const void* w, const void* xq, int64_t xq_col_bytes, float* y, double* part,
                                 int64_t m, int64_t k, int ncols, hipStream_t stream);

@@ -139,9 +139,10 @@ int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int6
  * vector kernels: v_dot4 sums, one column per pass over the staged
  * activation) or path 1 (the matrix cores, n >= 2: v_mfma_i32_16x16x64_i8
  * sums of 16 rows x 8 columns x 2 sub-blocks).  The batched entry point
- * itself takes path 1 for n >= 5.  Same arguments, errors and workspace as
- * mq_gemv_q4k_q8_batched; MQ_ERR_ARG for another path, MQ_ERR_SHAPE for
- * path 1 with n = 1. */
+ * itself takes path 1 for n >= 5 when the matrix and one more 16-row tile
+ * fit 32-bit byte offsets (under 4 GiB), else path 0.  Same arguments,
+ * errors and workspace as mq_gemv_q4k_q8_batched; MQ_ERR_ARG for another
+ * path, MQ_ERR_SHAPE for path 1 with n = 1 or a matrix beyond that size. */
 int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n, int path,
                                    hipStream_t stream);
 
