@@ -28,7 +28,7 @@ class ChainDesc(C.Structure):
                 ("inter", C.c_int64), ("vocab", C.c_int64),
                 ("w_qkv", C.POINTER(_u8p)), ("w_o", C.POINTER(_u8p)),
                 ("w_gu", C.POINTER(_u8p)), ("w_down", C.POINTER(_u8p)),
-                ("w_lm", _u8p), ("eps", C.c_float), ("weight_format", C.c_int)]
+                ("w_lm", _u8p), ("eps", C.c_float), ("weight_format", C.c_int), ("o_k", C.c_int64)]
 
 
 OREF_Q4K, OREF_Q4_0 = 0, 1
@@ -258,7 +258,8 @@ class Oracle:
         lm = _u8(weights["lm"])
         d = ChainDesc(L, model.hidden, model.qkv_rows, model.inter, model.vocab,
                       ptrs(weights["qkv"]), ptrs(weights["o"]), ptrs(weights["gu"]),
-                      ptrs(weights["down"]), _p(lm, _u8p), model.eps, weight_format_code(model))
+                      ptrs(weights["down"]), _p(lm, _u8p), model.eps, weight_format_code(model),
+                      getattr(model, "o_k", 0))
         h0 = np.ascontiguousarray(h0, dtype=np.float32)
         logits = np.empty(model.vocab, np.float32)
         s_abs = np.empty(model.vocab, np.float64)

@@ -315,15 +315,19 @@ int64_t oref_chain_f32_trace_len(const oref_chain_desc* d) {
 
 void oref_chain(const oref_chain_desc* d, const float* h0, float* logits,
                 uint8_t* q8_trace, float* f32_trace, double* s_abs) {
-    const int64_t H = d->hidden, I = d->inter;
+    const int64_t H = d->hidden, I = d->inter, Ko = d->o_k ? d->o_k : d->hidden;
     void (*gemv)(const uint8_t*, int64_t, int64_t, const uint8_t*, float*, double*) =
         d->weight_format == OREF_Q4_0 ? oref_gemv_q4_0 : oref_gemv_q4k;
     std::vector<float> h(h0, h0 + H), t(d->qkv_rows), o(H), gu(2 * I), nrm(I > H ? I : H);
     std::vector<uint8_t> q(I / 32 * 34 > H / 32 * 34 ? I / 32 * 34 : H / 32 * 34);
     uint8_t* q8t = q8_trace;
     float* f32t = f32_trace;
-    auto keep_q8 = [&](int64_t n) {
-        if (q8t) { memcpy(q8t, q.data(), n / 32 * 34); q8t += n / 32 * 34; }
+    /* n values kept in a slot of `slot` values, zero past them */
+    auto keep_q8 = [&](int64_t n, int64_t slot) {
+        if (!q8t) return;
+        memcpy(q8t, q.data(), n / 32 * 34);
+        memset(q8t + n / 32 * 34, 0, (slot - n) / 32 * 34);
+        q8t += slot / 32 * 34;
     };
     auto keep_f32 = [&](const std::vector<float>& v, int64_t n) {
         if (f32t) { memcpy(f32t, v.data(), n * sizeof(float)); f32t += n; }
@@ -331,22 +335,22 @@ void oref_chain(const oref_chain_desc* d, const float* h0, float* logits,
     for (int l = 0; l < d->n_layers; ++l) {
         oref_rmsnorm(h.data(), H, d->eps, nrm.data());
         oref_quantize_q8_0(nrm.data(), H, q.data());
-        keep_q8(H);
+        keep_q8(H, H);
         gemv(d->w_qkv[l], d->qkv_rows, H, q.data(), t.data(), nullptr);
 
-        oref_rmsnorm(t.data(), H, d->eps, nrm.data());      /* first H outputs of QKV */
-        oref_quantize_q8_0(nrm.data(), H, q.data());
-        keep_q8(H);
-        gemv(d->w_o[l], H, H, q.data(), o.data(), nullptr);
+        oref_rmsnorm(t.data(), Ko, d->eps, nrm.data());     /* first Ko outputs of QKV */
+        oref_quantize_q8_0(nrm.data(), Ko, q.data());
+        keep_q8(Ko, H);
+        gemv(d->w_o[l], H, Ko, q.data(), o.data(), nullptr);
 
         oref_rmsnorm(o.data(), H, d->eps, nrm.data());
         oref_quantize_q8_0(nrm.data(), H, q.data());
-        keep_q8(H);
+        keep_q8(H, H);
         gemv(d->w_gu[l], 2 * I, H, q.data(), gu.data(), nullptr);
 
         oref_swiglu(gu.data(), I, nrm.data());
         oref_quantize_q8_0(nrm.data(), I, q.data());
-        keep_q8(I);
+        keep_q8(I, I);
         gemv(d->w_down[l], H, I, q.data(), h.data(), nullptr);
 
         keep_f32(t, d->qkv_rows);
@@ -356,7 +360,7 @@ void oref_chain(const oref_chain_desc* d, const float* h0, float* logits,
     }
     oref_rmsnorm(h.data(), H, d->eps, nrm.data());
     oref_quantize_q8_0(nrm.data(), H, q.data());
-    keep_q8(H);
+    keep_q8(H, H);
     oref_gemv_q8_0(d->w_lm, d->vocab, H, q.data(), logits, s_abs);
 }
 

@@ -109,14 +109,15 @@ void oref_softmax(const float* logits, int64_t n, float* p);
 
 /* --- one decode step --------------------------------------------------------
  * Per layer:  a = Q8(RMSNorm(h));        t  = W_qkv  a   (qkv_rows)
- *             b = Q8(RMSNorm(t[0:H]));   o  = W_o    b   (H)
+ *             b = Q8(RMSNorm(t[0:Ko]));  o  = W_o    b   (H rows, Ko columns)
  *             c = Q8(RMSNorm(o));        gu = W_gu   c   (2*inter: gate rows, then up rows)
  *             g = Q8(SwiGLU(gu));        h  = W_down g   (H)
  * Final:      z = Q8(RMSNorm(h));        logits = W_lm z (q8_0 weights, vocab rows)
  * The four layer GEMVs take q4_K weights, or q4_0 with weight_format
  * OREF_Q4_0.  Weight pointers are host arrays of n_layers host pointers.
  * Optional traces (NULL to skip):
- *   q8_trace: per layer the Q8 bytes of a, b, c, g, then z at the end;
+ *   q8_trace: per layer the Q8 bytes of a, b, c, g, then z at the end (b in a
+ *             slot of H/32 blocks, zero past its Ko/32);
  *   f32_trace: per layer t, o, gu, h.
  *   s_abs: vocab f64 values for the final GEMV. */
 typedef struct {
@@ -129,6 +130,11 @@ typedef struct {
     const uint8_t* w_lm;
     float eps;
     int weight_format;      /* OREF_Q4K or OREF_Q4_0 */
+    /* Ko, O's K (0 means H): one rank's share of a tensor-parallel split
+     * takes O's columns for its own slice of the attention stand-in, the
+     * first Ko outputs of its QKV rows.  256 <= Ko <= H, Ko % 256 == 0,
+     * Ko <= qkv_rows. */
+    int64_t o_k;
 } oref_chain_desc;
 enum { OREF_Q4K = 0, OREF_Q4_0 = 1 };
 

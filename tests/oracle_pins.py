@@ -399,7 +399,7 @@ def _tiny_weights(g, model):
     L = model.n_layers
     return {
         "qkv": [RandomQ4K(g, model.qkv_rows, model.hidden).bytes for _ in range(L)],
-        "o": [RandomQ4K(g, model.hidden, model.hidden).bytes for _ in range(L)],
+        "o": [RandomQ4K(g, model.hidden, getattr(model, "o_k", 0) or model.hidden).bytes for _ in range(L)],
         "gu": [RandomQ4K(g, 2 * model.inter, model.hidden).bytes for _ in range(L)],
         "down": [RandomQ4K(g, model.hidden, model.inter).bytes for _ in range(L)],
         "lm": np.stack([RandomQ8(g, model.hidden).bytes for _ in range(model.vocab)]),
@@ -434,6 +434,41 @@ def pin_chain_structure(o):
 
 class _TinyModelQ4_0(_TinyModel):
     weight_format = "q4_0"
+
+
+class _TinyRank(_TinyModel):
+    """One rank's share of a tensor-parallel split: fewer QKV rows than the
+    hidden width, and O taking only the first o_k of them."""
+    hidden, qkv_rows, inter, vocab, o_k = 512, 320, 512, 64, 256
+
+
+def pin_chain_structure_o_k(o):
+    """With O's K set below the hidden width, O normalizes and consumes only
+    the first o_k QKV outputs (its (hidden x o_k) matrix), and the trace keeps
+    that q8_0 vector in a hidden-wide slot, zero past its o_k/32 blocks; the
+    rest of the step is unchanged."""
+    g = np.random.default_rng(71)
+    model = _TinyRank(2)
+    W = _tiny_weights(g, model)
+    h = g.standard_normal(model.hidden).astype(np.float32)
+    out = o.chain(model, W, h, traces=True)
+    H, I, K = model.hidden, model.inter, model.o_k
+    q8s = []
+    for l in range(2):
+        a = o.quantize_q8_0(o.rmsnorm(h, model.eps)).ravel(); q8s.append(a)
+        t, _ = o.gemv_q4k(W["qkv"][l], model.qkv_rows, H, a)
+        assert t.size == model.qkv_rows
+        b = o.quantize_q8_0(o.rmsnorm(t[:K], model.eps)).ravel()
+        q8s.append(np.concatenate([b, np.zeros((H - K) // 32 * 34, np.uint8)]))
+        ov, _ = o.gemv_q4k(W["o"][l], H, K, b)
+        c = o.quantize_q8_0(o.rmsnorm(ov, model.eps)).ravel(); q8s.append(c)
+        gu, _ = o.gemv_q4k(W["gu"][l], 2 * I, H, c)
+        gg = o.quantize_q8_0(o.swiglu(gu)).ravel(); q8s.append(gg)
+        h, _ = o.gemv_q4k(W["down"][l], H, I, gg)
+    z = o.quantize_q8_0(o.rmsnorm(h, model.eps)).ravel(); q8s.append(z)
+    logits, _ = o.gemv_q8_0(W["lm"], model.vocab, H, z)
+    assert np.array_equal(out["logits"], logits), "rank chain logits != composition"
+    assert np.array_equal(out["q8_trace"], np.concatenate(q8s)), "rank chain q8 trace"
 
 
 def pin_chain_structure_q4_0(o):

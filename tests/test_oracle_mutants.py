@@ -78,8 +78,8 @@ MUTATIONS = [
     ("softmax not normalised",
      "p[i] = (float)(exp((double)logits[i] - mx) / s);", "p[i] = (float)(exp((double)logits[i] - mx));"),
     ("chain O normalises all of QKV",
-     "oref_rmsnorm(t.data(), H, d->eps, nrm.data());      /* first H outputs of QKV */",
-     "oref_rmsnorm(t.data() + (d->qkv_rows - H), H, d->eps, nrm.data());"),
+     "oref_rmsnorm(t.data(), Ko, d->eps, nrm.data());     /* first Ko outputs of QKV */",
+     "oref_rmsnorm(t.data() + (d->qkv_rows - Ko), Ko, d->eps, nrm.data());"),
     ("chain layer output not carried",
      "gemv(d->w_down[l], H, I, q.data(), h.data(), nullptr);",
      "gemv(d->w_down[l], H, I, q.data(), o.data(), nullptr);"),
