@@ -28,7 +28,9 @@ in HBM.  Prints one JSON line (rank 0):
                kernel's in-graph span from the same stamps
   cpu_baseline = the reference oracle on the host, on a bounded sample
 
-Other workloads (--workload 05b|single|batched|moe) print their own line.
+Other workloads (--workload 05b|05b_q4_0|7b_tp8|single|batched|moe) print their
+own line; 7b_tp8 is the step of the largest of eight tensor-parallel ranks of
+the 7B-class model (its shard shapes, the collectives not run).
 """
 from __future__ import annotations
 
@@ -57,7 +59,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="7b", choices=["7b", "05b", "05b_q4_0", "single", "batched", "moe"])
+    p.add_argument("--workload", default="7b", choices=["7b", "05b", "05b_q4_0", "7b_tp8", "single", "batched", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ab", action="store_true", help="skip the interleaved A/B arms (for counter runs)")
     p.add_argument("--no-stamps", action="store_true", help="skip the span-stamp measurement of the step")
@@ -165,14 +167,14 @@ def gemv_kinds(model):
     weights + activation in (f32 where the kernel forms Q8(RMSNorm(x)) in its
     prologue, q8_0 otherwise) + output written (f32, or q8_0 after SwiGLU)."""
     from block_quantized_gemv_amd import workloads as wl
-    H, I, Q = model.hidden, model.inter, model.qkv_rows
+    H, I, Q, KO = model.hidden, model.inter, model.qkv_rows, model.o_in
     wb = model.layer_matrix_bytes
     f = 1 if model.weight_format == "q4_0" else 0      # the kernels' format template argument
     norm = f"mq::k_gemv_q4k<{f},1,false,2,false>"
     kinds = []
     for _ in range(model.n_layers):
         kinds += [("qkv", norm, wb(Q, H) + 4 * H + 4 * Q),
-                  ("o", norm, wb(H, H) + 4 * H + 4 * H),
+                  ("o", norm, wb(H, KO) + 4 * KO + 4 * H),
                   ("gate/up", f"mq::k_gemv_q4k_swiglu<{f},true,false>", wb(2 * I, H) + 4 * H + wl.q8_bytes(1, I)),
                   ("down", f"mq::k_gemv_q4k<{f},1,false,1,false>", wb(H, I) + wl.q8_bytes(1, I) + 4 * H)]
     kinds.append(("lm_head", "mq::k_gemv_q8_0<false,true,false>", wl.q8_bytes(model.vocab, H) + 4 * H + 4 * model.vocab))
@@ -541,7 +543,8 @@ def run_decode(args, model, cpu_layers, probe=None):
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
            "config": {"workload": model.name, "hidden": model.hidden, "layers": model.n_layers,
-                      "qkv_rows": model.qkv_rows, "inter": model.inter, "vocab": model.vocab, "n": 1,
+                      "qkv_rows": model.qkv_rows, "o_k": model.o_in, "inter": model.inter, "vocab": model.vocab,
+                      "n": 1,
                       "seed": model.seed, "weights": f"{model.weight_format} (lm_head q8_0)", "graph": bool(info["captured"]),
                       "graph_nodes": info["n_nodes"], "bytes_per_step": nbytes},
            "tok_per_s": round(1e3 / ms, 2), "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -760,11 +763,15 @@ def run_moe(args):
     return out
 
 
-def other_configs(args, probe):
-    """Compact results of the four other workloads (0.5B step, single GEMV,
-    batched 7B shapes, routed-expert token), GPU side only, for the default
-    line: each with its time, its algorithmic-byte rate and that rate as a
-    fraction of 8 TB/s."""
+TP8_COLLECTIVES = ("not run: a tensor-parallel step adds two all-reduces of the 14,336-byte f32 hidden "
+                   "vector per layer (after O and after down) and gathers the lm_head's vocabulary slices")
+
+
+def other_configs(args, probe, full_step_ms=None):
+    """Compact results of the other workloads (0.5B step, single GEMV,
+    batched 7B shapes, routed-expert token, one tensor-parallel rank of the
+    7B step), GPU side only, for the default line: each with its time, its
+    algorithmic-byte rate and that rate as a fraction of 8 TB/s."""
     import copy
     from block_quantized_gemv_amd import workloads
     a = copy.copy(args)
@@ -807,6 +814,17 @@ def other_configs(args, probe):
                            "tokens_per_s": m["tokens_per_s"], "GB_s": m["value"], "frac_of_8TBs": frac(m["value"]),
                            "tokens_per_graph_launch": m["config"]["tokens_per_graph_launch"]}
     log(f"extra: routed-expert token {m['us_per_token']} us ({time.perf_counter() - t0:.1f} s)")
+    a.no_stamps = True
+    r = run_decode(a, workloads.DECODE_7B_TP8, cpu_layers=0, probe=probe)
+    out["tp8_rank_7b_decode_step"] = {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
+                                      "GB_s": r["value"], "frac_of_8TBs": frac(r["value"]),
+                                      "bytes_per_step": r["config"]["bytes_per_step"],
+                                      "graph_nodes": r["config"]["graph_nodes"],
+                                      "per_kernel_us": {k: v["us"] for k, v in r["roofline"]["per_shape"].items()},
+                                      "collectives": TP8_COLLECTIVES}
+    if full_step_ms:
+        out["tp8_rank_7b_decode_step"]["full_step_over_rank_step"] = round(full_step_ms / r["ms_per_step"], 3)
+    log(f"extra: tensor-parallel rank step {r['ms_per_step']} ms ({time.perf_counter() - t0:.1f} s)")
     return out
 
 
@@ -839,11 +857,14 @@ def main():
         probe = stream_probe(mq)
         out = run_decode(args, workloads.DECODE_7B, cpu_layers=workloads.DECODE_7B.n_layers, probe=probe)
         if not args.no_extra:
-            out["other_configs"] = other_configs(args, probe)
+            out["other_configs"] = other_configs(args, probe, out["ms_per_step"])
     elif args.workload == "05b":
         out = run_decode(args, workloads.DECODE_05B, cpu_layers=workloads.DECODE_05B.n_layers)
     elif args.workload == "05b_q4_0":
         out = run_decode(args, workloads.DECODE_05B_Q4_0, cpu_layers=workloads.DECODE_05B_Q4_0.n_layers)
+    elif args.workload == "7b_tp8":
+        out = run_decode(args, workloads.DECODE_7B_TP8, cpu_layers=workloads.DECODE_7B_TP8.n_layers)
+        out["config"]["collectives"] = TP8_COLLECTIVES
     elif args.workload == "single":
         out = run_single(args)
     elif args.workload == "batched":

@@ -42,7 +42,8 @@ class ChainDesc(C.Structure):
                 ("inter", C.c_int64), ("vocab", C.c_int64),
                 ("w_qkv", C.POINTER(_vp)), ("w_o", C.POINTER(_vp)), ("w_gu", C.POINTER(_vp)),
                 ("w_down", C.POINTER(_vp)), ("w_lm", _vp), ("x_table", _vp), ("n_inputs", C.c_int),
-                ("logits", _vp), ("eps", C.c_float), ("flags", C.c_uint), ("weight_format", C.c_int)]
+                ("logits", _vp), ("eps", C.c_float), ("flags", C.c_uint), ("weight_format", C.c_int),
+                ("o_k", _i64)]
 
 
 class MoEDesc(C.Structure):
@@ -413,7 +414,7 @@ class DecodeChain:
                       _ptr(weights["lm"], torch.uint8, q8_bytes(model.vocab, model.hidden), "lm"),
                       _ptr(x_table, torch.float32, 4 * n_inputs * model.hidden, "x_table"), n_inputs,
                       _ptr(self.logits, torch.float32, 4 * model.vocab, "logits"), model.eps, flags,
-                      MQ_FMT_Q4_0 if fmt == "q4_0" else MQ_FMT_Q4_K)
+                      MQ_FMT_Q4_0 if fmt == "q4_0" else MQ_FMT_Q4_K, getattr(model, "o_k", 0))
         h = _vp()
         _check(lib().mq_chain_create(C.byref(d), _stream(stream), C.byref(h)))
         self.handle = h

@@ -734,8 +734,11 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     CHECK_SHAPE(d->n_layers >= 1 && d->n_layers <= 4096, "n_layers out of range");
     CHECK_SHAPE(d->hidden >= 256 && d->hidden % 256 == 0 && d->hidden <= kMaxK, "hidden must be a multiple of 256");
     CHECK_SHAPE(d->inter >= 256 && d->inter % 256 == 0 && d->inter <= kMaxK, "inter must be a multiple of 256");
-    CHECK_SHAPE(d->qkv_rows >= d->hidden && d->qkv_rows <= kMaxRows && d->qkv_rows % 4 == 0,
-                "qkv_rows must be >= hidden and a multiple of 4");
+    CHECK_SHAPE(d->o_k == 0 || (d->o_k >= 256 && d->o_k % 256 == 0 && d->o_k <= d->hidden),
+                "o_k must be 0 or a multiple of 256 in [256, hidden]");
+    const int64_t o_k = d->o_k ? d->o_k : d->hidden;
+    CHECK_SHAPE(d->qkv_rows >= o_k && d->qkv_rows <= kMaxRows && d->qkv_rows % 4 == 0,
+                "qkv_rows must be >= O's K (o_k, or hidden) and a multiple of 4");
     CHECK_SHAPE(d->vocab >= 1 && d->vocab <= kMaxRows, "vocab out of range");
     CHECK_SHAPE(stage_bytes((int)(d->inter / 32)) <= kMaxStageLds, "inter too large");
     CHECK_SHAPE(d->qkv_rows <= max_rows_per_launch(d->hidden) && 2 * d->inter <= max_rows_per_launch(d->hidden) &&
@@ -760,7 +763,7 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     c->logits = d->logits;
     c->vocab = d->vocab;
     const int L = d->n_layers;
-    const int64_t H = d->hidden, I = d->inter, QKV = d->qkv_rows;
+    const int64_t H = d->hidden, I = d->inter, QKV = d->qkv_rows, KO = o_k;
     const int64_t qH = H / 32 * kQ8Bytes, qI = I / 32 * kQ8Bytes;
     const bool keep = (d->flags & MQ_KEEP_INTERMEDIATES) != 0;
     const int exact = (d->flags & MQ_EXACT_GLUE) != 0;
@@ -775,6 +778,9 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
     const int64_t q8_alloc = keep ? c->q8_bytes : q8_layer + qH;
     const int64_t f32_alloc = keep ? c->f32_count : f32_layer;
     if (rc == MQ_OK) c->q8_trace = (uint8_t*)chain_alloc(c, q8_alloc, &rc);
+    // O's input fills only o_k/32 blocks of its slot: the rest reads as zeros
+    if (rc == MQ_OK && keep && KO < H && hipMemset(c->q8_trace, 0, q8_alloc) != hipSuccess)
+        rc = fail(MQ_ERR_HIP, "clearing the q8_0 trace");
     if (rc == MQ_OK) c->f32_trace = (float*)chain_alloc(c, f32_alloc * sizeof(float), &rc);
     // gate/up blocks beyond a multiple of the CU count are split in two halves
     // along K (launch_gemv_q4k_swiglu), with this hand-over space
@@ -816,8 +822,8 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
             const int nin = l == 0 ? n_inputs : 1;
             c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(xin, qa, H, eps, sel, nin, nullptr, s); });
             c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wq, qa, 0, t, nullptr, nullptr, QKV, H, 1, s, fmt); });
-            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, H, eps, nullptr, 1, nullptr, s); });
-            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, H, 1, s, fmt); });
+            c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(t, qb, KO, eps, nullptr, 1, nullptr, s); });
+            c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wo, qb, 0, o, nullptr, nullptr, H, KO, 1, s, fmt); });
             c->ops.push_back([=](hipStream_t s) { return launch_rmsnorm_quantize(o, qc, H, eps, nullptr, 1, nullptr, s); });
             c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k(wg, qc, 0, gu, nullptr, nullptr, 2 * I, H, 1, s, fmt); });
             c->ops.push_back([=](hipStream_t s) { return launch_swiglu_quantize(gu, qg, I, 1, I, s); });
@@ -853,7 +859,7 @@ int mq_chain_create(const mq_chain_desc* d, hipStream_t stream, mq_chain** out) 
         const NormIn nb{t, nullptr, 1, eps, keep ? qb : nullptr, nullptr, exact, st ? st + sr : nullptr};
         const NormIn nc{o, nullptr, 1, eps, keep ? qc : nullptr, nullptr, exact, st ? st + 2 * sr : nullptr};
         c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wq, na, t, QKV, H, s, fmt); });
-        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, H, s, fmt); });
+        c->ops.push_back([=](hipStream_t s) { return launch_gemv_q4k_norm(wo, nb, o, H, KO, s, fmt); });
         double* gp = c->gu_part;
         unsigned* gc = c->gu_cnt;
         const int gn = c->gu_split;

@@ -1308,10 +1308,15 @@ static hipError_t launch_swiglu(const void* w, const void* xq, const NormIn* nin
     return hipGetLastError();
 }
 
+// Blocks to split in two K-halves: those beyond a multiple of the CU count,
+// or, when even the doubled count leaves CUs idle (a small gate/up such as
+// one tensor-parallel rank's share), every block.  K must take at least two
+// passes.
 int swiglu_split_blocks(int64_t inter, int64_t k) {
     const int64_t nblk = inter / 32, cus = device_cu_count();
     const int64_t passes = (k / 256 + 3) / 4;
-    if (passes < 2 || nblk <= cus) return 0;
+    if (passes < 2) return 0;
+    if (nblk <= cus) return 2 * nblk <= cus ? (int)nblk : 0;
     return (int)(nblk % cus);
 }
 

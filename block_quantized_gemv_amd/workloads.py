@@ -48,10 +48,15 @@ class DecodeModel:
     seed: int
     eps: float = 1e-6
     weight_format: str = "q4_K"      # layer matrices: "q4_K" or "q4_0"
+    o_k: int = 0                     # O's K, the first o_k QKV outputs (0: hidden)
+
+    @property
+    def o_in(self) -> int:
+        return self.o_k or self.hidden
 
     def layer_shapes(self):
         """(rows, k) of the four 4-bit GEMVs of one layer, in step order."""
-        return [(self.qkv_rows, self.hidden), (self.hidden, self.hidden),
+        return [(self.qkv_rows, self.hidden), (self.hidden, self.o_in),
                 (2 * self.inter, self.hidden), (self.hidden, self.inter)]
 
     def layer_matrix_bytes(self, m: int, k: int) -> int:
@@ -80,6 +85,16 @@ DECODE_05B_Q4_0 = DecodeModel("0.5B-class decode step, q4_0 layer weights (hidde
                               weight_format="q4_0")
 DECODE_7B = DecodeModel("7B-class decode step (hidden 3584, 28 layers, q8_0 lm_head 152064x3584)",
                         hidden=3584, n_layers=28, qkv_rows=4608, inter=18944, vocab=152064, seed=2)
+# One rank of the 7B-class step split eight ways (tensor-parallel, the
+# collectives left out): QKV and gate/up split by rows, O and down by K on
+# super-block boundaries, the lm_head by vocabulary rows.  O's 14 and down's
+# 74 super-blocks of K do not divide by 8, so ranks take 2 or 1 and 10 or 9;
+# this is the largest rank (O K = 512, down K = 2560, so gate/up 2 x 2560
+# rows), whose step bounds the split step.
+DECODE_7B_TP8 = DecodeModel("7B-class decode step, largest of 8 tensor-parallel ranks (QKV 576x3584, "
+                            "O 3584x512, gate/up 5120x3584, down 3584x2560, q8_0 lm_head 19008x3584; "
+                            "collectives not run)",
+                            hidden=3584, n_layers=28, qkv_rows=576, inter=2560, vocab=19008, seed=6, o_k=512)
 
 
 @dataclass(frozen=True)

@@ -319,7 +319,7 @@ enum { MQ_FMT_Q4_K = 0, MQ_FMT_Q4_0 = 1 };
 
 typedef struct {
     int n_layers;                      /* >= 1 */
-    int64_t hidden, qkv_rows, inter, vocab;   /* hidden, inter % 256 == 0; qkv_rows >= hidden, % 4 == 0 */
+    int64_t hidden, qkv_rows, inter, vocab;   /* hidden, inter % 256 == 0; qkv_rows >= O's K, % 4 == 0 */
     const void* const* w_qkv;          /* HOST arrays of n_layers device pointers (weight_format) */
     const void* const* w_o;
     const void* const* w_gu;
@@ -332,6 +332,12 @@ typedef struct {
     unsigned flags;                    /* MQ_EAGER_ONLY | MQ_KEEP_INTERMEDIATES | MQ_EXACT_GLUE | MQ_UNFUSED_GLUE
                                           | MQ_LAZY_CAPTURE | MQ_HOST_LOGITS | MQ_SPAN_STAMPS */
     int weight_format;                 /* MQ_FMT_Q4_K or MQ_FMT_Q4_0 (layer matrices) */
+    int64_t o_k;                       /* O's K, 0 for hidden: O normalizes and reads the first o_k
+                                          QKV outputs (a [hidden][o_k] matrix), as one rank of a
+                                          tensor-parallel split takes its own slice of the attention
+                                          stand-in; 256 <= o_k <= hidden, o_k % 256 == 0.  With
+                                          MQ_KEEP_INTERMEDIATES O's q8_0 input keeps a slot of
+                                          hidden/32 blocks, zero past its o_k/32 */
 } mq_chain_desc;
 
 /* Validates, allocates every device buffer the step needs (nothing is

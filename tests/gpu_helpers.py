@@ -75,14 +75,16 @@ def oracle_chain_parallel(o, model, W, h0, n_layers, pool):
     Returns logits, s_abs, q8 trace, f32 trace, and the f64 sum_i |w_i x_i|
     of every f32 trace value (the per-row tolerance of its GEMV)."""
     H, I, eps = model.hidden, model.inter, model.eps
+    K = getattr(model, "o_k", 0) or H          # O's K: the first K QKV outputs
     gemv = o.gemv_q4_0 if getattr(model, "weight_format", "q4_K") == "q4_0" else o.gemv_q4k
     h = np.asarray(h0, np.float32)
     q8s, f32s, sabs = [], [], []
     for l in range(n_layers):
         a = o.quantize_q8_0(o.rmsnorm(h, eps)).ravel(); q8s.append(a)
         t, st = oracle_gemv_parallel(gemv, W["qkv"][l], model.qkv_rows, H, a, pool=pool)
-        b = o.quantize_q8_0(o.rmsnorm(t[:H], eps)).ravel(); q8s.append(b)
-        ov, so = oracle_gemv_parallel(gemv, W["o"][l], H, H, b, pool=pool)
+        b = o.quantize_q8_0(o.rmsnorm(t[:K], eps)).ravel()
+        q8s.append(np.concatenate([b, np.zeros((H - K) // 32 * 34, np.uint8)]))   # a hidden-wide trace slot
+        ov, so = oracle_gemv_parallel(gemv, W["o"][l], H, K, b, pool=pool)
         c = o.quantize_q8_0(o.rmsnorm(ov, eps)).ravel(); q8s.append(c)
         gu, sg = oracle_gemv_parallel(gemv, W["gu"][l], 2 * I, H, c, pool=pool)
         g = o.quantize_q8_0(o.swiglu(gu)).ravel(); q8s.append(g)
@@ -146,7 +148,7 @@ def model_weights(model, n_layers):
     W = {"qkv": [], "o": [], "gu": [], "down": []}
     for l in range(n_layers):
         W["qkv"].append(mat(s, (synth.KEY_LAYER, l, 0), model.qkv_rows, model.hidden))
-        W["o"].append(mat(s, (synth.KEY_LAYER, l, 1), model.hidden, model.hidden))
+        W["o"].append(mat(s, (synth.KEY_LAYER, l, 1), model.hidden, getattr(model, "o_k", 0) or model.hidden))
         W["gu"].append(mat(s, (synth.KEY_LAYER, l, 2), 2 * model.inter, model.hidden))
         W["down"].append(mat(s, (synth.KEY_LAYER, l, 3), model.hidden, model.inter))
     W["lm"] = synth.q8_0_matrix(s, (synth.KEY_LM_HEAD,), model.vocab, model.hidden)

@@ -119,7 +119,14 @@ def test_chain_argument_errors(mq):
     assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_ARG          # n_inputs
     d.n_inputs, d.qkv_rows = 1, 512
     assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # qkv_rows < hidden
-    d.qkv_rows, d.weight_format = 1280, 7
+    d.qkv_rows, d.o_k = 1280, 100
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # o_k % 256
+    d.o_k = 2048
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # o_k > hidden
+    d.o_k, d.qkv_rows = 512, 256
+    assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_SHAPE        # qkv_rows < o_k
+    assert "o_k" in L.mq_last_error().decode()
+    d.qkv_rows, d.o_k, d.weight_format = 1280, 0, 7
     assert L.mq_chain_create(C.byref(d), None, C.byref(out)) == mq.MQ_ERR_ARG          # weight_format
     assert "weight_format" in L.mq_last_error().decode()
     d.weight_format = mq.MQ_FMT_Q4_K

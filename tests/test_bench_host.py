@@ -7,7 +7,10 @@ The per-matrix weight bytes are the figures of the q4_K / q8_0 formats
 two decode steps: 7B-class layer QKV 9,289,728, O 7,225,344, gate/up
 76,382,208, down 38,191,104 and lm_head 579,059,712 bytes, 4,249,534,464
 weight bytes per step; 0.5B-class 737,280 / 589,824 / 5,603,328 / 2,801,664,
-lm_head 164,888,576, 398,458,880 per step."""
+lm_head 164,888,576, 398,458,880 per step; the largest of eight tensor-parallel
+ranks of the 7B-class step (QKV 576x3584, O 3584x512, gate/up 5120x3584, down
+3584x2560, lm_head 19008x3584) 1,161,216 / 1,032,192 / 10,321,920 / 5,160,960,
+lm_head 72,382,464, 567,318,528 per step."""
 import hashlib
 import os
 import subprocess
@@ -24,6 +27,7 @@ from block_quantized_gemv_amd import workloads  # noqa: E402
 WEIGHTS = {
     "7b": (workloads.DECODE_7B, [9_289_728, 7_225_344, 76_382_208, 38_191_104], 579_059_712, 4_249_534_464),
     "05b": (workloads.DECODE_05B, [737_280, 589_824, 5_603_328, 2_801_664], 164_888_576, 398_458_880),
+    "tp8": (workloads.DECODE_7B_TP8, [1_161_216, 1_032_192, 10_321_920, 5_160_960], 72_382_464, 567_318_528),
 }
 
 

@@ -316,6 +316,14 @@ def test_chain_7b_full_depth_vs_oracle(mq, o, pool):
     _chain_vs_oracle(mq, o, pool, workloads.DECODE_7B, workloads.DECODE_7B.n_layers, n_inputs=1)
 
 
+def test_chain_tp8_rank_full_depth_vs_oracle(mq, o, pool):
+    """One rank of the 7B-class step split eight ways (QKV 576 rows, O taking
+    the first 512 of them, gate/up 5120 rows, down K = 2560, lm_head 19008
+    rows), all 28 layers, collectives left out: the same stage-by-stage parity."""
+    from block_quantized_gemv_amd import workloads
+    _chain_vs_oracle(mq, o, pool, workloads.DECODE_7B_TP8, workloads.DECODE_7B_TP8.n_layers, n_inputs=1)
+
+
 def test_chain_05b_q4_0_full_depth_vs_oracle(mq, o, pool):
     """The pages' measured 0.5B model format: q4_0 layer weights, all 24 layers."""
     from block_quantized_gemv_amd import workloads
@@ -426,7 +434,8 @@ def _split_case(mq, o, pool, m, what):
     H, I, QKV = m.hidden, m.inter, m.qkv_rows
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nblk = I // 32
-    ns = nblk % cus if nblk > cus and (H // 256 + 3) // 4 >= 2 else 0
+    two_passes = (H // 256 + 3) // 4 >= 2
+    ns = (nblk % cus if nblk > cus else nblk if 2 * nblk <= cus else 0) if two_passes else 0
     assert ns > 0, f"{nblk} gate/up blocks on {cus} CUs: no split blocks to test"
     W = model_weights(m, 1)
     Wd = _dev_weights(W)
@@ -503,10 +512,11 @@ def test_span_stamps_7b_width(mq, fmt):
     stamped.close()
 
 
-@pytest.mark.parametrize("inter", [8448, 16128])
+@pytest.mark.parametrize("inter", [2560, 8448, 16128])
 def test_gate_up_split_block_counts(mq, o, pool, inter):
-    """Few and many split blocks: hidden 1280 (two passes over K), 264 and 504
-    gate/up blocks, so 8 and 248 of them split on a 256-CU GPU."""
+    """Few, many and all blocks split: hidden 1280 (two passes over K), 264
+    and 504 gate/up blocks, so 8 and 248 of them split on a 256-CU GPU, and
+    80 blocks, which fill fewer than half the CUs, so every one splits."""
     from block_quantized_gemv_amd import workloads
     m = dataclasses.replace(workloads.DECODE_7B, n_layers=1, hidden=1280, qkv_rows=1280 + 256, inter=inter,
                             vocab=4096)
