@@ -56,6 +56,22 @@ def test_kernel_bytes_7b():
     assert want["gate/up"] == 76_416_672       # the dominant kernel's bytes per launch
 
 
+def test_kernel_bytes_tp8_rank():
+    """The largest tensor-parallel rank's GEMVs: O reads its 512-wide f32 slice
+    of the QKV output and a 3584x512 matrix; down reads the 2560-value q8_0
+    SwiGLU vector (80 blocks of 34 bytes)."""
+    H = 3584
+    want = {
+        "qkv": 1_161_216 + 4 * H + 4 * 576,
+        "o": 1_032_192 + 4 * 512 + 4 * H,
+        "gate/up": 10_321_920 + 4 * H + 80 * 34,
+        "down": 5_160_960 + 80 * 34 + 4 * H,
+        "lm_head": 72_382_464 + 4 * H + 4 * 19008,
+    }
+    got = {name: nbytes for name, _, nbytes in bench.gemv_kinds(workloads.DECODE_7B_TP8)}
+    assert got == want
+
+
 def _record(path, kernel, workload, digest, value=79_648_254):
     path.write_text(
         "# a counter record\n\n"
