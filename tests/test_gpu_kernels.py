@@ -126,6 +126,46 @@ def test_gemv_q4k_full_size(mq, o, pool, name, m, k):
     check_tolerance(y, y_ref, s_abs, name)
 
 
+def test_matrix_of_4_gib_or_more(mq, o):
+    """A 4.32 GB q4_K matrix (30M rows of K = 256, over the 4 GiB that one
+    launch addresses with 32-bit offsets): the one-column GEMV splits it into
+    row blocks under 4 GiB; the batched GEMV at n = 5 takes the vector kernels,
+    because the matrix-core kernel's offsets cannot hold it, and the
+    matrix-core hook refuses it.  The matrix is a seeded 1M-row block repeated
+    on the device, so row r is block row r mod 1M: the rows at and around the
+    row-block boundary, both ends and a random sample are compared with the
+    oracle, and column 0 of the batched result with the one-column GEMV."""
+    import torch
+    synth = _synth()
+    base_rows, reps, k, n = 1_000_000, 30, 256, 5
+    m = base_rows * reps
+    wb = synth.q4k_matrix(7, (synth.KEY_MATRIX, base_rows, k), base_rows, k)
+    assert m * wb.shape[1] >= 1 << 32
+    w = to_dev(wb).reshape(-1).repeat(reps)
+    x = synth.normal_f32(7, (synth.KEY_COLUMNS, 8, k), (8, k))
+    xq8 = mq.mq_quantize_q8_0(to_dev(x))
+    xq_host = o.quantize_q8_0(x).reshape(8, -1)
+    assert np.array_equal(to_host(xq8), xq_host.ravel())
+    col = (k // 32) * 34
+    log(f"q4_K GEMV over {m * 144 / 1e9:.2f} GB ({m} rows)")
+    y1 = mq.mq_gemv_q4k_q8(w, xq8[:col], m, k)
+    y5 = mq.mq_gemv_q4k_q8_batched(w, xq8[:n * col], m, k, n)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y5[:, 0]), "batched column 0 differs from the one-column GEMV"
+    step = ((1 << 32) - 1) // 144          # rows per launch under 32-bit offsets
+    g = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 1, step - 1, step, step + 1, m - 2, m - 1], g.integers(0, m, 200)]))
+    yh = to_host(y5)[rows]
+    for c in range(n):
+        y_ref, s_abs = o.gemv_q4k(wb, base_rows, k, xq_host[c], rows=rows % base_rows)
+        check_tolerance(yh[:, c], y_ref, s_abs, f"4.32 GB matrix, column {c}")
+    with pytest.raises(mq.MQError) as e:
+        mq.mq_debug_gemv_q4k_batched_path(w, xq8, m, k, 8, 1)
+    assert e.value.code == mq.MQ_ERR_SHAPE
+    del w, y1, y5
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- batched ----
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8])
