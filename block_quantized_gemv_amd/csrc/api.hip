@@ -423,7 +423,7 @@ bool readback_reserve(size_t bytes) {
 extern "C" {
 
 const char* mq_last_error(void) { return g_err.c_str(); }
-const char* mq_version(void) { return "libmq 0.1 (gfx950)"; }
+const char* mq_version(void) { return "libmq 0.2 (gfx950)"; }
 
 int mq_time_next_launches(const hipEvent_t* starts, const hipEvent_t* stops, int n) {
     CHECK_ARG(n >= 0 && n <= 65536, "n=%d out of range", n);

@@ -68,6 +68,9 @@ typedef enum {
 } mq_status;
 
 const char* mq_last_error(void);
+/* "libmq <major>.<minor> (gfx950)".  The minor number rises when a
+ * descriptor struct grows (0.2: mq_chain_desc.o_k), so a caller built
+ * against an older mq.h can tell that its structs are too short. */
 const char* mq_version(void);
 
 /* ---------------------------------------------------------------------------
