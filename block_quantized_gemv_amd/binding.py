@@ -95,6 +95,7 @@ SIGNATURES = {
     "mq_probe_stream_read": ([_vp, _i64, _vp, _int, _vp], _int),
     "mq_probe_grid_barrier": ([_int, _int, _int, _int, _vp, _vp, _vp], _int),
     "mq_debug_gemv_q4k_batched_path": ([_vp, _vp, _vp, _i64, _i64, _int, _int, _vp], _int),
+    "mq_gemv_batched_path": ([_i64, _i64, _int, _int, C.POINTER(_int)], _int),
     "mq_probe_graph_boundary": ([_int, _int, _int, _vp], _int),
 }
 
@@ -275,6 +276,15 @@ def mq_debug_gemv_q4k_batched_path(w, xq, m, k, n, path, y=None, stream=None):
                                                 _ptr(y, torch.float32, 4 * m * n, "y"), m, k, n, path,
                                                 _stream(stream)))
     return y
+
+
+def mq_gemv_batched_path(m, k, n, weight_format="q4_K"):
+    """0 if the batched entry point takes the vector kernels for this shape,
+    1 if it takes the matrix cores (host only)."""
+    p = _int()
+    _check(lib().mq_gemv_batched_path(m, k, n, MQ_FMT_Q4_0 if weight_format == "q4_0" else MQ_FMT_Q4_K,
+                                      C.byref(p)))
+    return p.value
 
 
 def mq_gemv_q4k_q8_batched_noalloc(w, xq, m, k, n, y, stream=None):

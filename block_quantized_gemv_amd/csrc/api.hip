@@ -118,17 +118,28 @@ int workspace(size_t need, hipStream_t stream, void** out) {
 
 // Chooses full staging or split-k for a 4-bit GEMV with ncols columns
 // (the debug dump runs with full staging only).
-// Batched q4_K GEMVs with at least this many columns run on the matrix
-// cores (gemv_mfma.hip); fewer columns, q4_0 and the dump run the vector
-// kernels.  Measured on MI355X at the 7B shapes (cold, n = 2..8): the
-// matrix cores take the same time for any n, the vector kernels' time
-// grows with n; they tie at n = 4 and the matrix cores lead from n = 5
-// (gate/up 24 vs 37 us at n = 8).  Matrices too large for the matrix-core
-// kernel's 32-bit offsets (mfma_rows_fit) take the vector kernels.
-constexpr int kMfmaMinCols = 5;
+// Which kernel family a batched q4_K GEMV takes.  The matrix cores' cost
+// hardly grows with n, the vector kernels' does, and the crossover moves
+// to fewer columns as the matrix grows (measured on MI355X, cold, launches
+// alternating between the two paths; weight bytes -> first n where the
+// matrix cores are faster): 0.7-5.6 MB (the 0.5B shapes) none up to n = 8;
+// 7.2 and 9.3 MB (7B O and QKV) n = 8 (7 for QKV, ties at 6); 12 MB n = 7;
+// 16.5 and 19 MB n = 6; 33 and 38 MB n = 5, or n = 4 when K is long enough
+// that the vector kernels need split-k at n = 4 (the 7B down projection);
+// 76 MB (7B gate/up) n = 4.  q4_0, the debug dump and matrices beyond the
+// matrix-core kernel's 32-bit offsets (mfma_rows_fit) take the vector kernels.
+int mfma_min_cols(int64_t m, int64_t k) {
+    constexpr int64_t MB = 1000 * 1000;
+    const int64_t bytes = m * (k / 256) * kQ4KBytes;
+    if (bytes < 6 * MB) return 9;                 // never
+    if (bytes < 12 * MB) return 8;
+    if (bytes < 24 * MB) return 6;
+    if (bytes < 60 * MB) return 4 * stage_bytes((int)(k / 32)) > kMaxStageLds ? 4 : 5;
+    return 4;
+}
 
 bool use_mfma(int fmt, int ncols, int64_t m, int64_t k) {
-    return fmt == kFmtQ4K && ncols >= kMfmaMinCols && mfma_rows_fit(m, k);
+    return fmt == kFmtQ4K && ncols >= mfma_min_cols(m, k) && mfma_rows_fit(m, k);
 }
 
 int run_q4k_mfma(const void* w, const void* xq, int64_t col_bytes, float* y, int64_t m, int64_t k, int ncols,
@@ -597,6 +608,16 @@ int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int6
     if ((rc = scratch_address(&part)) != MQ_OK) return rc;
     return hip_status(launch_gemv_q4k_splitk(w, xq, col_bytes, y, (double*)part, m, k, n, stream, kFmtQ4K),
                       "4-bit split-k GEMV launch");
+}
+
+int mq_gemv_batched_path(int64_t m, int64_t k, int n, int weight_format, int* path) {
+    CHECK_ARG(path, "null path");
+    CHECK_ARG(weight_format == MQ_FMT_Q4_K || weight_format == MQ_FMT_Q4_0, "unknown weight_format %d", weight_format);
+    CHECK_SHAPE(m >= 1 && m <= kMaxRows, "m=%lld out of range", (long long)m);
+    CHECK_SHAPE(k >= 256 && k % 256 == 0 && k <= kMaxK, "k=%lld must be a positive multiple of 256", (long long)k);
+    CHECK_SHAPE(n >= 1 && n <= 8, "n=%d must be in 1..8", n);
+    *path = use_mfma(weight_format == MQ_FMT_Q4_0 ? kFmtQ4_0 : kFmtQ4K, n, m, k) ? 1 : 0;
+    return ok();
 }
 
 int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n, int path,

@@ -100,16 +100,17 @@ int mq_gemv_q4k_q8(const void* w, const void* xq, float* y, int64_t m, int64_t k
  * Batched q4_K x q8_0 GEMV, 1 <= n <= 8 activation columns, weights streamed
  * once for all columns.  xq: [n][k/32] q8_0 blocks (column c at
  * xq + c*(k/32)*34); y: f32 [m][n] row-major, y[r*n + c].
- * Same arithmetic per column as mq_gemv_q4k_q8 for n <= 4 (v_dot4 kernels);
- * for n >= 5 the integer sums come from the matrix cores and the f64 fixup
- * adds the same exact products in another order (results within the same
- * tolerance).  When the kernel splits k across workgroups (n <= 4: the
- * columns do not fit in 64 KB of LDS; n >= 5: rows of more than 16
- * super-blocks, or too few row tiles to fill the GPU) it sums the f64
- * partials in a second pass in split order;
- * the partials (n <= 4: ceil(k/4096)*m*n doubles; n >= 5: n_split*m*n
- * doubles, n_split <= k/256, e.g. 10 splits for the 3584 x 18944 matrix)
- * live in a device workspace that
+ * The kernel family depends on n and the matrix size (mq_gemv_batched_path
+ * says which): the vector kernels (v_dot4), with the arithmetic of
+ * mq_gemv_q4k_q8 per column, or the matrix cores, whose integer sums feed
+ * an f64 fixup that adds the same exact products in another order (results
+ * within the same tolerance).  When the kernel splits k across workgroups
+ * (vector kernels: the columns do not fit in 64 KB of LDS; matrix cores:
+ * rows of more than 16 super-blocks, or too few row tiles to fill the GPU)
+ * it sums the f64 partials in a second pass in split order;
+ * the partials (vector kernels: ceil(k/4096)*m*n doubles; matrix cores:
+ * n_split*m*n doubles, n_split <= k/256, e.g. 10 splits for the
+ * 3584 x 18944 matrix) live in a device workspace that
  * the library keeps per (device, stream) and grows on demand to the next
  * power of two (MQ_ERR_NOMEM if that allocation fails; MQ_ERR_CAPTURE if it
  * must grow while `stream` is being captured: call once outside capture
@@ -142,12 +143,28 @@ int mq_gemv_q4k_q8_batched_noalloc(const void* w, const void* xq, float* y, int6
  * vector kernels: v_dot4 sums, one column per pass over the staged
  * activation) or path 1 (the matrix cores, n >= 2: v_mfma_i32_16x16x64_i8
  * sums of 16 rows x 8 columns x 2 sub-blocks).  The batched entry point
- * itself takes path 1 for n >= 5 when the matrix and one more 16-row tile
- * fit 32-bit byte offsets (under 4 GiB), else path 0.  Same arguments,
- * errors and workspace as mq_gemv_q4k_q8_batched; MQ_ERR_ARG for another
- * path, MQ_ERR_SHAPE for path 1 with n = 1 or a matrix beyond that size. */
+ * itself takes the path mq_gemv_batched_path gives.  Path 1 needs the
+ * matrix and one more 16-row tile to fit 32-bit byte offsets (under 4 GiB).
+ * Same arguments, errors and workspace as mq_gemv_q4k_q8_batched;
+ * MQ_ERR_ARG for another path, MQ_ERR_SHAPE for path 1 with n = 1 or a
+ * matrix beyond that size. */
 int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int64_t m, int64_t k, int n, int path,
                                    hipStream_t stream);
+
+/* The kernel family the batched entry points (mq_gemv_q4k_q8_batched, its
+ * no-allocation form, mq_gemv_q4_0_q8_batched) take for an (m, k, n) shape:
+ * *path = 0 for the vector kernels, 1 for the matrix cores.  Host only (no
+ * HIP call).  The matrix cores' time hardly grows with n, the vector
+ * kernels' does, and the crossover moves to fewer columns as the matrix
+ * grows, so q4_K takes the matrix cores from n = min_cols(bytes) with
+ * bytes = m*(k/256)*144: below 6 MB never; below 12 MB n = 8; below 24 MB
+ * n = 6; below 60 MB n = 5, or n = 4 when the vector kernels would split k
+ * at n = 4 (4 columns of k values do not fit in 64 KB of staging); from
+ * 60 MB n = 4 — and only while the matrix fits 32-bit offsets.  q4_0 always
+ * takes the vector kernels.  weight_format: MQ_FMT_Q4_K or MQ_FMT_Q4_0.
+ * Errors: MQ_ERR_ARG for a null path or an unknown format, MQ_ERR_SHAPE as
+ * for the batched entry points. */
+int mq_gemv_batched_path(int64_t m, int64_t k, int n, int weight_format, int* path);
 
 /* The split-k workspaces (see mq_gemv_q4k_q8_batched).  Host out-params
  * (any may be NULL): bytes held in total, the (device, stream) pairs that

@@ -156,6 +156,28 @@ def test_workspace_and_gate_up_hook_on_the_host(mq):
     assert g(FAKE, C.c_void_p(0x10004), 1e-6, None, FAKE, 64, 256, 0, None, None, 0, None) == mq.MQ_ERR_ARG
 
 
+def test_batched_path_rule(mq):
+    """The kernel family of the batched entry points by shape, on the host:
+    the matrix cores from n = 4 on 76 MB (7B gate/up) and on the 38 MB 7B
+    down projection (whose vector kernels would split k at n = 4), from
+    n = 5 on a 38 MB matrix of short rows, from n = 6 at 16.5 MB, from n = 8
+    on the 7B QKV and O matrices, never on the 0.5B ones; q4_0 and a matrix
+    past 32-bit offsets never."""
+    cases = [((37888, 3584), 4), ((3584, 18944), 4), ((18944, 3584), 5), ((16384, 3584), 5),
+             ((8192, 3584), 6), ((1792, 18944), 6), ((4608, 3584), 8), ((3584, 3584), 8),
+             ((9728, 1024), 9), ((1280, 1024), 9), ((1024, 4864), 9), ((30_000_000, 256), 9)]
+    for (m, k), first in cases:
+        got = [mq.mq_gemv_batched_path(m, k, n) for n in range(1, 9)]
+        assert got == [int(n >= first) for n in range(1, 9)], (m, k, got)
+        assert all(mq.mq_gemv_batched_path(m, k, n, "q4_0") == 0 for n in range(1, 9))
+    L = mq.lib()
+    p = C.c_int()
+    assert L.mq_gemv_batched_path(100, 256, 9, 0, C.byref(p)) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_batched_path(100, 300, 2, 0, C.byref(p)) == mq.MQ_ERR_SHAPE
+    assert L.mq_gemv_batched_path(100, 256, 2, 3, C.byref(p)) == mq.MQ_ERR_ARG
+    assert L.mq_gemv_batched_path(100, 256, 2, 0, None) == mq.MQ_ERR_ARG
+
+
 def test_no_alloc_entry_point_refuses_on_the_host(mq):
     L = mq.lib()
     f = L.mq_gemv_q4k_q8_batched_noalloc

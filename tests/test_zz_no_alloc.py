@@ -29,6 +29,7 @@ def test_no_alloc_matches_the_allocating_entry_point(mq):
     # ranges, 2.2 MiB of partials), a smaller split-k call of the vector
     # kernels after it, then a one-pass shape
     cases = [(3584, 18944, 8), (515, 18944, 4), (301, 2560, 3)]
+    assert [mq.mq_gemv_batched_path(m, k, n) for m, k, n in cases] == [1, 0, 0]
     outs = []
     for m, k, n in cases:
         log(f"no-alloc batched {m}x{k} n={n}")
@@ -62,7 +63,8 @@ def test_no_alloc_under_graph_capture(mq):
     import oracle
     from block_quantized_gemv_amd import synth
     o = oracle.Oracle()
-    for m, k, n in ((2049, 4096, 8), (515, 18944, 3)):
+    for m, k, n in ((2049, 8192, 8), (515, 18944, 3)):
+        assert mq.mq_gemv_batched_path(m, k, n) == (1 if n == 8 else 0)
         log(f"no-alloc batched under capture {m}x{k} n={n}")
         w = to_dev(synth.q4k_matrix(17, (synth.KEY_MATRIX, m, k), m, k))
         xq = to_dev(o.quantize_q8_0(synth.normal_f32(17, (synth.KEY_COLUMNS, n, k), (n, k))).ravel())
