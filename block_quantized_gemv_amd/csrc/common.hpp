@@ -249,6 +249,38 @@ __device__ __forceinline__ void stage_q8_store(const uint8_t* __restrict__ xq, i
         stage_q8_block(b, dbits, q, lds);
     }
 }
+// The same two steps for ncols columns (column c at xq + c*col_stride,
+// staged at lds + c*col_bytes), their blocks taken as one flat list
+// f = c*nb + b, so that the columns' first blocks are requested together.
+__device__ __forceinline__ void stage_q8_load_cols(const uint8_t* __restrict__ xq, int64_t col_stride, int nb,
+                                                   int ncols, Q8Regs& r) {
+    const int total = nb * ncols;
+#pragma unroll
+    for (int k = 0; k < kStageRegBlocks; ++k) {
+        const int f = (int)threadIdx.x + k * (int)blockDim.x;
+        const int c = f < total ? f / nb : 0, b = f < total ? f - c * nb : 0;
+        r.d[k] = load_q8_block(xq + c * col_stride + (int64_t)b * kQ8Bytes, r.q[k]);
+    }
+}
+__device__ __forceinline__ void stage_q8_store_cols(const uint8_t* __restrict__ xq, int64_t col_stride, int nb,
+                                                    int ncols, const Q8Regs& r, uint8_t* __restrict__ lds,
+                                                    int col_bytes) {
+    const int total = nb * ncols;
+#pragma unroll
+    for (int k = 0; k < kStageRegBlocks; ++k) {
+        const int f = (int)threadIdx.x + k * (int)blockDim.x;
+        if (f < total) {
+            const int c = f / nb;
+            stage_q8_block(f - c * nb, r.d[k], r.q[k], lds + c * col_bytes);
+        }
+    }
+    for (int f = (int)threadIdx.x + kStageRegBlocks * (int)blockDim.x; f < total; f += (int)blockDim.x) {
+        const int c = f / nb, b = f - c * nb;
+        uint32_t q[8];
+        const uint32_t dbits = load_q8_block(xq + c * col_stride + (int64_t)b * kQ8Bytes, q);
+        stage_q8_block(b, dbits, q, lds + c * col_bytes);
+    }
+}
 
 // The staged data of pair P: codes of blocks 2P (c[0..7]) and 2P+1 (c[8..15]),
 // their scales and scale*code-sums.

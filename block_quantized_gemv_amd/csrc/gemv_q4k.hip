@@ -325,7 +325,8 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
 constexpr int kSrcQ8 = 0, kSrcQ8Early = 1, kSrcNorm = 2;
 
 template <int FMT, int NC, bool DUMP, int SRC, bool ST = false>
-__global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) __attribute__((amdgpu_waves_per_eu(1, NC >= 5 ? 3 : 8))) void k_gemv_q4k(
+__global__ __launch_bounds__(SRC == kSrcQ8 ? 256 : NC >= 5 ? 64 * kWavesQ8EarlyMax : 1024)
+__attribute__((amdgpu_waves_per_eu(1, NC >= 5 ? 3 : 8))) void k_gemv_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int64_t xq_col_bytes,
     float* __restrict__ y, int32_t* __restrict__ dump_isum, int32_t* __restrict__ dump_ysum,
     int M, int nsb, int log2s, int passes, int n_tiles, NormIn nin) {
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) __attribute__((amdgpu_w
     const int col_bytes = stage_bytes(nb);
     const int W = gridDim.x * (blockDim.x >> 6);
     constexpr bool kEarly = SRC != kSrcQ8;
-    static_assert(SRC == kSrcQ8 || (NC == 1 && !DUMP), "early staging takes one column");
+    static_assert(SRC == kSrcQ8 || SRC == kSrcQ8Early || (NC == 1 && !DUMP), "the norm prologue takes one column");
+    static_assert(SRC != kSrcQ8Early || !DUMP, "early staging has no dump");
     // The norm-prologue kernel keeps the wave index (and so its few items'
     // index arithmetic) in vector registers: measured faster there; the
     // others take it as a scalar and walk their items with a cursor.
@@ -406,7 +408,10 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) __attribute__((amdgpu_w
         xin = norm_row(nin, nsb * 256);
         norm_load(xin, nsb * 256, xr);
     }
-    if constexpr (SRC == kSrcQ8Early) stage_q8_load(xq, nb, qr);
+    if constexpr (SRC == kSrcQ8Early) {
+        if constexpr (NC == 1) stage_q8_load(xq, nb, qr);
+        else stage_q8_load_cols(xq, xq_col_bytes, nb, NC, qr);
+    }
     Item A, B;
     fetch(0, A);
     if constexpr (kEarly) fetch(1, B);
@@ -414,7 +419,8 @@ __global__ __launch_bounds__(SRC != kSrcQ8 ? 1024 : 256) __attribute__((amdgpu_w
         __shared__ double sh[16];
         stage_norm_input(nin, xin, nsb * 256, xr, lds, sh);
     } else if constexpr (SRC == kSrcQ8Early) {
-        stage_q8_store(xq, nb, qr, lds);
+        if constexpr (NC == 1) stage_q8_store(xq, nb, qr, lds);
+        else stage_q8_store_cols(xq, xq_col_bytes, nb, NC, qr, lds, col_bytes);
     } else {
         stage_q8_cols<4>(xq, xq_col_bytes, 0, nb, NC, lds, col_bytes, (DUMP && blockIdx.x == 0) ? dump_ysum : nullptr);
     }
@@ -1195,17 +1201,38 @@ hipError_t launch_gemv_q4k_norm(const void* w, const NormIn& nin, float* y, int6
                            : launch_norm<kFmtQ4K>(w, nin, y, m, k, stream);
 }
 
+// NC q8_0 columns with early staging: the one-column GEMV's launch shape
+// (one workgroup per CU, interleaved tiles, waves for about kItemsPerWave
+// items each), the columns' first blocks requested before the weights and
+// staged side by side (NC * stage_bytes <= kMaxStageLds, checked by the
+// caller).
+template <int FMT, int NC>
+static hipError_t launch_q8_early_nc(const void* w, const void* xq, int64_t xq_col_bytes, float* y, int64_t m,
+                                     int nsb, hipStream_t stream) {
+    const Q4KPlan p = plan_q4k(m, nsb);
+    const int lds = NC * stage_bytes(nsb * 8);
+    const int64_t per_cu = (int64_t)device_cu_count() * kItemsPerWave;
+    const int64_t want = ((int64_t)p.n_tiles * p.passes + per_cu - 1) / per_cu;
+    const int cap = (int)(want < kWavesQ8EarlyMin ? kWavesQ8EarlyMin : want > kWavesQ8EarlyMax ? kWavesQ8EarlyMax : want);
+    int grid = 1, threads = 64;
+    prologue_grid(p.n_tiles, (NC * nsb * 8 + kStageRegBlocks - 1) / kStageRegBlocks, &grid, &threads, cap);
+    MQ_LAUNCH((k_gemv_q4k<FMT, NC, false, kSrcQ8Early>), dim3(grid), dim3(threads), lds, stream, (const uint8_t*)w,
+              (const uint8_t*)xq, xq_col_bytes, y, (int32_t*)nullptr, (int32_t*)nullptr, (int)m, nsb, p.log2s,
+              p.passes, p.n_tiles, NormIn{});
+    return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t launch_fmt(const void* w, const void* xq, int64_t xq_col_bytes, float* y, int32_t* dump_isum,
                              int32_t* dump_ysum, int64_t m, int nsb, int ncols, hipStream_t stream) {
     if (dump_isum) return launch_nc<FMT, 1, true>(w, xq, xq_col_bytes, y, dump_isum, dump_ysum, m, nsb, stream);
     switch (ncols) {
         case 1: return launch_q8_early<FMT>(w, xq, y, m, nsb, stream);
-        case 2: return launch_nc<FMT, 2, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 3: return launch_nc<FMT, 3, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 4: return launch_nc<FMT, 4, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 5: return launch_nc<FMT, 5, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
-        case 6: return launch_nc<FMT, 6, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
+        case 2: return launch_q8_early_nc<FMT, 2>(w, xq, xq_col_bytes, y, m, nsb, stream);
+        case 3: return launch_q8_early_nc<FMT, 3>(w, xq, xq_col_bytes, y, m, nsb, stream);
+        case 4: return launch_q8_early_nc<FMT, 4>(w, xq, xq_col_bytes, y, m, nsb, stream);
+        case 5: return launch_q8_early_nc<FMT, 5>(w, xq, xq_col_bytes, y, m, nsb, stream);
+        case 6: return launch_q8_early_nc<FMT, 6>(w, xq, xq_col_bytes, y, m, nsb, stream);
         case 7: return launch_nc<FMT, 7, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
         case 8: return launch_nc<FMT, 8, false>(w, xq, xq_col_bytes, y, nullptr, nullptr, m, nsb, stream);
         default: return hipErrorInvalidValue;
