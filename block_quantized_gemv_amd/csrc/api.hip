@@ -120,21 +120,24 @@ int workspace(size_t need, hipStream_t stream, void** out) {
 // (the debug dump runs with full staging only).
 // Which kernel family a batched q4_K GEMV takes.  The matrix cores' cost
 // hardly grows with n, the vector kernels' does, and the crossover moves
-// to fewer columns as the matrix grows (measured on MI355X, cold, launches
-// alternating between the two paths; weight bytes -> first n where the
-// matrix cores are faster): 0.7-5.6 MB (the 0.5B shapes) none up to n = 8;
-// 7.2 and 9.3 MB (7B O and QKV) n = 8 (7 for QKV, ties at 6); 12 MB n = 7;
-// 16.5 and 19 MB n = 6; 33 and 38 MB n = 5, or n = 4 when K is long enough
-// that the vector kernels need split-k at n = 4 (the 7B down projection);
-// 76 MB (7B gate/up) n = 4.  q4_0, the debug dump and matrices beyond the
-// matrix-core kernel's 32-bit offsets (mfma_rows_fit) take the vector kernels.
+// to fewer columns as the matrix grows, and to fewer still where the
+// vector kernels must split k (their n columns do not fit in 64 KB of
+// staging).  Measured on MI355X, cold, launches alternating between the two
+// paths (weight bytes -> first n where the matrix cores are faster):
+// 0.7-5.6 MB (the 0.5B shapes) none up to n = 8; 7.2 MB (7B O) n = 8;
+// 9.3-16.5 MB (7B QKV and 12.4, 16.5 MB matrices) n = 7; 19 MB with
+// K = 18944 (split k from n = 3) n = 6; 33 and 38 MB of short rows n = 5-6;
+// 38 MB with K = 18944 (the 7B down projection) n = 4; 76 MB (7B gate/up)
+// n = 4.  q4_0, the debug dump and matrices beyond the matrix-core kernel's
+// 32-bit offsets (mfma_rows_fit) take the vector kernels.
 int mfma_min_cols(int64_t m, int64_t k) {
     constexpr int64_t MB = 1000 * 1000;
     const int64_t bytes = m * (k / 256) * kQ4KBytes;
+    auto splits_at = [&](int n) { return n * stage_bytes((int)(k / 32)) > kMaxStageLds; };
     if (bytes < 6 * MB) return 9;                 // never
-    if (bytes < 12 * MB) return 8;
-    if (bytes < 24 * MB) return 6;
-    if (bytes < 60 * MB) return 4 * stage_bytes((int)(k / 32)) > kMaxStageLds ? 4 : 5;
+    if (bytes < 8 * MB) return 8;
+    if (bytes < 24 * MB) return splits_at(6) ? 6 : 7;
+    if (bytes < 60 * MB) return splits_at(4) ? 4 : 6;
     return 4;
 }
 

@@ -157,10 +157,11 @@ int mq_debug_gemv_q4k_batched_path(const void* w, const void* xq, float* y, int6
  * HIP call).  The matrix cores' time hardly grows with n, the vector
  * kernels' does, and the crossover moves to fewer columns as the matrix
  * grows, so q4_K takes the matrix cores from n = min_cols(bytes) with
- * bytes = m*(k/256)*144: below 6 MB never; below 12 MB n = 8; below 24 MB
- * n = 6; below 60 MB n = 5, or n = 4 when the vector kernels would split k
- * at n = 4 (4 columns of k values do not fit in 64 KB of staging); from
- * 60 MB n = 4 — and only while the matrix fits 32-bit offsets.  q4_0 always
+ * bytes = m*(k/256)*144: below 6 MB never; below 8 MB n = 8; below 24 MB
+ * n = 7, or 6 when the vector kernels would split k at n = 6; below 60 MB
+ * n = 6, or 4 when they would split k at n = 4 (n columns of k values do
+ * not fit in 64 KB of staging); from 60 MB n = 4 — and only while the
+ * matrix fits 32-bit offsets.  q4_0 always
  * takes the vector kernels.  weight_format: MQ_FMT_Q4_K or MQ_FMT_Q4_0.
  * Errors: MQ_ERR_ARG for a null path or an unknown format, MQ_ERR_SHAPE as
  * for the batched entry points. */

@@ -160,11 +160,12 @@ def test_batched_path_rule(mq):
     """The kernel family of the batched entry points by shape, on the host:
     the matrix cores from n = 4 on 76 MB (7B gate/up) and on the 38 MB 7B
     down projection (whose vector kernels would split k at n = 4), from
-    n = 5 on a 38 MB matrix of short rows, from n = 6 at 16.5 MB, from n = 8
-    on the 7B QKV and O matrices, never on the 0.5B ones; q4_0 and a matrix
+    n = 6 on 33-38 MB matrices of short rows and on a 19 MB one whose vector
+    kernels would split k at n = 6, from n = 7 on 9.3-16.5 MB ones (7B QKV),
+    from n = 8 on the 7.2 MB 7B O, never on the 0.5B ones; q4_0 and a matrix
     past 32-bit offsets never."""
-    cases = [((37888, 3584), 4), ((3584, 18944), 4), ((18944, 3584), 5), ((16384, 3584), 5),
-             ((8192, 3584), 6), ((1792, 18944), 6), ((4608, 3584), 8), ((3584, 3584), 8),
+    cases = [((37888, 3584), 4), ((3584, 18944), 4), ((18944, 3584), 6), ((16384, 3584), 6),
+             ((1792, 18944), 6), ((8192, 3584), 7), ((6144, 3584), 7), ((4608, 3584), 7), ((3584, 3584), 8),
              ((9728, 1024), 9), ((1280, 1024), 9), ((1024, 4864), 9), ((30_000_000, 256), 9)]
     for (m, k), first in cases:
         got = [mq.mq_gemv_batched_path(m, k, n) for n in range(1, 9)]
