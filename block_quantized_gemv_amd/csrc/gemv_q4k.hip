@@ -315,9 +315,12 @@ __device__ __forceinline__ void group_item(const Q40Load& L, const Lanes& ln, in
 // w, w+W, w+2W, ... (W = waves in the grid); its items are (tile, pass) in
 // that order.  Where the activation comes from (SRC):
 //   kSrcQ8       q8_0 columns at xq, staged by 256-thread workgroups
-//                (several per CU) after the first item is requested;
-//   kSrcQ8Early  one q8_0 column at xq, requested before the weights and
-//                staged by one workgroup of up to 1024 threads per CU;
+//                (several per CU) after the first item is requested (the
+//                debug dump, and 7 or 8 columns, where the early form would
+//                spill registers);
+//   kSrcQ8Early  one to six q8_0 columns at xq, requested before the
+//                weights and staged by one workgroup per CU (up to 1024
+//                threads, 768 from five columns on, for the registers);
 //   kSrcNorm     Q8(RMSNorm(x)) of the f32 vector `nin` describes, formed
 //                by one workgroup of up to 1024 threads per CU.
 // The last two fetch two items before the prologue and give consecutive
