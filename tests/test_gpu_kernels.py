@@ -276,6 +276,62 @@ def test_batched_full_size(mq, o, pool, name, m, k, n):
             assert same == 1.0, f"{name} n={n} col {c}: batched column differs from the n = 1 kernel"
 
 
+def _sweep_cases(count=36, large=8, seed=20261202):
+    """Seeded random (format, m, k, n) beyond the hand-picked lists: m from 1
+    to 6000 (log-uniform), k a multiple of 256 up to 12288, n from 1 to 8,
+    every third case q4_0 (the long-k ones split k); then `large` q4_K cases
+    of 2000 to 8000 rows, k from 4096 and n from 5, which the size rule
+    sends to the matrix cores where it can."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        m = int(np.exp(g.uniform(0.0, np.log(6000.0))))
+        k = 256 * int(g.integers(1, 49))
+        n = int(g.integers(1, 9))
+        cases.append(("q4_0" if i % 3 == 0 else "q4_K", max(m, 1), k, n))
+    for _ in range(large):
+        cases.append(("q4_K", int(g.integers(2000, 8001)), 256 * int(g.integers(16, 49)), int(g.integers(5, 9))))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("fmt,m,k,n", SWEEP, ids=[f"{f}-{m}x{k}-n{n}" for f, m, k, n in SWEEP])
+def test_random_shape_sweep(mq, o, pool, fmt, m, k, n):
+    """Every column of every row against the oracle, through the batched
+    entry point (whichever family the size rule picks) and, for q4_K, the
+    vector kernels and the matrix cores forced; the vector kernels' columns
+    equal the n = 1 kernel's bit for bit where they make one pass over k."""
+    synth = _synth()
+    log(f"sweep {fmt} {m}x{k} n={n} (batched path {mq.mq_gemv_batched_path(m, k, n, fmt)})")
+    seed = 7000 + m + k + n
+    q4k = fmt == "q4_K"
+    w = (synth.q4k_matrix if q4k else synth.q4_0_matrix)(seed, (synth.KEY_MATRIX, m, k), m, k)
+    x = synth.normal_f32(seed, (synth.KEY_COLUMNS, n, k), (n, k))
+    xq = o.quantize_q8_0(x).reshape(n, -1)
+    wd, xd = to_dev(w), to_dev(xq.ravel())
+    ref = o.gemv_q4k if q4k else o.gemv_q4_0
+    single = mq.mq_gemv_q4k_q8 if q4k else mq.mq_gemv_q4_0_q8
+    y = to_host((mq.mq_gemv_q4k_q8_batched if q4k else mq.mq_gemv_q4_0_q8_batched)(wd, xd, m, k, n))
+    forced = {}
+    if q4k:
+        forced["vector kernels"] = to_host(mq.mq_debug_gemv_q4k_batched_path(wd, xd, m, k, n, 0))
+        if n >= 2:
+            forced["matrix cores"] = to_host(mq.mq_debug_gemv_q4k_batched_path(wd, xd, m, k, n, 1))
+    for c in range(n):
+        y_ref, s_abs = oracle_gemv_parallel(ref, w, m, k, xq[c], pool=pool)
+        check_tolerance(y[:, c], y_ref, s_abs, f"{fmt} {m}x{k} n={n} col {c}")
+        for what, yf in forced.items():
+            check_tolerance(yf[:, c], y_ref, s_abs, f"{fmt} {m}x{k} n={n} col {c}, {what}")
+        y1 = to_host(single(wd, to_dev(xq[c]), m, k))
+        check_tolerance(y1, y_ref, s_abs, f"{fmt} {m}x{k} col {c}, n = 1 kernel")
+        yv = forced.get("vector kernels", y if mq.mq_gemv_batched_path(m, k, n, fmt) == 0 else None)
+        if yv is not None and _single_pass(m, k, n):
+            assert np.array_equal(y1.view(np.uint32), yv[:, c].copy().view(np.uint32)), \
+                f"{fmt} {m}x{k} n={n} col {c}: vector kernels differ from the n = 1 kernel"
+
+
 # ------------------------------------------------------------- q4_0 GEMV ----
 
 Q4_0_SMALL = [(1, 256), (3, 512), (17, 768), (1023, 1024), (1025, 3584), (333, 4864), (64, 18944), (130, 4096)]
