@@ -330,6 +330,38 @@ def test_chain_05b_q4_0_full_depth_vs_oracle(mq, o, pool):
     _chain_vs_oracle(mq, o, pool, workloads.DECODE_05B_Q4_0, 24)
 
 
+def _random_chain_dims(count=16, seed=20261203):
+    """Seeded random decode-step shapes: hidden 256..3072, inter 256..10240
+    log-uniform (from a few gate/up output blocks to more than two per CU,
+    so the split of surplus blocks varies), QKV rows from O's K up to 2048 more, O's K
+    the whole hidden vector or a prefix of it, 1..3 layers, a vocabulary of
+    1..20000 rows, both weight formats."""
+    from block_quantized_gemv_amd import workloads
+    g = np.random.default_rng(seed)
+    dims = []
+    for i in range(count):
+        h = 256 * int(g.integers(1, 13))
+        o_k = 0 if i % 2 == 0 else 256 * int(g.integers(1, h // 256 + 1))
+        dims.append(workloads.DecodeModel(
+            name=f"random step {i}", hidden=h, n_layers=int(g.integers(1, 4)),
+            qkv_rows=(o_k or h) + 4 * int(g.integers(0, 513)), inter=256 * int(np.exp(g.uniform(0.0, np.log(40.0)))),
+            vocab=int(g.integers(1, 20001)), seed=300 + i, weight_format="q4_0" if i % 4 == 3 else "q4_K",
+            o_k=o_k))
+    return dims
+
+
+RANDOM_DIMS = _random_chain_dims()
+
+
+@pytest.mark.parametrize("model", RANDOM_DIMS, ids=[f"{m.weight_format}-h{m.hidden}-i{m.inter}-q{m.qkv_rows}-"
+                                                    f"ok{m.o_k}-L{m.n_layers}-v{m.vocab}" for m in RANDOM_DIMS])
+def test_chain_random_dims_vs_oracle(mq, o, pool, model):
+    """The stage-by-stage parity of the full-size steps on seeded random
+    shapes: every q8_0 vector byte-identical, every f32 intermediate and
+    logit bit-identical to the oracle's step, over two steps."""
+    _chain_vs_oracle(mq, o, pool, model, model.n_layers)
+
+
 def test_q4_0_chain_graph_equals_eager(mq):
     from block_quantized_gemv_amd import synth, workloads
     model = dataclasses.replace(workloads.DECODE_05B_Q4_0, n_layers=3)
