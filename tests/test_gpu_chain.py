@@ -455,6 +455,56 @@ def test_moe_chain(mq, o):
     assert np.array_equal(to_host(lz.y_table).view(np.uint32), yg.view(np.uint32)), "lazy capture changed the bytes"
 
 
+def _random_moe_dims(count=8, seed=20261204):
+    """Seeded random routed-expert shapes: 1..64 experts, 1..8 selected
+    (at most all of them), hidden 256..4096, expert inter 32..3072 in steps
+    of 32 (down's K padded to whole super-blocks where it is not one)."""
+    g = np.random.default_rng(seed)
+    dims = []
+    for i in range(count):
+        ne = int(g.integers(1, 65))
+        dims.append((ne, int(g.integers(1, min(8, ne) + 1)), 256 * int(g.integers(1, 17)),
+                     32 * int(g.integers(1, 97)), 400 + i))
+    return dims
+
+
+RANDOM_MOE = _random_moe_dims()
+
+
+@pytest.mark.parametrize("n_experts,n_sel,hidden,inter,seed", RANDOM_MOE,
+                         ids=[f"e{a}-s{b}-h{c}-i{d}" for a, b, c, d, _ in RANDOM_MOE])
+def test_moe_random_dims(mq, o, n_experts, n_sel, hidden, inter, seed):
+    """Four tokens of a routed-expert chain on seeded random shapes: graph
+    and eager byte-identical, each token within the combine's bound of the
+    oracle's token (sum over slots of |c_s| times the slot's S_abs)."""
+    from block_quantized_gemv_amd import synth
+    H, I, T = hidden, inter, 4
+    log(f"MoE {n_experts} experts, top-{n_sel}, hidden {H}, inter {I}")
+    gu = np.stack([synth.q4k_matrix(seed, (synth.KEY_EXPERT, e, 0), 2 * I, H) for e in range(n_experts)])
+    dn = np.stack([synth.q4k_matrix(seed, (synth.KEY_EXPERT, e, 1), H, I) for e in range(n_experts)])
+    ids, logits = synth.routing(seed, T, n_experts, n_sel)
+    X = synth.normal_f32(seed, (synth.KEY_TOKEN_X,), (T, H))
+    args = (n_experts, n_sel, H, I, to_dev(gu.ravel()), gu[0].nbytes, to_dev(dn.ravel()), dn[0].nbytes,
+            to_dev(ids), to_dev(logits), to_dev(X))
+    g = mq.MoEChain(*args)
+    e = mq.MoEChain(*args, flags=mq.MQ_EAGER_ONLY)
+    for _ in range(T):
+        g.step(mq.MQ_GRAPH)
+        e.step(mq.MQ_EAGER)
+    yg, ye = to_host(g.y_table), to_host(e.y_table)
+    assert np.array_equal(yg.view(np.uint32), ye.view(np.uint32)), "graph != eager"
+    for t in range(T):
+        y_ref, _, c_ref = o.moe_token(gu.ravel(), gu[0].nbytes, dn.ravel(), dn[0].nbytes, ids[t], logits[t],
+                                      X[t], H, I)
+        s_abs = np.zeros(H)
+        xq = o.quantize_q8_0(X[t]).ravel()
+        for sl, ex in enumerate(ids[t]):
+            t_gu, _ = o.gemv_q4k(gu[ex], 2 * I, H, xq)
+            _, sa = o.gemv_q4k(dn[ex], H, I, o.quantize_q8_0(o.swiglu(t_gu)).ravel())
+            s_abs += abs(float(c_ref[sl])) * sa
+        check_tolerance(yg[t], y_ref, s_abs, f"token {t}")
+
+
 def _split_case(mq, o, pool, m, what):
     """Graph == eager over six steps and a reset, for a one-layer chain whose
     gate/up has split blocks; then the step's trace against the oracle's own
