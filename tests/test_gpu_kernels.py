@@ -65,6 +65,34 @@ def test_quantize_bytes_exact(mq, o):
         assert np.array_equal(got, want), f"{name}: {q8_code_diff(got, want)}"
 
 
+def _random_quantize_cases(count=12, seed=20261205):
+    """Seeded random activation rows: length 32..131072 in blocks of 32
+    (log-uniform), magnitude 10^-6..10^6, and a random share of all-zero
+    blocks."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        nb = int(np.exp(g.uniform(0.0, np.log(4096.0))))
+        cases.append((32 * max(nb, 1), float(10.0 ** g.uniform(-6.0, 6.0)), float(g.uniform(0.0, 0.5)), 500 + i))
+    return cases
+
+
+RANDOM_QUANT = _random_quantize_cases()
+
+
+@pytest.mark.parametrize("k,scale,zero_share,seed", RANDOM_QUANT,
+                         ids=[f"k{k}-s{sc:.0e}-z{z:.2f}" for k, sc, z, _ in RANDOM_QUANT])
+def test_quantize_random_rows(mq, o, k, scale, zero_share, seed):
+    """q8_0 bytes of seeded random rows equal the oracle's, byte for byte."""
+    synth = _synth()
+    x = synth.normal_f32(seed, (k,), (k,)) * np.float32(scale)
+    zero = np.random.default_rng(seed).random(k // 32) < zero_share
+    x = np.where(np.repeat(zero, 32), np.float32(0.0), x).astype(np.float32)
+    got = to_host(mq.mq_quantize_q8_0(to_dev(x[None])))
+    want = o.quantize_q8_0(x[None]).ravel()
+    assert np.array_equal(got, want), f"k={k} scale={scale:.1e}: {q8_code_diff(got, want)}"
+
+
 # ------------------------------------------------------------- q4_K GEMV ----
 
 SMALL_SHAPES = [(1, 256), (3, 512), (17, 768), (1024, 1024), (1023, 1024), (1025, 3584), (4097, 1536),
@@ -468,6 +496,34 @@ def test_gemv_q8_0_small(mq, o, m, k):
     assert np.array_equal(to_host(y).view(np.uint32), y2.view(np.uint32))
     y_ref, s_abs = o.gemv_q8_0(w, m, k, xq)
     check_tolerance(y2, y_ref, s_abs, f"q8_0 {m}x{k}")
+
+
+def _random_q8_0_shapes(count=10, seed=20261206):
+    """Seeded random q8_0 GEMV shapes: m 1..200000 (log-uniform), k a
+    multiple of 64 up to 8192."""
+    g = np.random.default_rng(seed)
+    return [(max(int(np.exp(g.uniform(0.0, np.log(200000.0)))), 1), 64 * int(g.integers(1, 129)))
+            for _ in range(count)]
+
+
+RANDOM_Q8_0 = _random_q8_0_shapes()
+
+
+@pytest.mark.parametrize("m,k", RANDOM_Q8_0)
+def test_gemv_q8_0_random_shapes(mq, o, pool, m, k):
+    """Every row of seeded random q8_0 GEMV shapes within the gate of the
+    oracle; the debug build's y equals the production y bit for bit."""
+    synth = _synth()
+    log(f"q8_0 GEMV {m}x{k}")
+    w = synth.q8_0_matrix(6, (synth.KEY_MATRIX, m, k), m, k)
+    x = synth.normal_f32(6, (synth.KEY_COLUMNS, m, k), (k,))
+    xq = o.quantize_q8_0(x).ravel()
+    wd, xd = to_dev(w), to_dev(xq)
+    y = to_host(mq.mq_gemv_q8_0_q8(wd, xd, m, k))
+    yd, _ = mq.mq_debug_gemv_q8_0_q8_isums(wd, xd, m, k)
+    assert np.array_equal(to_host(yd).view(np.uint32), y.view(np.uint32))
+    y_ref, s_abs = oracle_gemv_parallel(o.gemv_q8_0, w, m, k, xq, pool=pool)
+    check_tolerance(y, y_ref, s_abs, f"q8_0 {m}x{k}")
 
 
 @pytest.mark.parametrize("name,m,k", [("0.5B lm_head", 151552, 1024), ("7B lm_head", 152064, 3584)])
