@@ -179,6 +179,21 @@ def test_batched_path_rule(mq):
     assert L.mq_gemv_batched_path(100, 256, 2, 0, None) == mq.MQ_ERR_ARG
 
 
+def test_random_sweeps_reach_every_kernel_family(mq):
+    """The seeded random GEMV sweep of the GPU tests keeps covering both
+    kernel families of the batched entry point, one-pass and split-k vector
+    shapes, and both weight formats (checked on the host, so that a change
+    of the size rule cannot quietly narrow it)."""
+    import test_gpu_kernels as tk
+    cases = tk._sweep_cases()
+    assert len(cases) == len(set(cases))
+    paths = [mq.mq_gemv_batched_path(m, k, n, f) for f, m, k, n in cases]
+    assert 1 in paths and 0 in paths
+    assert {f for f, *_ in cases} == {"q4_K", "q4_0"}
+    vec = [(m, k, n) for (f, m, k, n), p in zip(cases, paths) if p == 0 and n > 1]
+    assert any(tk._single_pass(m, k, n) for m, k, n in vec) and not all(tk._single_pass(m, k, n) for m, k, n in vec)
+
+
 def test_no_alloc_entry_point_refuses_on_the_host(mq):
     L = mq.lib()
     f = L.mq_gemv_q4k_q8_batched_noalloc
